@@ -1,0 +1,352 @@
+/*
+ * Oracle for the routed int4 MoE FFN with sigmoid top-k routing.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark, never by the product path.  It shares
+ * no code with the GPU library.
+ *
+ * What the method computes, and where the pages say so:
+ *
+ *  - Activations are quantised "Q8_0 style" to int8 and multiplied against
+ *    quantised weights with an integer dot product (discuss.pytorch.kr,
+ *    "colibri: 744B MoE ... 순수 C 추론 엔진", section "colibri의 주요 기능",
+ *    integer-dot-kernel bullet; jeff.news "7440억 파라미터 GLM-5.2 ...",
+ *    section on attention and kernels, integer matmul bullet).
+ *  - Expert weights are int4, stored as U8-packed nibbles with a separate
+ *    per-row F32 scale file, produced with np.rint so that they match the
+ *    engine's lrintf rounding (aitrends.kr "GLM-5.2-colibri-int4", sections
+ *    "TL;DR", "훈련 방식" and "기술적 특징").
+ *  - Routing is DeepSeek-V3 style: sigmoid scores, top-k with a selection
+ *    bias, plus an always-on shared expert (jeff.news, attention-and-kernels
+ *    section, DeepSeek-style tricks bullet); 8 of 256 experts per token
+ *    (discuss.pytorch.kr, "colibri의 핵심 아이디어"; jeff.news, disk
+ *    bottleneck section: 75 layers x 8 experts).
+ *  - Router and norm layers stay F32 (aitrends.kr, "알아두면 좋은 것").
+ *  - Prefill and the batched verify pass group tokens by expert so that
+ *    each selected expert is loaded once ("batch-union MoE", alphamatch.ai
+ *    "Colibri: 25GB RAM만으로 ...", section "기술적 우수성").
+ *
+ * Readings where the pages are silent (each is the plainest one the rest
+ * supports): Q8 blocks hold 32 values with an F32 scale max|x|/127; int4
+ * rows use s = max|w|/7 and codes in [-7, 7]; the low nibble holds the even
+ * column; the expert FFN is SwiGLU; the combine is shared + sum_j w_j o_j;
+ * the hidden vector is re-quantised with Q8_0 before the down projection;
+ * fp32 accumulation runs over blocks in ascending order with one fused
+ * multiply-add per block; exp is a fixed fp32 algorithm (below) so that the
+ * integer decisions it feeds are reproducible.
+ */
+#include "coli_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------
+ * exp(x) in fp32 (Cody & Waite, "Software Manual for the Elementary
+ * Functions", 1980: argument reduction by n*ln2 with ln2 split in a high
+ * part that has trailing zero bits and a low part).  x is clamped to
+ * [-87, 88.5] so every result is a normal float; n = rint(x*log2(e));
+ * r = x - n*ln2 with |r| <= ln2/2; e^r by its Taylor series to degree 7
+ * (truncation < 6e-9, below half an ulp) in Horner form with fmaf; the
+ * result is scaled by 2^n.
+ */
+float orc_expf(float x) {
+  if (x > 88.5f) x = 88.5f;
+  if (x < -87.0f) x = -87.0f;
+  const float n = rintf(x * 1.44269504088896341f);
+  float r = fmaf(-n, 0.693145751953125f, x);       /* ln2 high part, 16 bits */
+  r = fmaf(-n, 1.42860676533018708e-06f, r);       /* ln2 - high part        */
+  float p = 1.98412698412698413e-04f;              /* 1/7! */
+  p = fmaf(p, r, 1.38888888888888889e-03f);        /* 1/6! */
+  p = fmaf(p, r, 8.33333333333333333e-03f);        /* 1/5! */
+  p = fmaf(p, r, 4.16666666666666667e-02f);        /* 1/4! */
+  p = fmaf(p, r, 1.66666666666666667e-01f);        /* 1/3! */
+  p = fmaf(p, r, 0.5f);                            /* 1/2! */
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)n);
+}
+
+/* sigma(x) = 1 / (1 + e^-x): the sigmoid score of the router. */
+float orc_sigmoidf(float x) { return 1.0f / (1.0f + orc_expf(-x)); }
+
+/* silu(g) = g / (1 + e^-g): the SwiGLU gate activation. */
+float orc_siluf(float g) { return g / (1.0f + orc_expf(-g)); }
+
+void orc_expf_vec(const float* x, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_expf(x[i]);
+}
+void orc_sigmoidf_vec(const float* x, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_sigmoidf(x[i]);
+}
+void orc_siluf_vec(const float* x, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_siluf(x[i]);
+}
+
+/* ------------------------------------------------------------------------
+ * Q8_0 activation quantisation, per block of 32: d = max|x| / 127 (fp32,
+ * correctly rounded), q = lrintf(x / d) (round half to even, the rounding
+ * the pages name for the int4 conversion), clamped to [-127, 127]; an
+ * all-zero block gets d = 0 and q = 0.
+ */
+void orc_q8_quant(const float* x, int64_t n, int8_t* q, float* d) {
+  for (int64_t b = 0; b < n / 32; ++b) {
+    const float* xb = x + 32 * b;
+    float amax = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+      const float a = fabsf(xb[j]);
+      if (a > amax) amax = a;
+    }
+    const float db = amax / 127.0f;
+    d[b] = db;
+    for (int j = 0; j < 32; ++j) {
+      long v = 0;
+      if (db != 0.0f) v = lrintf(xb[j] / db);
+      if (v > 127) v = 127;
+      if (v < -127) v = -127;
+      q[32 * b + j] = (int8_t)v;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Per-row symmetric int4 (aitrends.kr "GLM-5.2-colibri-int4": per-row F32
+ * scale, np.rint matching the engine's lrintf): s = max|w| / 7,
+ * q = lrintf(w / s) clamped to [-7, 7]; an all-zero row gets s = 0, q = 0.
+ */
+void orc_q4_quant_row(const float* w, int64_t k, int8_t* q, float* s) {
+  float amax = 0.0f;
+  for (int64_t j = 0; j < k; ++j) {
+    const float a = fabsf(w[j]);
+    if (a > amax) amax = a;
+  }
+  const float sc = amax / 7.0f;
+  *s = sc;
+  for (int64_t j = 0; j < k; ++j) {
+    long v = 0;
+    if (sc != 0.0f) v = lrintf(w[j] / sc);
+    if (v > 7) v = 7;
+    if (v < -7) v = -7;
+    q[j] = (int8_t)v;
+  }
+}
+
+/* Signed nibbles packed two per U8 byte, low nibble = even column. */
+void orc_pack_q4(const int8_t* q, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n / 2; ++i)
+    out[i] = (uint8_t)(((uint8_t)q[2 * i] & 0x0F) | (((uint8_t)q[2 * i + 1] & 0x0F) << 4));
+}
+
+/* Two's-complement nibble n -> n - 16 if n >= 8. */
+void orc_unpack_q4(const uint8_t* in, int64_t n, int8_t* q) {
+  for (int64_t i = 0; i < n / 2; ++i) {
+    const int lo = in[i] & 0x0F, hi = in[i] >> 4;
+    q[2 * i] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+    q[2 * i + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+  }
+}
+
+void orc_q4_quant(const float* w, int64_t rows, int64_t k, uint8_t* packed, float* s) {
+#pragma omp parallel
+  {
+    int8_t* q = (int8_t*)malloc((size_t)k);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      orc_q4_quant_row(w + r * k, k, q, s + r);
+      orc_pack_q4(q, k, packed + r * (k / 2));
+    }
+    free(q);
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Sigmoid top-k routing (DeepSeek-V3 style, jeff.news attention-and-kernels
+ * section).  Per token: s_e = sigma(logit_e); the selection score is
+ * c_e = s_e + bias_e (the bias steers selection only); the k largest c are
+ * taken, a tie going to the lower expert index, listed in descending c;
+ * the routing weights are w_j = (s_idx_j / sum) * routed_scale where sum
+ * adds the selected s in that order in fp32.
+ */
+void orc_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+               float routed_scale, int32_t* idx, float* w) {
+  float* s = (float*)malloc(sizeof(float) * (size_t)E);
+  float* c = (float*)malloc(sizeof(float) * (size_t)E);
+  char* taken = (char*)malloc((size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e) {
+      s[e] = orc_sigmoidf(logits[t * E + e]);
+      c[e] = s[e] + bias[e];
+      taken[e] = 0;
+    }
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || c[e] > c[best]) best = e;
+      }
+      taken[best] = 1;
+      idx[t * k + j] = best;
+    }
+    float sum = 0.0f;
+    for (int32_t j = 0; j < k; ++j) sum = sum + s[idx[t * k + j]];
+    for (int32_t j = 0; j < k; ++j) w[t * k + j] = (s[idx[t * k + j]] / sum) * routed_scale;
+  }
+  free(s);
+  free(c);
+  free(taken);
+}
+
+/* ------------------------------------------------------------------------
+ * Integer dot of one packed int4 row with a Q8 vector, per block of 32:
+ * P_b = sum_j q_w * q_x, exact in int32 (|P_b| <= 32*8*127).
+ */
+void orc_row_partials(const uint8_t* wrow, const int8_t* xq, int64_t k, int32_t* P) {
+  for (int64_t b = 0; b < k / 32; ++b) {
+    int32_t acc = 0;
+    for (int j = 0; j < 16; ++j) {
+      const uint8_t byte = wrow[16 * b + j];
+      const int lo = byte & 0x0F, hi = byte >> 4;
+      const int w0 = lo >= 8 ? lo - 16 : lo, w1 = hi >= 8 ? hi - 16 : hi;
+      acc += w0 * (int32_t)xq[32 * b + 2 * j] + w1 * (int32_t)xq[32 * b + 2 * j + 1];
+    }
+    P[b] = acc;
+  }
+}
+
+/* Block rescale: acc = 0; acc = fmaf((float)P_b, d_b, acc) for b ascending;
+ * the row result is acc * s (the row's F32 scale). */
+float orc_rescale(const int32_t* P, const float* d, int64_t nb, float s) {
+  float acc = 0.0f;
+  for (int64_t b = 0; b < nb; ++b) acc = fmaf((float)P[b], d[b], acc);
+  return acc * s;
+}
+
+void orc_matvec(const uint8_t* Wq, const float* Ws, int64_t rows, int64_t k,
+                const int8_t* xq, const float* xd, float* y, int32_t* P, double* absterm) {
+  const int64_t nb = k / 32;
+#pragma omp parallel
+  {
+    int32_t* Pl = (int32_t*)malloc(sizeof(int32_t) * (size_t)nb);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      orc_row_partials(Wq + r * (k / 2), xq, k, Pl);
+      y[r] = orc_rescale(Pl, xd, nb, Ws[r]);
+      if (P) memcpy(P + r * nb, Pl, sizeof(int32_t) * (size_t)nb);
+      if (absterm) {
+        double m = 0.0;
+        for (int64_t b = 0; b < nb; ++b) m += fabs((double)Ws[r] * (double)xd[b] * (double)Pl[b]);
+        absterm[r] = m;
+      }
+    }
+    free(Pl);
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * One SwiGLU expert: g = W_gate x, u = W_up x (both from the Q8 token),
+ * h = silu(g) * u, (hq, hd) = Q8_0(h), o = W_down hq.
+ */
+void orc_expert(const uint8_t* gate_q, const float* gate_s, const uint8_t* up_q,
+                const float* up_s, const uint8_t* down_q, const float* down_s, int64_t D,
+                int64_t F, const int8_t* xq, const float* xd, float* g, float* u, float* h,
+                int8_t* hq, float* hd, float* o, int32_t* P_gate, int32_t* P_up,
+                int32_t* P_down, double* abs_down) {
+  orc_matvec(gate_q, gate_s, F, D, xq, xd, g, P_gate, NULL);
+  orc_matvec(up_q, up_s, F, D, xq, xd, u, P_up, NULL);
+  for (int64_t r = 0; r < F; ++r) h[r] = orc_siluf(g[r]) * u[r];
+  orc_q8_quant(h, F, hq, hd);
+  orc_matvec(down_q, down_s, D, F, hq, hd, o, P_down, abs_down);
+}
+
+/* ------------------------------------------------------------------------
+ * The MoE layer, token by token: y = o_shared (0 without a shared expert),
+ * then y = fmaf(w_j, o_idx_j, y) for j = 0..k-1; out = y or out + y.
+ */
+int orc_moe_layer(const void* const* experts, int32_t E, int32_t S, int64_t D, int64_t F,
+                  int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
+                  const float* w, int32_t k, float* out, int accumulate, double* absterm) {
+  float* g = (float*)malloc(sizeof(float) * (size_t)F);
+  float* u = (float*)malloc(sizeof(float) * (size_t)F);
+  float* h = (float*)malloc(sizeof(float) * (size_t)F);
+  int8_t* hq = (int8_t*)malloc((size_t)F);
+  float* hd = (float*)malloc(sizeof(float) * (size_t)(F / 32));
+  float* o = (float*)malloc(sizeof(float) * (size_t)D);
+  float* y = (float*)malloc(sizeof(float) * (size_t)D);
+  double* m = (double*)malloc(sizeof(double) * (size_t)D);
+  double* my = (double*)malloc(sizeof(double) * (size_t)D);
+  int rc = 0;
+  for (int64_t t = 0; t < T && rc == 0; ++t) {
+    const int8_t* xt = xq + t * D;
+    const float* dt = xd + t * (D / 32);
+    for (int64_t r = 0; r < D; ++r) { y[r] = 0.0f; my[r] = 0.0; }
+    for (int32_t j = -S; j < k; ++j) {   /* j = -1: the shared expert first */
+      const int32_t e = j < 0 ? E : idx[t * k + j];
+      if (e < 0 || e >= E + S) { rc = -1; break; }
+      const void* const* ex = experts + 6 * (int64_t)e;
+      if (!ex[0] || !ex[1] || !ex[2] || !ex[3] || !ex[4] || !ex[5]) { rc = -1; break; }
+      orc_expert((const uint8_t*)ex[0], (const float*)ex[1], (const uint8_t*)ex[2],
+                 (const float*)ex[3], (const uint8_t*)ex[4], (const float*)ex[5], D, F, xt, dt,
+                 g, u, h, hq, hd, o, NULL, NULL, NULL, m);
+      if (j < 0) {
+        for (int64_t r = 0; r < D; ++r) { y[r] = o[r]; my[r] = m[r]; }
+      } else {
+        const float wj = w[t * k + j];
+        for (int64_t r = 0; r < D; ++r) {
+          y[r] = fmaf(wj, o[r], y[r]);
+          my[r] += fabs((double)wj) * m[r];
+        }
+      }
+    }
+    for (int64_t r = 0; r < D; ++r) {
+      out[t * D + r] = accumulate ? out[t * D + r] + y[r] : y[r];
+      if (absterm) absterm[t * D + r] = my[r];
+    }
+  }
+  free(g); free(u); free(h); free(hq); free(hd); free(o); free(y); free(m); free(my);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * RMSNorm with unit gain (norm weights are F32 on the pages; the deep stack
+ * uses gain 1): ss = sum h_i^2 in fp64 (each square exact), r =
+ * (float)(1 / sqrt(ss / D + eps)) computed in fp64, out_i = h_i * r in fp32.
+ */
+void orc_rmsnorm(const float* h, int64_t T, int64_t D, float eps, float* out, float* r_out) {
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < D; ++i) ss += (double)h[t * D + i] * (double)h[t * D + i];
+    const float r = (float)(1.0 / sqrt(ss / (double)D + (double)eps));
+    if (r_out) r_out[t] = r;
+    for (int64_t i = 0; i < D; ++i) out[t * D + i] = h[t * D + i] * r;
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * Batch-union dispatch: the expert-major view of the routing so that each
+ * selected expert's weights are read once per pass.
+ */
+int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
+                 int32_t* counts, int32_t* lists, int32_t* n_active, int32_t* active) {
+  for (int32_t e = 0; e < E + S; ++e) counts[e] = 0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t j = 0; j < k; ++j) {
+      if (idx[t * k + j] < 0 || idx[t * k + j] >= E) return -1;
+      for (int32_t i = 0; i < j; ++i)
+        if (idx[t * k + i] == idx[t * k + j]) return -1;   /* top-k never repeats */
+    }
+  for (int32_t e = 0; e < E + S; ++e) {
+    for (int64_t t = 0; t < T; ++t) {
+      if (e == E) {
+        lists[(int64_t)e * T + counts[e]++] = (int32_t)(t * (k + S) + k);
+        continue;
+      }
+      for (int32_t j = 0; j < k; ++j)
+        if (idx[t * k + j] == e) lists[(int64_t)e * T + counts[e]++] = (int32_t)(t * (k + S) + j);
+    }
+  }
+  int32_t na = 0;
+  for (int32_t e = 0; e < E + S; ++e)
+    if (counts[e] > 0) active[na++] = e;
+  *n_active = na;
+  return 0;
+}
