@@ -1,0 +1,218 @@
+/*
+ * coli.h - C ABI of the MI355X (gfx950) routed int4 MoE FFN library.
+ *
+ * The method (colibri, as described on the discuss.pytorch.kr, jeff.news,
+ * alphamatch.ai and aitrends.kr pages about it): a DeepSeek-V3-style sigmoid
+ * top-k router with a selection bias picks k of E routed experts per token;
+ * activations are quantised Q8_0 style to int8; every expert is a SwiGLU FFN
+ * whose int4 weights (signed nibbles packed in U8, one F32 scale per row,
+ * rounded with lrintf half-to-even) are multiplied against the int8
+ * activations with an integer dot product; the expert outputs are combined
+ * with the normalised routing weights plus one always-on shared expert;
+ * tokens that share a pass are grouped by expert (batch union) so that each
+ * selected expert's weights are read once.
+ *
+ * Conventions for every entry point:
+ *  - Bulk arrays (f32 inputs of the quantisers, packed weights, table arrays,
+ *    workspace) must be 16-byte aligned, every other pointer 4-byte aligned
+ *    (torch allocations are); misaligned pointers return COLI_E_INVAL.
+ *  - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
+ *    owned by the caller; the library never allocates, frees or keeps them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; nothing synchronises the host except
+ *    coli_moe_status(), which is documented as synchronising.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failed check returns a negative coli_status and enqueues nothing.
+ *    A failed launch returns COLI_E_HIP (see coli_last_hip_error()).
+ *  - Row-major layouts; int64 sizes; all shapes in elements.
+ *  - Results are a deterministic function of the inputs (bit-reproducible).
+ *
+ * Numerics (identical op order to the oracle, so integers, quantised values
+ * and the fp32 decode outputs match it bit for bit):
+ *  - Q8_0: per block of 32 values, d = max|x| / 127.0f (IEEE division),
+ *    q = clamp(rint_half_even(x / d), -127, 127); d == 0 gives q = 0.
+ *  - int4 rows: s = max|w| / 7.0f, q = clamp(rint_half_even(w / s), -7, 7).
+ *  - Dot of a packed row with a Q8 vector: int32 block partials
+ *    P_b = sum_32 q_w q_x; acc = 0; acc = fmaf((float)P_b, d_b, acc) for b
+ *    ascending; y = acc * s_row.
+ *  - exp is a fixed fp32 algorithm (Cody-Waite reduction by ln2 split into
+ *    0.693145751953125 + 1.42860676533018708e-6, degree-7 Taylor in Horner
+ *    form with fmaf, input clamped to [-87, 88.5]); sigmoid(x) =
+ *    1 / (1 + exp(-x)); silu(g) = g / (1 + exp(-g)).
+ */
+#ifndef COLI_H
+#define COLI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COLI_OK = 0,
+  COLI_E_INVAL = -1,     /* null pointer or out-of-range scalar argument      */
+  COLI_E_SHAPE = -2,     /* a size is not a multiple the layout needs, or too big */
+  COLI_E_WORKSPACE = -3, /* workspace smaller than coli_moe_workspace_bytes()  */
+  COLI_E_DEVICE = -4,    /* the current device is not gfx950                   */
+  COLI_E_HIP = -5,       /* a HIP runtime call failed                          */
+  COLI_E_INDEX = -6      /* an expert index was outside [0, E) or repeated     */
+} coli_status;
+
+/* Limits of this build. */
+#define COLI_MAX_EXPERTS 256 /* routed experts per layer                    */
+#define COLI_MAX_TOPK 64     /* experts selected per token                  */
+
+/* ------------------------------------------------------------------------
+ * Device-resident expert table of one MoE layer.
+ *
+ * The pages' container is row-major U8 nibbles plus a per-row F32 scale file
+ * (aitrends.kr "GLM-5.2-colibri-int4", section "기술적 특징"); coli_quant_weight_q4
+ * produces exactly that.  The table holds the same codes re-laid for the
+ * gfx950 GEMV: every 64-lane wavefront load of 1 KB brings one 16-byte,
+ * 32-column chunk of 64 different rows, so each lane owns one row and runs
+ * its block accumulation in order without cross-lane traffic.
+ *
+ *   gu_q  [E+S][F/32][D/32][64][16] bytes.  Group g, block b, lane l holds
+ *         columns 32b..32b+31 of gate row 32g+l (l < 32) or up row
+ *         32g+l-32 (l >= 32).
+ *   gu_s  [E+S][F/32][64] f32, the row scales in the same lane order.
+ *   dn_q  [E+S][D/64][F/32][64][16] bytes.  Group g, block b, lane l holds
+ *         columns 32b..32b+31 of down row 64g+l.
+ *   dn_s  [E+S][D] f32.
+ *
+ * Within a 16-byte chunk, 32-bit word k (0..3) holds columns 8k..8k+7 of
+ * the block: byte j (0..3) has column 8k+j in its low nibble and column
+ * 8k+4+j in its high nibble; each nibble stores q + 8 (0..15).
+ * The shared expert (when S = 1) is index E.  E <= 256, S in {0, 1},
+ * D % 64 == 0, F % 32 == 0.
+ */
+typedef struct {
+  int32_t n_routed; /* E */
+  int32_t n_shared; /* S */
+  int32_t d_model;  /* D */
+  int32_t d_ff;     /* F */
+  uint8_t* gu_q;
+  float* gu_s;
+  uint8_t* dn_q;
+  float* dn_s;
+} coli_expert_table;
+
+/* Sizes in bytes of the four table arrays for (E, S, D, F).  Returns the
+ * total, or 0 for an unsupported shape.  Output pointers may be NULL. */
+size_t coli_table_bytes(int32_t n_routed, int32_t n_shared, int64_t d_model, int64_t d_ff,
+                        size_t* gu_q, size_t* gu_s, size_t* dn_q, size_t* dn_s);
+
+/* Copies one expert, given as the pages' canonical containers (device
+ * pointers: gate_q, up_q [F][D/2] bytes with scales [F]; down_q [D][F/2]
+ * with scales [D]; low nibble = even column, two's complement), into slot
+ * `expert` (0..E+S-1) of the table.  The codes are unchanged; only their
+ * placement and nibble encoding change (see above). */
+int coli_table_set_expert(const coli_expert_table* table, int32_t expert, const uint8_t* gate_q,
+                          const float* gate_s, const uint8_t* up_q, const float* up_s,
+                          const uint8_t* down_q, const float* down_s, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Q8_0 activation quantisation (discuss.pytorch.kr colibri summary, section
+ * "colibri의 주요 기능": int8 activations, Q8_0 style; jeff.news, kernel
+ * section).  x [rows][k] f32 -> q [rows][k] int8, d [rows][k/32] f32.
+ * k % 32 == 0.  rows may be 0 (no work). */
+int coli_quant_act_q8(const float* x, int64_t rows, int64_t k, int8_t* q, float* d, void* stream);
+
+/* Per-row symmetric int4 quantisation into the pages' container
+ * (aitrends.kr "GLM-5.2-colibri-int4": per-row F32 scale, np.rint/lrintf).
+ * w [rows][k] f32 -> q [rows][k/2] bytes (low nibble = even column, two's
+ * complement) and s [rows] f32.  k % 32 == 0. */
+int coli_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, float* s,
+                         void* stream);
+
+/* Fused RMSNorm (unit gain) + Q8_0 of the normalised vector, for a pre-norm
+ * residual stack (router and norm stay F32: aitrends.kr, "알아두면 좋은 것").
+ * Per row: ss = sum h^2 accumulated in fp64, r = (float)(1/sqrt(ss/D + eps))
+ * in fp64, xhat = h * r in fp32, then Q8_0 of xhat.  h [T][D] f32 -> q [T][D],
+ * d [T][D/32]; r_out [T] (may be NULL) receives r.  D % 32 == 0, eps >= 0. */
+int coli_rmsnorm_q8(const float* h, int64_t T, int64_t D, float eps, int8_t* q, float* d,
+                    float* r_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sigmoid top-k routing, DeepSeek-V3 style (jeff.news, attention-and-kernels
+ * section; 8 of 256 experts per token).  Per token: s_e = sigmoid(logit_e);
+ * selection score c_e = s_e + bias_e; the k largest c are chosen, a tie
+ * going to the lower expert index, and listed in descending c; weights
+ * w_j = (s_j / sum) * routed_scale with sum the fp32 sum of the selected s
+ * in that order.  logits [T][E] f32, bias [E] f32 (NULL = no bias) ->
+ * idx [T][k] int32, w [T][k] f32.  1 <= E <= 256, 1 <= k <= min(E, 64). */
+int coli_route_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                    float routed_scale, int32_t* idx, float* w, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Batch-union dispatch (alphamatch.ai page, "기술적 우수성": prefill groups
+ * tokens by expert; discuss.pytorch.kr: the batched verify pass).  From
+ * idx [T][k] builds, for every expert e in [0, E+S): counts[e] and
+ * lists[e][0..counts[e]) (row stride T) of pair ids p = t*(k+S) + slot in
+ * ascending token order, the shared expert E taking slot k of every token;
+ * active[0..*n_active) = experts with counts > 0, ascending.  Indices outside
+ * [0, E) or repeated within a token are dropped and set *err to COLI_E_INDEX
+ * (else *err = 0).  counts [E+S], lists [E+S][T], n_active [1],
+ * active [E+S], err [1]: int32 device arrays. */
+int coli_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
+                  int32_t* counts, int32_t* lists, int32_t* n_active, int32_t* active,
+                  int32_t* err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The MoE FFN forward over a device-resident table.
+ *   xq [T][D] int8, xd [T][D/32] f32: the Q8_0 tokens.
+ *   idx [T][k] int32, w [T][k] f32: the routing (coli_route_topk).
+ *   y [T][D] f32: y = moe (accumulate = 0) or y + moe (accumulate = 1), with
+ *   moe = o_shared + sum_j w_j o_idx_j accumulated as y = fmaf(w_j, o_j, y)
+ *   in slot order after the shared expert.
+ * Each expert: g = W_gate x, u = W_up x, h = silu(g) u, (hq, hd) = Q8_0(h),
+ * o = W_down hq.  The workspace (caller-owned, device memory) must hold
+ * coli_moe_workspace_bytes(table, T, k) bytes; its contents need no
+ * initialisation and are clobbered.  Calls that share a workspace must not
+ * overlap.  An invalid expert index does not fault: its slot contributes
+ * nothing and coli_moe_status() reports COLI_E_INDEX. */
+size_t coli_moe_workspace_bytes(const coli_expert_table* table, int64_t T, int32_t k);
+
+int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                     int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                     int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/* Intermediate dumps for testing; every pointer may be NULL (not written).
+ * Pair p = t*(k+S) + slot indexes per-(token, slot) arrays; pairs with an
+ * invalid index are left unwritten. */
+typedef struct {
+  int32_t* counts;   /* [E+S]                    dispatch counts      */
+  int32_t* lists;    /* [E+S][T]                 dispatch lists       */
+  int32_t* n_active; /* [1]                                            */
+  int32_t* active;   /* [E+S]                                          */
+  int32_t* p_gate;   /* [T*(k+S)][F][D/32]       int32 block partials */
+  int32_t* p_up;     /* [T*(k+S)][F][D/32]                             */
+  int32_t* p_down;   /* [T*(k+S)][D][F/32]                             */
+  float* g;          /* [T*(k+S)][F]                                   */
+  float* u;          /* [T*(k+S)][F]                                   */
+  float* h;          /* [T*(k+S)][F]                                   */
+  int8_t* hq;        /* [T*(k+S)][F]                                   */
+  float* hd;         /* [T*(k+S)][F/32]                                */
+  float* o;          /* [T*(k+S)][D]             expert outputs       */
+} coli_moe_trace;
+
+int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                            int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                            int accumulate, void* workspace, size_t ws_bytes,
+                            const coli_moe_trace* trace, void* stream);
+
+/* Synchronises `stream`, then reports the device-side index check of the
+ * last forward that used `workspace`: COLI_OK or COLI_E_INDEX. */
+int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+const char* coli_status_string(int status);
+/* hipError_t of the most recent COLI_E_HIP on the calling thread. */
+int coli_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

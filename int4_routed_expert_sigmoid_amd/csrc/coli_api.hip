@@ -1,0 +1,282 @@
+// C ABI of the gfx950 routed int4 MoE library: argument validation on the
+// host (before anything is enqueued), device check, workspace layout and the
+// calls into the kernel launchers.  No entry point allocates memory.
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "coli_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return COLI_E_HIP;
+}
+
+// Per-device memo of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_device_ok[64];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return COLI_E_DEVICE;
+  }
+  if (dev < 0 || dev >= 64) return COLI_E_DEVICE;
+  int st = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return COLI_E_DEVICE;
+    }
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? COLI_OK : COLI_E_DEVICE;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// The kernels use 16-byte vector accesses on bulk arrays and 4-byte scalar
+// loads elsewhere; misaligned pointers are rejected instead of faulting.
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+int table_check(const coli_expert_table* t) {
+  if (!t) return COLI_E_INVAL;
+  if (t->n_routed < 1 || t->n_routed > COLI_MAX_EXPERTS) return COLI_E_SHAPE;
+  if (t->n_shared < 0 || t->n_shared > 1) return COLI_E_SHAPE;
+  if (t->d_model <= 0 || t->d_model % 64 != 0 || t->d_ff <= 0 || t->d_ff % 32 != 0)
+    return COLI_E_SHAPE;
+  if (!t->gu_q || !t->gu_s || !t->dn_q || !t->dn_s) return COLI_E_INVAL;
+  if (!al16(t->gu_q) || !al16(t->dn_q) || !al4(t->gu_s) || !al4(t->dn_s)) return COLI_E_INVAL;
+  return COLI_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+
+}  // namespace
+
+namespace coli {
+
+MoeWorkspace moe_workspace_layout(void* base, int E, int S, int64_t D, int64_t F, int64_t T,
+                                  int k) {
+  MoeWorkspace w = {};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  const size_t A = (size_t)(E + S), P = (size_t)T * (size_t)(k + S);
+  w.err = static_cast<int32_t*>(take(sizeof(int32_t)));   // first: coli_moe_status reads it
+  w.n_active = static_cast<int32_t*>(take(sizeof(int32_t)));
+  w.counts = static_cast<int32_t*>(take(sizeof(int32_t) * A));
+  w.active = static_cast<int32_t*>(take(sizeof(int32_t) * A));
+  w.lists = static_cast<int32_t*>(take(sizeof(int32_t) * A * (size_t)T));
+  w.xsum8 = static_cast<int32_t*>(take(sizeof(int32_t) * (size_t)T * (size_t)(D / 32)));
+  w.hq = static_cast<int8_t*>(take(P * (size_t)F));
+  w.hd = static_cast<float*>(take(sizeof(float) * P * (size_t)(F / 32)));
+  w.hsum8 = static_cast<int32_t*>(take(sizeof(int32_t) * P * (size_t)(F / 32)));
+  w.o = static_cast<float*>(take(sizeof(float) * P * (size_t)D));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace coli
+
+extern "C" {
+
+const char* coli_status_string(int status) {
+  switch (status) {
+    case COLI_OK: return "ok";
+    case COLI_E_INVAL: return "invalid argument (null pointer or scalar out of range)";
+    case COLI_E_SHAPE: return "unsupported shape";
+    case COLI_E_WORKSPACE: return "workspace too small";
+    case COLI_E_DEVICE: return "current device is not gfx950 (or no device)";
+    case COLI_E_HIP: return "HIP runtime error";
+    case COLI_E_INDEX: return "expert index out of range or repeated within a token";
+    default: return "unknown status";
+  }
+}
+
+int coli_last_hip_error(void) { return g_last_hip_error; }
+
+size_t coli_table_bytes(int32_t E, int32_t S, int64_t D, int64_t F, size_t* gu_q, size_t* gu_s,
+                        size_t* dn_q, size_t* dn_s) {
+  if (E < 1 || E > COLI_MAX_EXPERTS || S < 0 || S > 1 || D <= 0 || D % 64 || F <= 0 || F % 32)
+    return 0;
+  const size_t n = (size_t)(E + S);
+  const size_t a = n * (size_t)(D * F), b = n * (size_t)(2 * F) * sizeof(float),
+               c = n * (size_t)(D * F / 2), d = n * (size_t)D * sizeof(float);
+  if (gu_q) *gu_q = a;
+  if (gu_s) *gu_s = b;
+  if (dn_q) *dn_q = c;
+  if (dn_s) *dn_s = d;
+  return a + b + c + d;
+}
+
+int coli_table_set_expert(const coli_expert_table* table, int32_t expert, const uint8_t* gate_q,
+                          const float* gate_s, const uint8_t* up_q, const float* up_s,
+                          const uint8_t* down_q, const float* down_s, void* stream) {
+  int rc = table_check(table);
+  if (rc) return rc;
+  if (expert < 0 || expert >= table->n_routed + table->n_shared) return COLI_E_INVAL;
+  if (!gate_q || !gate_s || !up_q || !up_s || !down_q || !down_s) return COLI_E_INVAL;
+  if (!al16(gate_q) || !al16(up_q) || !al16(down_q) || !al4(gate_s) || !al4(up_s) ||
+      !al4(down_s))
+    return COLI_E_INVAL;
+  if ((rc = check_device())) return rc;
+  hipError_t e = coli::launch_table_set_expert(*table, expert, gate_q, gate_s, up_q, up_s, down_q,
+                                               down_s, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_quant_act_q8(const float* x, int64_t rows, int64_t k, int8_t* q, float* d, void* stream) {
+  if (rows < 0 || k <= 0) return COLI_E_SHAPE;
+  if (k % 32) return COLI_E_SHAPE;
+  if (rows == 0) return COLI_OK;
+  if (!x || !q || !d) return COLI_E_INVAL;
+  if (!al16(x) || !al4(q) || !al4(d)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_quant_act_q8(x, rows, k, q, d, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, float* s,
+                         void* stream) {
+  if (rows < 0 || k <= 0 || k % 32) return COLI_E_SHAPE;
+  if (rows > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (rows == 0) return COLI_OK;
+  if (!w || !q || !s) return COLI_E_INVAL;
+  if (!al16(w) || !al4(q) || !al4(s)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_quant_weight_q4(w, rows, k, q, s, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_rmsnorm_q8(const float* h, int64_t T, int64_t D, float eps, int8_t* q, float* d,
+                    float* r_out, void* stream) {
+  if (T < 0 || D <= 0 || D % 32 || T > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (!(eps >= 0.0f) || std::isinf(eps)) return COLI_E_INVAL;
+  if (T == 0) return COLI_OK;
+  if (!h || !q || !d) return COLI_E_INVAL;
+  if (!al16(h) || !al4(q) || !al4(d) || !al4(r_out)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_rmsnorm_q8(h, T, D, eps, q, d, r_out, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_route_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                    float routed_scale, int32_t* idx, float* w, void* stream) {
+  if (E < 1 || E > COLI_MAX_EXPERTS) return COLI_E_SHAPE;
+  if (k < 1 || k > E || k > COLI_MAX_TOPK) return COLI_E_SHAPE;
+  if (T < 0 || T > 0x7FFFFFFF / 4) return COLI_E_SHAPE;
+  if (!std::isfinite(routed_scale)) return COLI_E_INVAL;
+  if (T == 0) return COLI_OK;
+  if (!logits || !idx || !w) return COLI_E_INVAL;
+  if (!al4(logits) || !al4(bias) || !al4(idx) || !al4(w)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_route_topk(logits, bias, T, E, k, routed_scale, idx, w,
+                                         as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S, int32_t* counts,
+                  int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
+                  void* stream) {
+  if (E < 1 || E > COLI_MAX_EXPERTS || S < 0 || S > 1) return COLI_E_SHAPE;
+  if (k < 1 || k > E || k > COLI_MAX_TOPK) return COLI_E_SHAPE;
+  if (T < 0 || T * (int64_t)(k + S) > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (!counts || !lists || !n_active || !active || !err || (T > 0 && !idx)) return COLI_E_INVAL;
+  if (!al4(idx) || !al4(counts) || !al4(lists) || !al4(n_active) || !al4(active) || !al4(err))
+    return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_dispatch(idx, T, k, E, S, counts, lists, n_active, active, err,
+                                       nullptr, 0, nullptr, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+size_t coli_moe_workspace_bytes(const coli_expert_table* table, int64_t T, int32_t k) {
+  if (!table || T < 0 || k < 1) return 0;
+  return coli::moe_workspace_layout(nullptr, table->n_routed, table->n_shared, table->d_model,
+                                    table->d_ff, T, k)
+      .bytes;
+}
+
+static int forward_impl(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                        int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                        int accumulate, void* workspace, size_t ws_bytes,
+                        const coli_moe_trace* trace, void* stream) {
+  int rc = table_check(table);
+  if (rc) return rc;
+  if (k < 1 || k > table->n_routed || k > COLI_MAX_TOPK) return COLI_E_SHAPE;
+  if (T < 0 || T * (int64_t)(k + table->n_shared) > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return COLI_E_INVAL;
+  if (T == 0) return COLI_OK;
+  if (!xq || !xd || !idx || !w || !y || !workspace) return COLI_E_INVAL;
+  if (!al4(xq) || !al4(xd) || !al4(idx) || !al4(w) || !al4(y) || !al16(workspace))
+    return COLI_E_INVAL;
+  const coli::MoeWorkspace ws = coli::moe_workspace_layout(
+      workspace, table->n_routed, table->n_shared, table->d_model, table->d_ff, T, k);
+  if (ws_bytes < ws.bytes) return COLI_E_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  coli::ForwardArgs a;
+  a.table = table;
+  a.xq = xq;
+  a.xd = xd;
+  a.T = T;
+  a.idx = idx;
+  a.w = w;
+  a.k = k;
+  a.y = y;
+  a.accumulate = accumulate;
+  a.ws = ws;
+  a.trace = trace;
+  hipError_t e = coli::launch_moe_forward(a, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const float* xd, int64_t T,
+                     const int32_t* idx, const float* w, int32_t k, float* y, int accumulate,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, nullptr,
+                      stream);
+}
+
+int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                            int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                            int accumulate, void* workspace, size_t ws_bytes,
+                            const coli_moe_trace* trace, void* stream) {
+  if (!trace) return COLI_E_INVAL;
+  return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, trace,
+                      stream);
+}
+
+int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || ws_bytes < sizeof(int32_t)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  int32_t err = 0;
+  hipError_t e = hipMemcpyAsync(&err, workspace, sizeof(err), hipMemcpyDeviceToHost,
+                                as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return err == 0 ? COLI_OK : COLI_E_INDEX;
+}
+
+}  // extern "C"

@@ -1,0 +1,439 @@
+// Decode / verify path: int4 x int8 GEMV over the batch-union expert set.
+//
+// The integer dot of int8 (Q8_0) activations with packed int4 weights is the
+// method's hot loop (discuss.pytorch.kr colibri summary, "colibri의 주요 기능";
+// jeff.news, kernel section: int4 wins in batch and loses for a single row on
+// the CPU, so the path is chosen per shape).  On gfx950 a decode token reads
+// every selected expert once from HBM, so these kernels are written to stream
+// the table at HBM speed:
+//
+//  - one 64-lane wavefront owns a row group (32 gate + 32 up rows, or 64 down
+//    rows); every load is one 1 KB coalesced dwordx4 per wavefront bringing
+//    block b of all 64 rows, lane l holding its own row's 32 nibbles;
+//  - the token's block (8 int8 words, its scale and its -8*sum) is uniform
+//    across the wavefront and comes through scalar loads, so the nibble
+//    unpack (3 ALU ops per word) feeds eight v_dot4_i32_i8 per block directly;
+//  - each lane runs its row's accumulation acc = fmaf(P_b, d_b, acc) over b
+//    in ascending order in registers: the exact op order of the numerics, with
+//    no cross-lane reduction;
+//  - a ring of PF outstanding 1 KB loads per wavefront keeps HBM busy;
+//  - every token that selected the expert (up to MAXT per pass) is served from
+//    the same weight load: the batch union of the alphamatch.ai page
+//    ("기술적 우수성").
+//
+// Nibbles are stored offset-binary (q + 8), so a dot with them is
+// sum (q+8) x = P + 8 sum x; the -8 sum x term is precomputed per block.
+//
+// The SwiGLU, the row scale and the Q8_0 re-quantisation of h are fused into
+// the gate/up epilogue; the routing-weighted combine runs as its own kernel in
+// slot order (shared expert first), which keeps it deterministic.
+#include "coli_internal.h"
+
+namespace coli {
+namespace {
+
+constexpr int kWave = 64;
+// Word 3 of a gfx9-family buffer descriptor for raw 32-bit-element access.
+constexpr int kBufferConfig = 0x00020000;
+
+struct GuArgs {
+  const uint4* gu_q;
+  const float* gu_s;
+  const int8_t* xq;
+  const float* xd;
+  const int32_t* xsum8;
+  const int32_t* counts;
+  const int32_t* lists;
+  const int32_t* n_active;
+  const int32_t* active;
+  int8_t* hq;
+  float* hd;
+  int32_t* hsum8;
+  int64_t T, D, F;
+  int k, S;
+  int32_t* tr_pg;
+  int32_t* tr_pu;
+  float* tr_g;
+  float* tr_u;
+  float* tr_h;
+};
+
+struct DnArgs {
+  const uint4* dn_q;
+  const float* dn_s;
+  const int8_t* hq;
+  const float* hd;
+  const int32_t* hsum8;
+  const int32_t* counts;
+  const int32_t* lists;
+  const int32_t* n_active;
+  const int32_t* active;
+  float* o;
+  int64_t T, D, F;
+  int k, S;
+  int32_t* tr_pd;
+};
+
+// The 32 offset-binary nibbles of one chunk, split into the 8 byte-vectors
+// that line up with the 8 int8 words of the activation block.
+struct Unpacked {
+  uint32_t v[8];
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
+  Unpacked u;
+  u.v[0] = w.x & 0x0F0F0F0Fu;
+  u.v[1] = (w.x >> 4) & 0x0F0F0F0Fu;
+  u.v[2] = w.y & 0x0F0F0F0Fu;
+  u.v[3] = (w.y >> 4) & 0x0F0F0F0Fu;
+  u.v[4] = w.z & 0x0F0F0F0Fu;
+  u.v[5] = (w.z >> 4) & 0x0F0F0F0Fu;
+  u.v[6] = w.w & 0x0F0F0F0Fu;
+  u.v[7] = (w.w >> 4) & 0x0F0F0F0Fu;
+  return u;
+}
+
+// One activation block of one token: 8 int8 words, -8 * sum, scale.
+struct XBlock {
+  int x[8];
+  int m8sum;
+  float d;
+};
+
+__device__ __forceinline__ XBlock load_xblock(cptr<int> xrow, cptr<int> srow, cptr<float> drow,
+                                              int b) {
+  XBlock v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v.x[i] = xrow[8 * b + i];
+  v.m8sum = srow[b];
+  v.d = drow[b];
+  return v;
+}
+
+// P_b of one row with one activation block: sum over 32 of q_w * q_x.
+__device__ __forceinline__ int block_dot(const Unpacked& u, const XBlock& xb) {
+  int s = xb.m8sum;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = sdot4((int)u.v[i], xb.x[i], s);
+  return s;
+}
+
+// Streams the NB chunks of one row group (lane-owned rows) and accumulates
+// exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
+// the ring of PF weight loads in flight: every refill is unconditional (its
+// index is clamped into the row group), the scalar loads of the next
+// activation block are issued one block ahead of use, and a block past the
+// end of the row (only when PF does not divide NB) is computed on clamped
+// data with scale 0, which leaves the accumulator bit-identical (it starts
+// at +0 and so is never -0).
+template <int NT, int PF, bool TRACE>
+__device__ __forceinline__ void stream_rows(const char* __restrict__ wbase, uint32_t loff, int NB,
+                                            const cptr<int>* xrow, const cptr<float>* drow,
+                                            const cptr<int>* srow, float* acc,
+                                            int32_t* const* trace_row) {
+  // Buffer loads: the row group is one descriptor (scalar registers), the
+  // lane's 16-byte column is a constant vector offset and the block is a
+  // scalar offset, so no per-load vector address is built.  Each ring slot
+  // is unpacked before it is refilled, letting the refill reuse the slot's
+  // registers: the ring stays PF loads deep across the loop back-edge.
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, NB * 1024, kBufferConfig);
+  u32x4 buf[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {   // issued in slot order, so slot 0 lands first
+    buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, (i < NB ? i : NB - 1) * 1024, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  XBlock cur[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) cur[j] = load_xblock(xrow[j], srow[j], drow[j], 0);
+  for (int b0 = 0; b0 < NB; b0 += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int b = b0 + i;
+      const Unpacked u = unpack_chunk(buf[i]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int bn = b + PF < NB ? b + PF : NB - 1;
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, bn * 1024, 0);
+      const int bx = b + 1 < NB ? b + 1 : NB - 1;
+      XBlock nxt[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) nxt[j] = load_xblock(xrow[j], srow[j], drow[j], bx);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int p = block_dot(u, cur[j]);
+        if (TRACE) {
+          if (trace_row[j] && b < NB) trace_row[j][b] = p;
+        }
+        const float d = b < NB ? cur[j].d : 0.0f;
+        acc[j] = __builtin_fmaf((float)p, d, acc[j]);
+        cur[j] = nxt[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Runs stream_rows for the nt (1..MAXT) tokens of one pass.
+template <int MAXT, int PF, bool TRACE>
+__device__ __forceinline__ void stream_pass(int nt, const char* __restrict__ wbase, uint32_t loff,
+                                            int NB,
+                                            const cptr<int>* xrow, const cptr<float>* drow,
+                                            const cptr<int>* srow, float* acc,
+                                            int32_t* const* trace_row) {
+  if (MAXT >= 8 && nt > 4) {
+    stream_rows<(MAXT >= 8 ? 8 : 1), PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+  } else if (MAXT >= 4 && nt > 2) {
+    stream_rows<(MAXT >= 4 ? 4 : 1), PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+  } else if (MAXT >= 2 && nt == 2) {
+    stream_rows<(MAXT >= 2 ? 2 : 1), PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+  } else {
+    stream_rows<1, PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+  }
+}
+
+template <int MAXT, int PF, bool TRACE>
+__global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
+  const int grp = blockIdx.x;
+  const int slot = blockIdx.y;
+  if (slot >= *as_const(a.n_active)) return;
+  const int e = as_const(a.active)[slot];
+  const int cnt = as_const(a.counts)[e];
+  const int lane = threadIdx.x;
+  const int NB = (int)(a.D / 32);
+  const int64_t G = a.F / 32;
+  const int KS = a.k + a.S;
+  const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)e * G + grp) * (size_t)NB * kWave);
+  const uint32_t loff = 16u * (uint32_t)lane;
+  const float rs = a.gu_s[((size_t)e * G + grp) * kWave + lane];
+  const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
+  for (int c0 = 0; c0 < cnt; c0 += MAXT) {
+    const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
+    int pair[MAXT];
+    cptr<int> xrow[MAXT];
+    cptr<float> drow[MAXT];
+    cptr<int> srow[MAXT];
+    int32_t* trow[MAXT];
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      pair[j] = list[c0 + (j < nt ? j : nt - 1)];
+      const int64_t tok = __builtin_amdgcn_readfirstlane(pair[j] / KS);
+      xrow[j] = as_const(reinterpret_cast<const int*>(a.xq + tok * a.D));
+      drow[j] = as_const(a.xd + tok * NB);
+      srow[j] = as_const(a.xsum8 + tok * NB);
+      trow[j] = nullptr;
+      if (TRACE) {
+        int32_t* base = lane < 32 ? a.tr_pg : a.tr_pu;
+        if (base) trow[j] = base + ((size_t)pair[j] * a.F + 32 * (size_t)grp + (lane & 31)) * NB;
+      }
+    }
+    float acc[MAXT];
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
+    stream_pass<MAXT, PF, TRACE>(nt, wbase, loff, NB, xrow, drow, srow, acc, trow);
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      if (j < nt) {
+        const float v = acc[j] * rs;              // g (lanes 0-31) or u (lanes 32-63)
+        const float up = __shfl_down(v, 32);      // lanes 0-31 receive their up row
+        const float h = silu_f32(v) * up;
+        float amax = fabsf(h);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+        const float d = amax / 127.0f;
+        const int q = q8_code(h, d);
+        int qs = q;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) qs += __shfl_xor(qs, off, 32);
+        const size_t p = (size_t)pair[j];
+        if (lane < 32) {
+          const size_t r = 32 * (size_t)grp + lane;
+          a.hq[p * a.F + r] = (int8_t)q;
+          if (lane == 0) {
+            a.hd[p * G + grp] = d;
+            a.hsum8[p * G + grp] = -8 * qs;
+          }
+          if (TRACE) {
+            if (a.tr_g) a.tr_g[p * a.F + r] = v;
+            if (a.tr_u) a.tr_u[p * a.F + r] = up;
+            if (a.tr_h) a.tr_h[p * a.F + r] = h;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MAXT, int PF, bool TRACE>
+__global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
+  const int grp = blockIdx.x;
+  const int slot = blockIdx.y;
+  if (slot >= *as_const(a.n_active)) return;
+  const int e = as_const(a.active)[slot];
+  const int cnt = as_const(a.counts)[e];
+  const int lane = threadIdx.x;
+  const int NB = (int)(a.F / 32);
+  const int KS = a.k + a.S;
+  const char* wbase =
+      reinterpret_cast<const char*>(a.dn_q + ((size_t)e * (a.D / 64) + grp) * (size_t)NB * kWave);
+  const uint32_t loff = 16u * (uint32_t)lane;
+  const size_t row = 64 * (size_t)grp + lane;
+  const float rs = a.dn_s[(size_t)e * a.D + row];
+  const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
+  for (int c0 = 0; c0 < cnt; c0 += MAXT) {
+    const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
+    int pair[MAXT];
+    cptr<int> xrow[MAXT];
+    cptr<float> drow[MAXT];
+    cptr<int> srow[MAXT];
+    int32_t* trow[MAXT];
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      pair[j] = list[c0 + (j < nt ? j : nt - 1)];
+      xrow[j] = as_const(reinterpret_cast<const int*>(a.hq + (size_t)pair[j] * a.F));
+      drow[j] = as_const(a.hd + (size_t)pair[j] * NB);
+      srow[j] = as_const(a.hsum8 + (size_t)pair[j] * NB);
+      trow[j] = (TRACE && a.tr_pd) ? a.tr_pd + ((size_t)pair[j] * a.D + row) * NB : nullptr;
+    }
+    float acc[MAXT];
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
+    stream_pass<MAXT, PF, TRACE>(nt, wbase, loff, NB, xrow, drow, srow, acc, trow);
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j)
+      if (j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
+  }
+  (void)KS;
+}
+
+// y[t][r] = o_shared + sum_j w_j o_j, as y = fmaf(w_j, o_j, y) in slot order.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
+                                                      const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ w, int64_t D,
+                                                      int k, int E, int S, float* __restrict__ y,
+                                                      int accumulate) {
+  const int64_t t = blockIdx.y;
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= D) return;
+  const int KS = k + S;
+  const float* ot = o + (size_t)t * KS * D;
+  float acc = S ? ot[(size_t)k * D + r] : 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e < 0 || e >= E) continue;
+    acc = __builtin_fmaf(w[t * k + j], ot[(size_t)j * D + r], acc);
+  }
+  float* yt = y + t * D + r;
+  *yt = accumulate ? *yt + acc : acc;
+}
+
+constexpr int kPfGateUp = 16;
+constexpr int kPfDown = 16;
+
+template <int MAXT, bool TRACE>
+hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, hipStream_t s) {
+  hipLaunchKernelGGL((gate_up_kernel<MAXT, kPfGateUp, TRACE>), dim3((unsigned)(g.F / 32), maxA),
+                     dim3(kWave), 0, s, g);
+  hipError_t rc = hipGetLastError();
+  if (rc != hipSuccess) return rc;
+  hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, TRACE>), dim3((unsigned)(d.D / 64), maxA),
+                     dim3(kWave), 0, s, d);
+  return hipGetLastError();
+}
+
+template <bool TRACE>
+hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, hipStream_t s) {
+  if (T <= 1) return launch_pair<1, TRACE>(g, d, maxA, s);
+  if (T <= 2) return launch_pair<2, TRACE>(g, d, maxA, s);
+  if (T <= 4) return launch_pair<4, TRACE>(g, d, maxA, s);
+  return launch_pair<8, TRACE>(g, d, maxA, s);
+}
+
+}  // namespace
+
+hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
+  const coli_expert_table& t = *f.table;
+  const int E = t.n_routed, S = t.n_shared;
+  const int64_t D = t.d_model, F = t.d_ff, T = f.T;
+  if (T == 0) return hipSuccess;
+  const MoeWorkspace& ws = f.ws;
+  hipError_t rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active,
+                                  ws.active, ws.err, f.xq, D, ws.xsum8, s);
+  if (rc != hipSuccess) return rc;
+  const int64_t maxA = (T * f.k < E ? T * f.k : E) + S;
+
+  GuArgs g = {};
+  g.gu_q = reinterpret_cast<const uint4*>(t.gu_q);
+  g.gu_s = t.gu_s;
+  g.xq = f.xq;
+  g.xd = f.xd;
+  g.xsum8 = ws.xsum8;
+  g.counts = ws.counts;
+  g.lists = ws.lists;
+  g.n_active = ws.n_active;
+  g.active = ws.active;
+  g.hq = ws.hq;
+  g.hd = ws.hd;
+  g.hsum8 = ws.hsum8;
+  g.T = T;
+  g.D = D;
+  g.F = F;
+  g.k = f.k;
+  g.S = S;
+  DnArgs d = {};
+  d.dn_q = reinterpret_cast<const uint4*>(t.dn_q);
+  d.dn_s = t.dn_s;
+  d.hq = ws.hq;
+  d.hd = ws.hd;
+  d.hsum8 = ws.hsum8;
+  d.counts = ws.counts;
+  d.lists = ws.lists;
+  d.n_active = ws.n_active;
+  d.active = ws.active;
+  d.o = ws.o;
+  d.T = T;
+  d.D = D;
+  d.F = F;
+  d.k = f.k;
+  d.S = S;
+  const coli_moe_trace* tr = f.trace;
+  if (tr) {
+    g.tr_pg = tr->p_gate;
+    g.tr_pu = tr->p_up;
+    g.tr_g = tr->g;
+    g.tr_u = tr->u;
+    g.tr_h = tr->h;
+    d.tr_pd = tr->p_down;
+    rc = launch_gemv<true>(g, d, (int)maxA, T, s);
+  } else {
+    rc = launch_gemv<false>(g, d, (int)maxA, T, s);
+  }
+  if (rc != hipSuccess) return rc;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((D + 255) / 256), (unsigned)T), dim3(256), 0,
+                     s, ws.o, f.idx, f.w, D, f.k, E, S, f.y, f.accumulate);
+  rc = hipGetLastError();
+  if (rc != hipSuccess || !tr) return rc;
+  // test dumps of the dispatch and of the workspace intermediates
+  const int64_t A = E + S, P = T * (f.k + S);
+  struct Copy { void* dst; const void* src; size_t n; };
+  const Copy copies[] = {
+      {tr->counts, ws.counts, sizeof(int32_t) * A},
+      {tr->lists, ws.lists, sizeof(int32_t) * A * T},
+      {tr->n_active, ws.n_active, sizeof(int32_t)},
+      {tr->active, ws.active, sizeof(int32_t) * A},
+      {tr->hq, ws.hq, (size_t)(P * F)},
+      {tr->hd, ws.hd, sizeof(float) * P * (F / 32)},
+      {tr->o, ws.o, sizeof(float) * P * D},
+  };
+  for (const Copy& c : copies) {
+    if (!c.dst) continue;
+    rc = hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s);
+    if (rc != hipSuccess) return rc;
+  }
+  return hipSuccess;
+}
+
+}  // namespace coli

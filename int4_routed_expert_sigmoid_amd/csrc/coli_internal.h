@@ -1,0 +1,119 @@
+// Internal declarations of the gfx950 library: device math shared by its
+// kernels and the host-side launchers called by the C ABI (coli_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "coli.h"
+
+namespace coli {
+
+// ---------------------------------------------------------------------------
+// Device math.  The fp32 op sequence is fixed (hipcc -ffp-contract=off; IEEE
+// division and square root; fmaf -> v_fma_f32; rintf -> v_rndne_f32) so that
+// every integer decision it feeds (top-k order, Q8 codes) is reproducible.
+
+// exp(x): Cody & Waite reduction (1980) by n*ln2, ln2 split into a 16-bit
+// high part and its remainder, |r| <= ln2/2, Taylor series of e^r to degree 7
+// in Horner form (truncation < half an ulp), scaled by 2^n.  The input is
+// clamped to [-87, 88.5] so results stay normal floats.
+__device__ __forceinline__ float exp_f32(float x) {
+  if (x > 88.5f) x = 88.5f;
+  if (x < -87.0f) x = -87.0f;
+  const float n = __builtin_rintf(x * 1.44269504088896341f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, x);
+  r = __builtin_fmaf(-n, 1.42860676533018708e-06f, r);
+  float p = 1.98412698412698413e-04f;
+  p = __builtin_fmaf(p, r, 1.38888888888888889e-03f);
+  p = __builtin_fmaf(p, r, 8.33333333333333333e-03f);
+  p = __builtin_fmaf(p, r, 4.16666666666666667e-02f);
+  p = __builtin_fmaf(p, r, 1.66666666666666667e-01f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + exp_f32(-x)); }
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + exp_f32(-g)); }
+
+// Q8_0 code of v in a block whose scale is d (d == 0: code 0).
+__device__ __forceinline__ int q8_code(float v, float d) {
+  if (d == 0.0f) return 0;
+  float q = __builtin_rintf(v / d);
+  q = q > 127.0f ? 127.0f : q;
+  q = q < -127.0f ? -127.0f : q;
+  return (int)q;
+}
+
+// Read-only data that is uniform across a wavefront (the token's Q8 block,
+// dispatch lists) is read through the constant address space: the compiler
+// then issues scalar loads, which complete on lgkmcnt and leave the vector
+// memory counter to the weight stream.
+template <class T>
+using cptr = const T __attribute__((address_space(4)))*;
+template <class T>
+__device__ __forceinline__ cptr<T> as_const(const T* p) {
+  return (cptr<T>)(p);
+}
+
+// Signed int8 dot of four packed bytes, accumulated into c (v_dot4_i32_i8).
+__device__ __forceinline__ int sdot4(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of coli_moe_forward, carved from the caller's buffer.
+struct MoeWorkspace {
+  int32_t* counts;   // [A]
+  int32_t* lists;    // [A][T]
+  int32_t* n_active; // [1]
+  int32_t* active;   // [A]
+  int32_t* err;      // [1]
+  int32_t* xsum8;    // [T][D/32]   -8 * sum of each Q8 block of x
+  int8_t* hq;        // [P][F]
+  float* hd;         // [P][F/32]
+  int32_t* hsum8;    // [P][F/32]   -8 * sum of each Q8 block of h
+  float* o;          // [P][D]
+  size_t bytes;
+};
+
+// Layout for (E, S, D, F, T, k); base == nullptr only sizes it.
+MoeWorkspace moe_workspace_layout(void* base, int E, int S, int64_t D, int64_t F, int64_t T, int k);
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipError_t of the launch).
+hipError_t launch_quant_act_q8(const float* x, int64_t rows, int64_t k, int8_t* q, float* d,
+                               hipStream_t s);
+hipError_t launch_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, float* sc,
+                                  hipStream_t s);
+hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const uint8_t* gate_q,
+                                   const float* gate_s, const uint8_t* up_q, const float* up_s,
+                                   const uint8_t* down_q, const float* down_s, hipStream_t s);
+hipError_t launch_rmsnorm_q8(const float* h, int64_t T, int64_t D, float eps, int8_t* q, float* d,
+                             float* r_out, hipStream_t s);
+hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, int E, int k,
+                             float routed_scale, int32_t* idx, float* w, hipStream_t s);
+// Dispatch lists + compaction + index check; xq != nullptr also fills xsum8.
+hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, int32_t* counts,
+                           int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
+                           const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s);
+
+struct ForwardArgs {
+  const coli_expert_table* table;
+  const int8_t* xq;
+  const float* xd;
+  int64_t T;
+  const int32_t* idx;
+  const float* w;
+  int k;
+  float* y;
+  int accumulate;
+  MoeWorkspace ws;
+  const coli_moe_trace* trace;  // may be null
+};
+hipError_t launch_moe_forward(const ForwardArgs& a, hipStream_t s);
+
+}  // namespace coli

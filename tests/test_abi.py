@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every symbol include/coli.h declares, and
+rejects bad arguments on the host before any HIP call (CPU only: none of
+these calls reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_routed_expert_sigmoid_amd as coli
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coli.h")
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(coli_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("coli_quant_act_q8", "coli_route_topk", "coli_moe_forward"):
+        assert n in names
+    assert names == sorted(coli.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(coli.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = coli.lib()
+    for st in range(-6, 1):
+        assert L.coli_status_string(st)
+    assert L.coli_status_string(-99) == b"unknown status"
+
+
+def test_table_bytes():
+    L = coli.lib()
+    sizes = [ctypes.c_size_t() for _ in range(4)]
+    tot = L.coli_table_bytes(256, 1, 6144, 2048, *[ctypes.byref(s) for s in sizes])
+    # 257 experts x (3 * 6144 * 2048 / 2 nibble bytes + 4 * (2 * 2048 + 6144) scale bytes)
+    assert tot == 257 * 18915328
+    assert [s.value for s in sizes] == [257 * 6144 * 2048, 257 * 2 * 2048 * 4,
+                                       257 * 6144 * 1024, 257 * 6144 * 4]
+    assert L.coli_table_bytes(256, 1, 6144 + 32, 2048, None, None, None, None) == 0  # D % 64
+    assert L.coli_table_bytes(257, 1, 6144, 2048, None, None, None, None) == 0
+    assert L.coli_table_bytes(16, 2, 256, 128, None, None, None, None) == 0
+    assert L.coli_table_bytes(16, 0, 256, 128 + 16, None, None, None, None) == 0
+
+
+def _table(E=16, S=1, D=256, F=128, ptr=FAKE):
+    return coli.coli_expert_table(E, S, D, F, ptr, ptr, ptr, ptr)
+
+
+def test_validation_quant():
+    L = coli.lib()
+    assert L.coli_quant_act_q8(FAKE, 1, 33, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert L.coli_quant_act_q8(FAKE, -1, 32, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert L.coli_quant_act_q8(None, 1, 32, FAKE, FAKE, None) == coli.COLI_E_INVAL
+    assert L.coli_quant_act_q8(None, 0, 32, None, None, None) == coli.COLI_OK      # no work
+    assert L.coli_quant_weight_q4(FAKE, 4, 48, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert L.coli_quant_weight_q4(FAKE, 4, 64, None, FAKE, None) == coli.COLI_E_INVAL
+    assert L.coli_rmsnorm_q8(FAKE, 1, 40, 1e-6, FAKE, FAKE, None, None) == coli.COLI_E_SHAPE
+    assert L.coli_rmsnorm_q8(FAKE, 1, 64, -1.0, FAKE, FAKE, None, None) == coli.COLI_E_INVAL
+    assert L.coli_rmsnorm_q8(FAKE, 1, 64, float("nan"), FAKE, FAKE, None, None) == coli.COLI_E_INVAL
+
+
+def test_validation_route_and_dispatch():
+    L = coli.lib()
+    r = L.coli_route_topk
+    assert r(FAKE, None, 1, 0, 1, 1.0, FAKE, FAKE, None) == coli.COLI_E_SHAPE       # E = 0
+    assert r(FAKE, None, 1, 257, 8, 1.0, FAKE, FAKE, None) == coli.COLI_E_SHAPE     # E > 256
+    assert r(FAKE, None, 1, 16, 17, 1.0, FAKE, FAKE, None) == coli.COLI_E_SHAPE     # k > E
+    assert r(FAKE, None, 1, 200, 65, 1.0, FAKE, FAKE, None) == coli.COLI_E_SHAPE    # k > 64
+    assert r(FAKE, None, 1, 16, 0, 1.0, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert r(None, None, 1, 16, 2, 1.0, FAKE, FAKE, None) == coli.COLI_E_INVAL
+    assert r(FAKE, None, 1, 16, 2, float("inf"), FAKE, FAKE, None) == coli.COLI_E_INVAL
+    assert r(None, None, 0, 16, 2, 1.0, None, None, None) == coli.COLI_OK          # T = 0
+    d = L.coli_dispatch
+    assert d(FAKE, 4, 2, 16, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE   # S = 2
+    assert d(FAKE, 4, 17, 16, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert d(FAKE, 4, 2, 16, 1, FAKE, FAKE, None, FAKE, FAKE, None) == coli.COLI_E_INVAL
+    assert d(FAKE, 2**31, 8, 256, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+
+
+def test_validation_forward():
+    L = coli.lib()
+    t = _table()
+    ws = L.coli_moe_workspace_bytes(ctypes.byref(t), 4, 2)
+    assert ws > 0
+    f = L.coli_moe_forward
+    args = lambda tab, T=4, k=2, acc=0, wsb=ws, y=FAKE: (ctypes.byref(tab), FAKE, FAKE, T, FAKE,
+                                                          FAKE, k, y, acc, FAKE, wsb, None)
+    assert f(*args(t, wsb=ws - 1)) == coli.COLI_E_WORKSPACE
+    assert f(*args(t, k=0)) == coli.COLI_E_SHAPE
+    assert f(*args(t, k=17)) == coli.COLI_E_SHAPE
+    assert f(*args(t, acc=2)) == coli.COLI_E_INVAL
+    assert f(*args(t, y=None)) == coli.COLI_E_INVAL
+    assert f(*args(_table(D=96))) == coli.COLI_E_SHAPE
+    assert f(*args(_table(F=48))) == coli.COLI_E_SHAPE
+    assert f(*args(_table(E=300))) == coli.COLI_E_SHAPE
+    assert f(*args(_table(ptr=None))) == coli.COLI_E_INVAL
+    assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK          # empty batch: nothing to do
+    assert L.coli_moe_forward_traced(*args(t), None) == coli.COLI_E_INVAL
+    assert L.coli_moe_status(None, 64, None) == coli.COLI_E_INVAL
+    assert L.coli_table_set_expert(ctypes.byref(t), 17, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == coli.COLI_E_INVAL
+    assert L.coli_table_set_expert(ctypes.byref(t), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == coli.COLI_E_INVAL
+
+
+def test_workspace_grows_with_tokens():
+    L = coli.lib()
+    t = _table(256, 1, 6144, 2048)
+    a, b = (L.coli_moe_workspace_bytes(ctypes.byref(t), T, 8) for T in (1, 2048))
+    assert 0 < a < b
+    # per-pair outputs dominate: T (k+S) D fp32
+    assert b >= 2048 * 9 * 6144 * 4

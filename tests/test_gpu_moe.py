@@ -1,0 +1,226 @@
+"""MoE layer parity of the HIP path against the oracle (GPU).
+
+Each side draws the same seeded fp32 inputs and quantises them with its own
+code; the comparison is bit-exact for every integer, quantised value and
+fp32 intermediate of the decode path, and the layer output is also checked
+against the |gpu - oracle| <= 1e-5 * sum|terms| + 1e-6 bound.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (OracleExperts, assert_bitexact, assert_within_tol, build_table)
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import int4_routed_expert_sigmoid_amd as coli  # noqa: E402
+
+dev = "cuda"
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+class GpuLayer:
+    """quant -> route -> forward through the C ABI for one batch of tokens."""
+
+    def __init__(self, table, w, T):
+        self.table, self.w, self.T = table, w, T
+        self.ws = torch.empty(coli.coli_moe_workspace_bytes(table, T, w.k), dtype=torch.uint8,
+                              device=dev)
+
+    def run(self, x, logits, bias, trace=False, y0=None, accumulate=False):
+        w, T = self.w, self.T
+        xq = torch.empty((T, w.D), dtype=torch.int8, device=dev)
+        xd = torch.empty((T, w.D // 32), dtype=torch.float32, device=dev)
+        coli.coli_quant_act_q8(to_dev(x), xq, xd)
+        idx = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+        wt = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+        coli.coli_route_topk(to_dev(logits), to_dev(bias), w.k, idx, wt)
+        y = to_dev(y0) if y0 is not None else torch.empty((T, w.D), dtype=torch.float32,
+                                                          device=dev)
+        out = {}
+        if trace:
+            P = T * (w.k + w.S)
+            A = w.E + w.S
+            tr = {
+                "counts": torch.empty(A, dtype=torch.int32, device=dev),
+                "lists": torch.empty((A, T), dtype=torch.int32, device=dev),
+                "n_active": torch.empty(1, dtype=torch.int32, device=dev),
+                "active": torch.empty(A, dtype=torch.int32, device=dev),
+                "p_gate": torch.empty((P, w.F, w.D // 32), dtype=torch.int32, device=dev),
+                "p_up": torch.empty((P, w.F, w.D // 32), dtype=torch.int32, device=dev),
+                "p_down": torch.empty((P, w.D, w.F // 32), dtype=torch.int32, device=dev),
+                "g": torch.empty((P, w.F), dtype=torch.float32, device=dev),
+                "u": torch.empty((P, w.F), dtype=torch.float32, device=dev),
+                "h": torch.empty((P, w.F), dtype=torch.float32, device=dev),
+                "hq": torch.empty((P, w.F), dtype=torch.int8, device=dev),
+                "hd": torch.empty((P, w.F // 32), dtype=torch.float32, device=dev),
+                "o": torch.empty((P, w.D), dtype=torch.float32, device=dev),
+            }
+            coli.coli_moe_forward_traced(self.table, xq, xd, idx, wt, y, self.ws, tr,
+                                         accumulate=accumulate)
+            out = {k: v.cpu().numpy() for k, v in tr.items()}
+        else:
+            coli.coli_moe_forward(self.table, xq, xd, idx, wt, y, self.ws, accumulate=accumulate)
+        assert coli.coli_moe_status(self.ws) == coli.COLI_OK
+        out.update(xq=xq.cpu().numpy(), xd=xd.cpu().numpy(), idx=idx.cpu().numpy(),
+                   w=wt.cpu().numpy(), y=y.cpu().numpy())
+        return out
+
+
+def oracle_layer(ox: OracleExperts, w, x, logits, bias, y0=None, accumulate=False):
+    xq, xd = oracle.q8_quant(x)
+    idx, wt = oracle.route(logits, bias, w.k)
+    y, A = oracle.moe_layer(ox.table_for(idx), w.E, w.S, xq, xd, idx, wt, out=y0,
+                            accumulate=accumulate)
+    return dict(xq=xq, xd=xd, idx=idx, w=wt, y=y, absterm=A)
+
+
+def check_front(g, r):
+    assert_bitexact("xq", g["xq"], r["xq"])
+    assert_bitexact("xd", g["xd"], r["xd"])
+    assert_bitexact("idx", g["idx"], r["idx"])
+    assert_bitexact("w", g["w"], r["w"])
+
+
+def check_trace(g, ox, w, r, tokens=None):
+    """Every pair's partials and intermediates against the oracle's expert."""
+    T = r["idx"].shape[0]
+    counts, lists, na, act = oracle.dispatch(r["idx"], w.E, w.S)
+    assert_bitexact("counts", g["counts"], counts)
+    assert int(g["n_active"][0]) == na
+    assert_bitexact("active", g["active"][:na], act)
+    for e in act:
+        assert_bitexact(f"list {e}", g["lists"][e, :counts[e]], lists[e, :counts[e]])
+    for t in (range(T) if tokens is None else tokens):
+        for slot in range(w.k + w.S):
+            e = w.E if slot == w.k else int(r["idx"][t, slot])
+            p = t * (w.k + w.S) + slot
+            ref = oracle.expert_forward(ox[e], r["xq"][t], r["xd"][t], want_partials=True)
+            tag = f"t{t} slot{slot} e{e}"
+            assert_bitexact(f"P_gate {tag}", g["p_gate"][p], ref["P_gate"])
+            assert_bitexact(f"P_up {tag}", g["p_up"][p], ref["P_up"])
+            assert_bitexact(f"g {tag}", g["g"][p], ref["g"])
+            assert_bitexact(f"u {tag}", g["u"][p], ref["u"])
+            assert_bitexact(f"h {tag}", g["h"][p], ref["h"])
+            assert_bitexact(f"hq {tag}", g["hq"][p], ref["hq"])
+            assert_bitexact(f"hd {tag}", g["hd"][p], ref["hd"])
+            assert_bitexact(f"P_down {tag}", g["p_down"][p], ref["P_down"])
+            assert_bitexact(f"o {tag}", g["o"][p], ref["o"])
+
+
+# ---------------------------------------------------------------- tiny layer
+@pytest.fixture(scope="module")
+def tiny():
+    w = synth.WORKLOADS[0]
+    return w, build_table(w), OracleExperts(w)
+
+
+def test_tiny_layer_traced(tiny):
+    w, table, ox = tiny
+    x, lg, b = synth.activations(w, w.T), synth.logits(w, w.T), synth.router_bias(w)
+    g = GpuLayer(table, w, w.T).run(x, lg, b, trace=True)
+    r = oracle_layer(ox, w, x, lg, b)
+    check_front(g, r)
+    check_trace(g, ox, w, r)
+    assert_bitexact("y", g["y"], r["y"])
+    assert_within_tol("y", g["y"], r["y"], r["absterm"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 17, 64])
+def test_tiny_layer_token_counts(tiny, T):
+    """Ragged batches: every pass size of the GEMV path and partial chunks."""
+    w, table, ox = tiny
+    x, lg, b = synth.activations(w, T, 100), synth.logits(w, T, 100), synth.router_bias(w)
+    g = GpuLayer(table, w, T).run(x, lg, b)
+    r = oracle_layer(ox, w, x, lg, b)
+    check_front(g, r)
+    assert_bitexact("y", g["y"], r["y"])
+
+
+def test_tiny_layer_accumulate_and_determinism(tiny):
+    w, table, ox = tiny
+    x, lg, b = synth.activations(w, w.T, 7), synth.logits(w, w.T, 7), synth.router_bias(w)
+    y0 = synth.normal(12345, w.T * w.D, 1.0).reshape(w.T, w.D)
+    L = GpuLayer(table, w, w.T)
+    g1 = L.run(x, lg, b, y0=y0, accumulate=True)
+    g2 = L.run(x, lg, b, y0=y0, accumulate=True)
+    r = oracle_layer(ox, w, x, lg, b, y0=y0, accumulate=True)
+    assert_bitexact("y (run 1)", g1["y"], r["y"])
+    assert_bitexact("y (run 2)", g2["y"], g1["y"])
+
+
+def test_invalid_index_is_reported_not_faulting(tiny):
+    w, table, _ = tiny
+    T = 2
+    xq = torch.zeros((T, w.D), dtype=torch.int8, device=dev)
+    xd = torch.ones((T, w.D // 32), dtype=torch.float32, device=dev)
+    idx = to_dev(np.int32([[0, 16], [3, -2]]))
+    wt = torch.full((T, w.k), 0.5, dtype=torch.float32, device=dev)
+    y = torch.empty((T, w.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(coli.coli_moe_workspace_bytes(table, T, w.k), dtype=torch.uint8, device=dev)
+    coli.coli_moe_forward(table, xq, xd, idx, wt, y, ws)
+    assert coli.coli_moe_status(ws) == coli.COLI_E_INDEX
+    assert torch.isfinite(y).all()
+    # a valid call on the same workspace clears the flag
+    coli.coli_moe_forward(table, xq, xd, to_dev(np.int32([[0, 1], [2, 3]])), wt, y, ws)
+    assert coli.coli_moe_status(ws) == coli.COLI_OK
+
+
+# ---------------------------------------------------------------- page-scale layer
+@pytest.fixture(scope="module")
+def big():
+    w = synth.WORKLOADS[1]
+    return build_table(w), OracleExperts(w)
+
+
+def test_decode_layer_traced(big):
+    """1 token, d_model 6144, d_ff 2048, 256+1 experts, top-8 (4.86 GB table in HBM)."""
+    table, ox = big
+    w = synth.WORKLOADS[1]
+    L = GpuLayer(table, w, 1)
+    for tok in (0, 1):
+        x, lg, b = synth.activations(w, 1, tok), synth.logits(w, 1, tok), synth.router_bias(w)
+        g = L.run(x, lg, b, trace=True)
+        r = oracle_layer(ox, w, x, lg, b)
+        check_front(g, r)
+        check_trace(g, ox, w, r)
+        assert_bitexact("y", g["y"], r["y"])
+        assert_within_tol("y", g["y"], r["y"], r["absterm"])
+
+
+def test_verify_layer_traced(big):
+    """4 tokens through one pass: the batch union of their experts."""
+    table, ox = big
+    w = synth.WORKLOADS[2]
+    x, lg, b = synth.activations(w, 4), synth.logits(w, 4), synth.router_bias(w)
+    g = GpuLayer(table, w, 4).run(x, lg, b, trace=True)
+    r = oracle_layer(ox, w, x, lg, b)
+    check_front(g, r)
+    check_trace(g, ox, w, r)
+    assert_bitexact("y", g["y"], r["y"])
+    assert_within_tol("y", g["y"], r["y"], r["absterm"])
+
+
+def test_prefill_layer_sampled(big):
+    """2048 tokens in one pass; the oracle recomputes a sample of tokens."""
+    table, ox = big
+    w = synth.WORKLOADS[3]
+    T = 2048
+    x, lg, b = synth.activations(w, T), synth.logits(w, T), synth.router_bias(w)
+    g = GpuLayer(table, w, T).run(x, lg, b)
+    xq, xd = oracle.q8_quant(x)
+    idx, wt = oracle.route(lg, b, w.k)
+    assert_bitexact("xq", g["xq"], xq)
+    assert_bitexact("idx", g["idx"], idx)
+    assert_bitexact("w", g["w"], wt)
+    sample = [0, 1, 777, 2047]
+    ys, A = oracle.moe_layer(ox.table_for(idx[sample]), w.E, w.S, xq[sample], xd[sample],
+                             idx[sample], wt[sample])
+    assert_bitexact("y sample", g["y"][sample], ys)
+    assert_within_tol("y sample", g["y"][sample], ys, A)
