@@ -203,6 +203,23 @@ int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, co
                             int accumulate, void* workspace, size_t ws_bytes,
                             const coli_moe_trace* trace, void* stream);
 
+/* Stage timing: hipEvent_t handles (created by the caller, passed as void*)
+ * that the forward records on `stream` between its internal kernels.  Any
+ * may be NULL.  Used by the benchmark to time the dominant kernel.  Not for
+ * use under stream capture (a captured record expresses a dependency only). */
+typedef struct {
+  void* begin;   /* before the dispatch kernels                        */
+  void* gate_up; /* after dispatch, before the gate/up GEMV            */
+  void* down;    /* after the gate/up GEMV, before the down GEMV       */
+  void* combine; /* after the down GEMV, before the weighted combine   */
+  void* end;     /* after the weighted combine                         */
+} coli_moe_events;
+
+int coli_moe_forward_profiled(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                              int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                              int accumulate, void* workspace, size_t ws_bytes,
+                              const coli_moe_events* events, void* stream);
+
 /* Synchronises `stream`, then reports the device-side index check of the
  * last forward that used `workspace`: COLI_OK or COLI_E_INDEX. */
 int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream);

@@ -29,7 +29,8 @@ COLI_MAX_TOPK = 64
 EXPORTED = [
     "coli_table_bytes", "coli_table_set_expert", "coli_quant_act_q8", "coli_quant_weight_q4",
     "coli_rmsnorm_q8", "coli_route_topk", "coli_dispatch", "coli_moe_workspace_bytes",
-    "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_status", "coli_status_string",
+    "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
+    "coli_moe_status", "coli_status_string",
     "coli_last_hip_error",
 ]
 
@@ -50,6 +51,10 @@ class coli_expert_table(ctypes.Structure):
                 ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("gu_q", ctypes.c_void_p), ("gu_s", ctypes.c_void_p),
                 ("dn_q", ctypes.c_void_p), ("dn_s", ctypes.c_void_p)]
+
+
+class coli_moe_events(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("begin", "gate_up", "down", "combine", "end")]
 
 
 class coli_moe_trace(ctypes.Structure):
@@ -86,6 +91,8 @@ def lib():
                                  ctypes.c_int),
             "coli_moe_forward_traced": ([_P, _P, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P,
                                          sz, _P, _P], ctypes.c_int),
+            "coli_moe_forward_profiled": ([_P, _P, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P,
+                                           sz, _P, _P], ctypes.c_int),
             "coli_moe_status": ([_P, sz, _P], ctypes.c_int),
             "coli_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "coli_last_hip_error": ([], ctypes.c_int),
@@ -224,6 +231,18 @@ def coli_moe_forward_traced(table: ExpertTable, xq, xd, idx, w, y, workspace, tr
                                          k, _ptr(y), int(bool(accumulate)), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(),
                                          ctypes.byref(tr), _stream(stream)))
+
+
+def coli_moe_forward_profiled(table: ExpertTable, xq, xd, idx, w, y, workspace, events: dict,
+                              accumulate=False, stream=None):
+    """events: name -> hipEvent_t handle (int) for fields of coli_moe_events."""
+    ev = coli_moe_events(*[events.get(n) for n, _ in coli_moe_events._fields_])
+    T, k = idx.shape
+    _check("coli_moe_forward_profiled",
+           lib().coli_moe_forward_profiled(table.ref(), _ptr(xq), _ptr(xd), T, _ptr(idx), _ptr(w),
+                                           k, _ptr(y), int(bool(accumulate)), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           ctypes.byref(ev), _stream(stream)))
 
 
 def coli_moe_status(workspace, stream=None) -> int:

@@ -220,7 +220,8 @@ size_t coli_moe_workspace_bytes(const coli_expert_table* table, int64_t T, int32
 static int forward_impl(const coli_expert_table* table, const int8_t* xq, const float* xd,
                         int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
                         int accumulate, void* workspace, size_t ws_bytes,
-                        const coli_moe_trace* trace, void* stream) {
+                        const coli_moe_trace* trace, const coli_moe_events* events,
+                        void* stream) {
   int rc = table_check(table);
   if (rc) return rc;
   if (k < 1 || k > table->n_routed || k > COLI_MAX_TOPK) return COLI_E_SHAPE;
@@ -246,6 +247,7 @@ static int forward_impl(const coli_expert_table* table, const int8_t* xq, const 
   a.accumulate = accumulate;
   a.ws = ws;
   a.trace = trace;
+  a.events = events;
   hipError_t e = coli::launch_moe_forward(a, as_stream(stream));
   return e == hipSuccess ? COLI_OK : hip_fail(e);
 }
@@ -254,7 +256,16 @@ int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const flo
                      const int32_t* idx, const float* w, int32_t k, float* y, int accumulate,
                      void* workspace, size_t ws_bytes, void* stream) {
   return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, nullptr,
-                      stream);
+                      nullptr, stream);
+}
+
+int coli_moe_forward_profiled(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                              int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                              int accumulate, void* workspace, size_t ws_bytes,
+                              const coli_moe_events* events, void* stream) {
+  if (!events) return COLI_E_INVAL;
+  return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, nullptr,
+                      events, stream);
 }
 
 int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, const float* xd,
@@ -263,7 +274,7 @@ int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, co
                             const coli_moe_trace* trace, void* stream) {
   if (!trace) return COLI_E_INVAL;
   return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, trace,
-                      stream);
+                      nullptr, stream);
 }
 
 int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream) {

@@ -330,26 +330,34 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   *yt = accumulate ? *yt + acc : acc;
 }
 
+// Stage events (profiled forward only; not for stream capture, where a record
+// only expresses a dependency).
+hipError_t record(void* ev, hipStream_t s) {
+  return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
+}
+
 constexpr int kPfGateUp = 16;
 constexpr int kPfDown = 16;
 
 template <int MAXT, bool TRACE>
-hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, hipStream_t s) {
+hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
   hipLaunchKernelGGL((gate_up_kernel<MAXT, kPfGateUp, TRACE>), dim3((unsigned)(g.F / 32), maxA),
                      dim3(kWave), 0, s, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
+  if ((rc = record(ev_down, s)) != hipSuccess) return rc;
   hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, TRACE>), dim3((unsigned)(d.D / 64), maxA),
                      dim3(kWave), 0, s, d);
   return hipGetLastError();
 }
 
 template <bool TRACE>
-hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, hipStream_t s) {
-  if (T <= 1) return launch_pair<1, TRACE>(g, d, maxA, s);
-  if (T <= 2) return launch_pair<2, TRACE>(g, d, maxA, s);
-  if (T <= 4) return launch_pair<4, TRACE>(g, d, maxA, s);
-  return launch_pair<8, TRACE>(g, d, maxA, s);
+hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, void* ev_down,
+                       hipStream_t s) {
+  if (T <= 1) return launch_pair<1, TRACE>(g, d, maxA, ev_down, s);
+  if (T <= 2) return launch_pair<2, TRACE>(g, d, maxA, ev_down, s);
+  if (T <= 4) return launch_pair<4, TRACE>(g, d, maxA, ev_down, s);
+  return launch_pair<8, TRACE>(g, d, maxA, ev_down, s);
 }
 
 }  // namespace
@@ -360,7 +368,11 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   const int64_t D = t.d_model, F = t.d_ff, T = f.T;
   if (T == 0) return hipSuccess;
   const MoeWorkspace& ws = f.ws;
-  hipError_t rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active,
+  const coli_moe_events no_events = {};
+  const coli_moe_events& ev = f.events ? *f.events : no_events;
+  hipError_t rc = record(ev.begin, s);
+  if (rc != hipSuccess) return rc;
+  rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active,
                                   ws.active, ws.err, f.xq, D, ws.xsum8, s);
   if (rc != hipSuccess) return rc;
   const int64_t maxA = (T * f.k < E ? T * f.k : E) + S;
@@ -399,6 +411,7 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   d.F = F;
   d.k = f.k;
   d.S = S;
+  if ((rc = record(ev.gate_up, s)) != hipSuccess) return rc;
   const coli_moe_trace* tr = f.trace;
   if (tr) {
     g.tr_pg = tr->p_gate;
@@ -407,14 +420,16 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
     g.tr_u = tr->u;
     g.tr_h = tr->h;
     d.tr_pd = tr->p_down;
-    rc = launch_gemv<true>(g, d, (int)maxA, T, s);
+    rc = launch_gemv<true>(g, d, (int)maxA, T, ev.down, s);
   } else {
-    rc = launch_gemv<false>(g, d, (int)maxA, T, s);
+    rc = launch_gemv<false>(g, d, (int)maxA, T, ev.down, s);
   }
   if (rc != hipSuccess) return rc;
+  if ((rc = record(ev.combine, s)) != hipSuccess) return rc;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((D + 255) / 256), (unsigned)T), dim3(256), 0,
                      s, ws.o, f.idx, f.w, D, f.k, E, S, f.y, f.accumulate);
   rc = hipGetLastError();
+  if (rc == hipSuccess) rc = record(ev.end, s);
   if (rc != hipSuccess || !tr) return rc;
   // test dumps of the dispatch and of the workspace intermediates
   const int64_t A = E + S, P = T * (f.k + S);

@@ -112,7 +112,8 @@ struct ForwardArgs {
   float* y;
   int accumulate;
   MoeWorkspace ws;
-  const coli_moe_trace* trace;  // may be null
+  const coli_moe_trace* trace;   // may be null
+  const coli_moe_events* events; // may be null
 };
 hipError_t launch_moe_forward(const ForwardArgs& a, hipStream_t s);
 

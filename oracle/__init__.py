@@ -22,6 +22,7 @@ _I32 = ctypes.c_int32
 _F = ctypes.c_float
 
 _SIG = {
+    "orc_num_threads": ([], ctypes.c_int),
     "orc_expf": ([_F], _F),
     "orc_sigmoidf": ([_F], _F),
     "orc_siluf": ([_F], _F),
@@ -99,6 +100,9 @@ class Oracle:
             fn = getattr(self.L, name)
             fn.argtypes = args
             fn.restype = res
+
+    def num_threads(self) -> int:
+        return int(self.L.orc_num_threads())
 
     # ---------------------------------------------------------------- scalar math
     def expf(self, x: float) -> float:

@@ -38,8 +38,12 @@
 #include "coli_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops of this library use (reported with timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------
  * exp(x) in fp32 (Cody & Waite, "Software Manual for the Elementary

@@ -20,6 +20,9 @@
 extern "C" {
 #endif
 
+/* OpenMP threads used by the parallel loops. */
+int orc_num_threads(void);
+
 /* exp / sigmoid / silu in fp32 (Cody-Waite reduction + degree-7 Taylor). */
 float orc_expf(float x);
 float orc_sigmoidf(float x);
