@@ -6,10 +6,11 @@ d_ff 2048, 256 routed experts + 1 shared, top-8 sigmoid routing, the whole
 4.86 GB int4 table resident in HBM.  One step = the whole hot path for one
 token: Q8_0 quantisation of x, sigmoid top-k routing, batch-union dispatch,
 gate/up int4 x int8 GEMV with fused SwiGLU + Q8(h), down GEMV, weighted
-combine.  Steps cycle through a pool of 64 distinct seeded tokens (their
-expert union covers the table), so the weights stream from HBM rather than
+combine, through one coli_moe_layer call (4 kernels: fused front, gate/up,
+down, combine).  Steps cycle through a pool of 64 distinct seeded tokens
+(their expert union is 2.2 GB), so the weights stream from HBM rather than
 from the 256 MB Infinity Cache.  Steps are captured in HIP graphs (launch
-overhead of the 7 kernels per step is then the device's, not Python's).
+overhead is then the device's, not Python's).
 
 Prints one JSON line with the decode rate (tokens/s per MoE layer), the
 roofline of the dominant kernel (gate/up GEMV) against 8 TB/s, and the
@@ -141,20 +142,13 @@ def main():
     lg_pool = torch.from_numpy(synth.logits(w, P)).cuda()
     bias = torch.from_numpy(synth.router_bias(w)).cuda()
     y_pool = torch.zeros((P, w.D), dtype=torch.float32, device="cuda")
-    xq = torch.empty((1, w.D), dtype=torch.int8, device="cuda")
-    xd = torch.empty((1, w.D // 32), dtype=torch.float32, device="cuda")
-    idx = torch.empty((1, w.k), dtype=torch.int32, device="cuda")
-    wt = torch.empty((1, w.k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(coli.coli_moe_workspace_bytes(table, 1, w.k), dtype=torch.uint8,
+    ws = torch.empty(coli.coli_moe_layer_workspace_bytes(table, 1, w.k), dtype=torch.uint8,
                      device="cuda")
 
     def step(j, events=None):
-        coli.coli_quant_act_q8(x_pool[j:j + 1], xq, xd)
-        coli.coli_route_topk(lg_pool[j:j + 1], bias, w.k, idx, wt)
-        if events is None:
-            coli.coli_moe_forward(table, xq, xd, idx, wt, y_pool[j:j + 1], ws)
-        else:
-            coli.coli_moe_forward_profiled(table, xq, xd, idx, wt, y_pool[j:j + 1], ws, events)
+        """One token through the layer: f32 x and router logits in, f32 y out."""
+        coli.coli_moe_layer(table, x_pool[j:j + 1], lg_pool[j:j + 1], bias, w.k,
+                            y_pool[j:j + 1], ws, events=events)
 
     for j in range(P):                               # setup: one eager pass over the pool
         step(j)
@@ -212,7 +206,7 @@ def main():
     # replays so that every event and kernel is already queued when the GPU
     # reaches it (the events then bracket the kernel, not host launch gaps).
     hev = HipEvents()
-    ev_names = ("gate_up", "down", "combine", "end")
+    ev_names = ("begin", "gate_up", "down", "combine", "end")
     prof = [{k: hev.create() for k in ev_names} for _ in range(P)]
     if graphs:
         for _ in range(4):
@@ -222,7 +216,10 @@ def main():
     torch.cuda.synchronize()
     gu = [hev.elapsed_ms(e["gate_up"], e["down"]) for e in prof]
     dn = [hev.elapsed_ms(e["down"], e["combine"]) for e in prof]
+    fr = [hev.elapsed_ms(e["begin"], e["gate_up"]) for e in prof]
+    cb = [hev.elapsed_ms(e["combine"], e["end"]) for e in prof]
     gu_ms, dn_ms = sum(gu) / len(gu), sum(dn) / len(dn)
+    fr_ms, cb_ms = sum(fr) / len(fr), sum(cb) / len(cb)
     gu_bytes, dn_bytes = expert_bytes(w)
     active = w.k + w.S
     # algorithmic bytes of one gate/up launch: 9 experts' gate+up nibbles and row scales,
@@ -251,7 +248,8 @@ def main():
                    "table_bytes": table.bytes,
                    "launch": "eager" if args.eager else "hipgraph"},
         "weight_gbps_per_step": round(layer_bytes * tok_s / 1e9, 1),
-        "kernels_ms": {"gate_up": round(gu_ms, 5), "down": round(dn_ms, 5)},
+        "kernels_ms": {"front": round(fr_ms, 5), "gate_up": round(gu_ms, 5),
+                       "down": round(dn_ms, 5), "combine": round(cb_ms, 5)},
         "down_gbps": round(active * dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "gate_up_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

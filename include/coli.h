@@ -63,6 +63,7 @@ typedef enum {
 /* Limits of this build. */
 #define COLI_MAX_EXPERTS 256 /* routed experts per layer                    */
 #define COLI_MAX_TOPK 64     /* experts selected per token                  */
+#define COLI_MAX_DIM 32768   /* d_model and d_ff of an expert table         */
 
 /* ------------------------------------------------------------------------
  * Device-resident expert table of one MoE layer.
@@ -86,7 +87,7 @@ typedef enum {
  * the block: byte j (0..3) has column 8k+j in its low nibble and column
  * 8k+4+j in its high nibble; each nibble stores q + 8 (0..15).
  * The shared expert (when S = 1) is index E.  E <= 256, S in {0, 1},
- * D % 64 == 0, F % 32 == 0.
+ * D % 64 == 0, F % 32 == 0, D and F <= COLI_MAX_DIM.
  */
 typedef struct {
   int32_t n_routed; /* E */
@@ -196,6 +197,11 @@ typedef struct {
   int8_t* hq;        /* [T*(k+S)][F]                                   */
   float* hd;         /* [T*(k+S)][F/32]                                */
   float* o;          /* [T*(k+S)][D]             expert outputs       */
+  /* coli_moe_layer only: its own front-end results                        */
+  int8_t* xq;        /* [T][D]                   Q8_0 codes of x      */
+  float* xd;         /* [T][D/32]                Q8_0 scales of x     */
+  int32_t* idx;      /* [T][k]                   routing              */
+  float* w;          /* [T][k]                                         */
 } coli_moe_trace;
 
 int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, const float* xd,
@@ -208,7 +214,8 @@ int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, co
  * may be NULL.  Used by the benchmark to time the dominant kernel.  Not for
  * use under stream capture (a captured record expresses a dependency only). */
 typedef struct {
-  void* begin;   /* before the dispatch kernels                        */
+  void* begin;   /* before the dispatch kernels (coli_moe_layer*: before
+                    the front end: quantisation, routing, dispatch)     */
   void* gate_up; /* after dispatch, before the gate/up GEMV            */
   void* down;    /* after the gate/up GEMV, before the down GEMV       */
   void* combine; /* after the down GEMV, before the weighted combine   */
@@ -220,8 +227,30 @@ int coli_moe_forward_profiled(const coli_expert_table* table, const int8_t* xq, 
                               int accumulate, void* workspace, size_t ws_bytes,
                               const coli_moe_events* events, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The whole layer in one call, from f32 activations and router logits:
+ * Q8_0 of x (coli_quant_act_q8), routing (coli_route_topk, bias may be NULL),
+ * then coli_moe_forward, with the same numerics as those calls.  For small
+ * batches (T <= 64 and T*k <= 1024: decode and speculative verify) the
+ * quantisation, routing and dispatch run fused in one single-workgroup
+ * kernel, so a decode step is 4 kernels.  The workspace must hold
+ * coli_moe_layer_workspace_bytes(table, T, k) bytes (no initialisation;
+ * clobbered; calls sharing it must not overlap).  _ex additionally takes the
+ * optional trace and stage events of the forward (both may be NULL; events
+ * are not for use under stream capture). */
+size_t coli_moe_layer_workspace_bytes(const coli_expert_table* table, int64_t T, int32_t k);
+
+int coli_moe_layer(const coli_expert_table* table, const float* x, const float* logits,
+                   const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                   int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const float* logits,
+                      const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                      int accumulate, void* workspace, size_t ws_bytes,
+                      const coli_moe_trace* trace, const coli_moe_events* events, void* stream);
+
 /* Synchronises `stream`, then reports the device-side index check of the
- * last forward that used `workspace`: COLI_OK or COLI_E_INDEX. */
+ * last forward or layer call that used `workspace`: COLI_OK or COLI_E_INDEX. */
 int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

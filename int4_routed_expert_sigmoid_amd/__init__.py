@@ -30,8 +30,8 @@ EXPORTED = [
     "coli_table_bytes", "coli_table_set_expert", "coli_quant_act_q8", "coli_quant_weight_q4",
     "coli_rmsnorm_q8", "coli_route_topk", "coli_dispatch", "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
-    "coli_moe_status", "coli_status_string",
-    "coli_last_hip_error",
+    "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex",
+    "coli_moe_status", "coli_status_string", "coli_last_hip_error",
 ]
 
 
@@ -60,7 +60,7 @@ class coli_moe_events(ctypes.Structure):
 class coli_moe_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("counts", "lists", "n_active", "active", "p_gate", "p_up", "p_down", "g", "u",
-                 "h", "hq", "hd", "o")]
+                 "h", "hq", "hd", "o", "xq", "xd", "idx", "w")]
 
 
 _lib = None
@@ -93,6 +93,11 @@ def lib():
                                          sz, _P, _P], ctypes.c_int),
             "coli_moe_forward_profiled": ([_P, _P, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P,
                                            sz, _P, _P], ctypes.c_int),
+            "coli_moe_layer_workspace_bytes": ([_P, _I64, _I32], sz),
+            "coli_moe_layer": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P, ctypes.c_int, _P,
+                                sz, _P], ctypes.c_int),
+            "coli_moe_layer_ex": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P, ctypes.c_int,
+                                   _P, sz, _P, _P, _P], ctypes.c_int),
             "coli_moe_status": ([_P, sz, _P], ctypes.c_int),
             "coli_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "coli_last_hip_error": ([], ctypes.c_int),
@@ -243,6 +248,36 @@ def coli_moe_forward_profiled(table: ExpertTable, xq, xd, idx, w, y, workspace, 
                                            k, _ptr(y), int(bool(accumulate)), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(),
                                            ctypes.byref(ev), _stream(stream)))
+
+
+def coli_moe_layer_workspace_bytes(table: ExpertTable, T: int, k: int) -> int:
+    return int(lib().coli_moe_layer_workspace_bytes(table.ref(), T, k))
+
+
+def coli_moe_layer(table: ExpertTable, x, logits, bias, k, y, workspace, routed_scale=1.0,
+                   accumulate=False, trace: dict | None = None, events: dict | None = None,
+                   stream=None):
+    """x [T][D] f32, logits [T][E] f32, bias [E] f32 or None -> y [T][D] f32."""
+    import torch
+    _dtype(x, torch.float32, "x"); _dtype(logits, torch.float32, "logits")
+    _dtype(bias, torch.float32, "bias"); _dtype(y, torch.float32, "y")
+    T = x.shape[0]
+    ws = workspace.numel() * workspace.element_size()
+    if trace is None and events is None:
+        _check("coli_moe_layer",
+               lib().coli_moe_layer(table.ref(), _ptr(x), _ptr(logits), _ptr(bias), T, k,
+                                    routed_scale, _ptr(y), int(bool(accumulate)),
+                                    _ptr(workspace), ws, _stream(stream)))
+        return
+    tr = None if trace is None else coli_moe_trace(
+        *[_ptr(trace.get(n)) for n, _ in coli_moe_trace._fields_])
+    ev = None if events is None else coli_moe_events(
+        *[events.get(n) for n, _ in coli_moe_events._fields_])
+    _check("coli_moe_layer_ex",
+           lib().coli_moe_layer_ex(table.ref(), _ptr(x), _ptr(logits), _ptr(bias), T, k,
+                                   routed_scale, _ptr(y), int(bool(accumulate)), _ptr(workspace),
+                                   ws, None if tr is None else ctypes.byref(tr),
+                                   None if ev is None else ctypes.byref(ev), _stream(stream)))
 
 
 def coli_moe_status(workspace, stream=None) -> int:

@@ -54,6 +54,7 @@ int table_check(const coli_expert_table* t) {
   if (t->n_shared < 0 || t->n_shared > 1) return COLI_E_SHAPE;
   if (t->d_model <= 0 || t->d_model % 64 != 0 || t->d_ff <= 0 || t->d_ff % 32 != 0)
     return COLI_E_SHAPE;
+  if (t->d_model > COLI_MAX_DIM || t->d_ff > COLI_MAX_DIM) return COLI_E_SHAPE;
   if (!t->gu_q || !t->gu_s || !t->dn_q || !t->dn_s) return COLI_E_INVAL;
   if (!al16(t->gu_q) || !al16(t->dn_q) || !al4(t->gu_s) || !al4(t->dn_s)) return COLI_E_INVAL;
   return COLI_OK;
@@ -112,7 +113,8 @@ int coli_last_hip_error(void) { return g_last_hip_error; }
 
 size_t coli_table_bytes(int32_t E, int32_t S, int64_t D, int64_t F, size_t* gu_q, size_t* gu_s,
                         size_t* dn_q, size_t* dn_s) {
-  if (E < 1 || E > COLI_MAX_EXPERTS || S < 0 || S > 1 || D <= 0 || D % 64 || F <= 0 || F % 32)
+  if (E < 1 || E > COLI_MAX_EXPERTS || S < 0 || S > 1 || D <= 0 || D % 64 || F <= 0 || F % 32 ||
+      D > COLI_MAX_DIM || F > COLI_MAX_DIM)
     return 0;
   const size_t n = (size_t)(E + S);
   const size_t a = n * (size_t)(D * F), b = n * (size_t)(2 * F) * sizeof(float),
@@ -248,6 +250,7 @@ static int forward_impl(const coli_expert_table* table, const int8_t* xq, const 
   a.ws = ws;
   a.trace = trace;
   a.events = events;
+  a.dispatched = false;
   hipError_t e = coli::launch_moe_forward(a, as_stream(stream));
   return e == hipSuccess ? COLI_OK : hip_fail(e);
 }
@@ -275,6 +278,103 @@ int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, co
   if (!trace) return COLI_E_INVAL;
   return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, trace,
                       nullptr, stream);
+}
+
+// Layer workspace: the forward's, then the front-end results.
+struct LayerWorkspace {
+  coli::MoeWorkspace fwd;
+  int8_t* xq;
+  float* xd;
+  int32_t* idx;
+  float* w;
+  size_t bytes;
+};
+
+static LayerWorkspace layer_workspace_layout(void* base, const coli_expert_table* t, int64_t T,
+                                             int k) {
+  LayerWorkspace l;
+  l.fwd = coli::moe_workspace_layout(base, t->n_routed, t->n_shared, t->d_model, t->d_ff, T, k);
+  size_t off = l.fwd.bytes;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  l.xq = static_cast<int8_t*>(take((size_t)(T * t->d_model)));
+  l.xd = static_cast<float*>(take(sizeof(float) * (size_t)(T * (t->d_model / 32))));
+  l.idx = static_cast<int32_t*>(take(sizeof(int32_t) * (size_t)(T * k)));
+  l.w = static_cast<float*>(take(sizeof(float) * (size_t)(T * k)));
+  l.bytes = off;
+  return l;
+}
+
+size_t coli_moe_layer_workspace_bytes(const coli_expert_table* table, int64_t T, int32_t k) {
+  if (!table || T < 0 || k < 1) return 0;
+  return layer_workspace_layout(nullptr, table, T, k).bytes;
+}
+
+int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const float* logits,
+                      const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                      int accumulate, void* workspace, size_t ws_bytes,
+                      const coli_moe_trace* trace, const coli_moe_events* events, void* stream) {
+  int rc = table_check(table);
+  if (rc) return rc;
+  const int E = table->n_routed, S = table->n_shared;
+  if (k < 1 || k > E || k > COLI_MAX_TOPK) return COLI_E_SHAPE;
+  if (T < 0 || T * (int64_t)(k + S) > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (accumulate != 0 && accumulate != 1) return COLI_E_INVAL;
+  if (!std::isfinite(routed_scale)) return COLI_E_INVAL;
+  if (T == 0) return COLI_OK;
+  if (!x || !logits || !y || !workspace) return COLI_E_INVAL;
+  if (!al16(x) || !al4(logits) || !al4(bias) || !al4(y) || !al16(workspace)) return COLI_E_INVAL;
+  const LayerWorkspace l = layer_workspace_layout(workspace, table, T, k);
+  if (ws_bytes < l.bytes) return COLI_E_WORKSPACE;
+  if ((rc = check_device())) return rc;
+  const int64_t D = table->d_model;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = hipSuccess;
+  // `begin` marks the start of the front end; the forward records the rest
+  coli_moe_events fwd_events = {};
+  if (events) {
+    fwd_events = *events;
+    fwd_events.begin = nullptr;
+    if (events->begin) e = hipEventRecord(reinterpret_cast<hipEvent_t>(events->begin), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  const bool small = T <= coli::kPrologueMaxTokens && T * k <= coli::kPrologueMaxEntries;
+  if (small) {
+    e = coli::launch_prologue_small(x, logits, bias, T, E, S, k, routed_scale, D, l.xq, l.xd,
+                                    l.fwd.xsum8, l.idx, l.w, l.fwd.counts, l.fwd.lists,
+                                    l.fwd.n_active, l.fwd.active, l.fwd.err, s);
+  } else {
+    e = coli::launch_quant_act_q8(x, T, D, l.xq, l.xd, s);
+    if (e == hipSuccess) e = coli::launch_route_topk(logits, bias, T, E, k, routed_scale, l.idx, l.w, s);
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  coli::ForwardArgs a;
+  a.table = table;
+  a.xq = l.xq;
+  a.xd = l.xd;
+  a.T = T;
+  a.idx = l.idx;
+  a.w = l.w;
+  a.k = k;
+  a.y = y;
+  a.accumulate = accumulate;
+  a.ws = l.fwd;
+  a.trace = trace;
+  a.events = events ? &fwd_events : nullptr;
+  a.dispatched = small;
+  e = coli::launch_moe_forward(a, s);
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_moe_layer(const coli_expert_table* table, const float* x, const float* logits,
+                   const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                   int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  return coli_moe_layer_ex(table, x, logits, bias, T, k, routed_scale, y, accumulate, workspace,
+                           ws_bytes, nullptr, nullptr, stream);
 }
 
 int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream) {

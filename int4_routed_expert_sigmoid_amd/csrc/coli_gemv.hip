@@ -26,7 +26,10 @@
 //
 // The SwiGLU, the row scale and the Q8_0 re-quantisation of h are fused into
 // the gate/up epilogue; the routing-weighted combine runs as its own kernel in
-// slot order (shared expert first), which keeps it deterministic.
+// slot order (shared expert first), which keeps it deterministic.  (Folding it
+// into the down kernel as a last-arriver reduction needs agent-scope release/
+// acquire fences, which write back and invalidate the L2 of every XCD and
+// measured slower on MI355X than the extra launch.)
 #include "coli_internal.h"
 
 namespace coli {
@@ -35,6 +38,8 @@ namespace {
 constexpr int kWave = 64;
 // Word 3 of a gfx9-family buffer descriptor for raw 32-bit-element access.
 constexpr int kBufferConfig = 0x00020000;
+// Cache-policy operand of a buffer load: non-temporal (streamed once).
+constexpr int kNonTemporal = 2;
 
 struct GuArgs {
   const uint4* gu_q;
@@ -70,7 +75,7 @@ struct DnArgs {
   const int32_t* active;
   float* o;
   int64_t T, D, F;
-  int k, S;
+  int k, S, E;
   int32_t* tr_pd;
 };
 
@@ -95,72 +100,114 @@ __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
   return u;
 }
 
-// One activation block of one token: 8 int8 words, -8 * sum, scale.
-struct XBlock {
-  int x[8];
-  int m8sum;
-  float d;
+// The token blocks of one pass live in LDS: per token, NB blocks of 32 int8
+// (xs) and per block the pair (d, -8 * sum) (dm).  One wavefront stages them
+// once, then reads them with broadcast LDS loads one block ahead of use; LDS
+// returns in order, so those waits never drain the weight ring.
+struct TokenLds {
+  uint4* xs;   // [NB][2] 16-byte halves of each block
+  float2* dm;  // [NB] (d, bitcast(-8 * sum))
 };
 
-__device__ __forceinline__ XBlock load_xblock(cptr<int> xrow, cptr<int> srow, cptr<float> drow,
-                                              int b) {
+__device__ __forceinline__ void stage_token(TokenLds t, const int8_t* __restrict__ xrow,
+                                            const float* __restrict__ drow,
+                                            const int32_t* __restrict__ srow, int NB, int lane) {
+  const uint4* xg = reinterpret_cast<const uint4*>(xrow);
+  for (int i = lane; i < 2 * NB; i += kWave) t.xs[i] = xg[i];
+  for (int b = lane; b < NB; b += kWave) t.dm[b] = make_float2(drow[b], __int_as_float(srow[b]));
+}
+
+struct XBlock {
+  uint4 lo, hi;
+  float2 dm;
+};
+
+__device__ __forceinline__ XBlock read_xblock(TokenLds t, int b) {
   XBlock v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v.x[i] = xrow[8 * b + i];
-  v.m8sum = srow[b];
-  v.d = drow[b];
+  v.lo = t.xs[2 * b];
+  v.hi = t.xs[2 * b + 1];
+  v.dm = t.dm[b];
   return v;
 }
 
 // P_b of one row with one activation block: sum over 32 of q_w * q_x.
 __device__ __forceinline__ int block_dot(const Unpacked& u, const XBlock& xb) {
-  int s = xb.m8sum;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = sdot4((int)u.v[i], xb.x[i], s);
+  int s = __float_as_int(xb.dm.y);
+  s = sdot4((int)u.v[0], (int)xb.lo.x, s);
+  s = sdot4((int)u.v[1], (int)xb.lo.y, s);
+  s = sdot4((int)u.v[2], (int)xb.lo.z, s);
+  s = sdot4((int)u.v[3], (int)xb.lo.w, s);
+  s = sdot4((int)u.v[4], (int)xb.hi.x, s);
+  s = sdot4((int)u.v[5], (int)xb.hi.y, s);
+  s = sdot4((int)u.v[6], (int)xb.hi.z, s);
+  s = sdot4((int)u.v[7], (int)xb.hi.w, s);
   return s;
 }
 
 // Streams the NB chunks of one row group (lane-owned rows) and accumulates
 // exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
 // the ring of PF weight loads in flight: every refill is unconditional (its
-// index is clamped into the row group), the scalar loads of the next
-// activation block are issued one block ahead of use, and a block past the
-// end of the row (only when PF does not divide NB) is computed on clamped
-// data with scale 0, which leaves the accumulator bit-identical (it starts
-// at +0 and so is never -0).
-template <int NT, int PF, bool TRACE>
-__device__ __forceinline__ void stream_rows(const char* __restrict__ wbase, uint32_t loff, int NB,
-                                            const cptr<int>* xrow, const cptr<float>* drow,
-                                            const cptr<int>* srow, float* acc,
-                                            int32_t* const* trace_row) {
-  // Buffer loads: the row group is one descriptor (scalar registers), the
-  // lane's 16-byte column is a constant vector offset and the block is a
-  // scalar offset, so no per-load vector address is built.  Each ring slot
-  // is unpacked before it is refilled, letting the refill reuse the slot's
-  // registers: the ring stays PF loads deep across the loop back-edge.
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, NB * 1024, kBufferConfig);
+// index is clamped into the row group), and a block past the end of the row
+// (only when PF does not divide NB) is computed on clamped data with scale 0,
+// which leaves the accumulator bit-identical (it starts at +0 and so is
+// never -0).  Buffer loads: the row group is one descriptor (scalar
+// registers), the lane's 16-byte column a constant vector offset and the block
+// a scalar offset; each ring slot is unpacked before it is refilled, so the
+// refill reuses the slot's registers and the ring stays PF deep across the
+// loop back-edge.  Weight loads are non-temporal: each byte is used once.
+// The weight ring of one row group: PF outstanding 16-byte loads per lane.
+template <int PF>
+struct Ring {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t loff;
+  int NB;
   u32x4 buf[PF];
+
+  // Issues the first PF loads, in slot order so that slot 0 lands first.
+  __device__ __forceinline__ void start(const char* wbase, uint32_t lane_off, int nb) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, nb * 1024, kBufferConfig);
+    loff = lane_off;
+    NB = nb;
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {   // issued in slot order, so slot 0 lands first
-    buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, (i < NB ? i : NB - 1) * 1024, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < PF; ++i) {
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, (i < NB ? i : NB - 1) * 1024,
+                                                     kNonTemporal);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+};
+
+// Streams the NB chunks of one row group (lane-owned rows) and accumulates
+// exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
+// the ring of PF weight loads in flight: every refill is unconditional (its
+// index is clamped into the row group), and a block past the end of the row
+// (only when PF does not divide NB) is computed on clamped data with scale 0,
+// which leaves the accumulator bit-identical (it starts at +0 and so is
+// never -0).  Buffer loads: the row group is one descriptor (scalar
+// registers), the lane's 16-byte column a constant vector offset and the block
+// a scalar offset; each ring slot is unpacked before it is refilled, so the
+// refill reuses the slot's registers and the ring stays PF deep across the
+// loop back-edge.  Weight loads are non-temporal: each byte is used once.
+template <int NT, int PF, bool TRACE>
+__device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok, float* acc,
+                                            int32_t* const* trace_row) {
+  const int NB = ring.NB;
   XBlock cur[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) cur[j] = load_xblock(xrow[j], srow[j], drow[j], 0);
+  for (int j = 0; j < NT; ++j) cur[j] = read_xblock(tok[j], 0);
   for (int b0 = 0; b0 < NB; b0 += PF) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int b = b0 + i;
-      const Unpacked u = unpack_chunk(buf[i]);
+      const Unpacked u = unpack_chunk(ring.buf[i]);
       __builtin_amdgcn_sched_barrier(0);
       const int bn = b + PF < NB ? b + PF : NB - 1;
-      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, bn * 1024, 0);
+      ring.buf[i] = __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff, bn * 1024,
+                                                          kNonTemporal);
       const int bx = b + 1 < NB ? b + 1 : NB - 1;
       XBlock nxt[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) nxt[j] = load_xblock(xrow[j], srow[j], drow[j], bx);
+      for (int j = 0; j < NT; ++j) nxt[j] = read_xblock(tok[j], bx);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -168,7 +215,7 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ wbase, uint
         if (TRACE) {
           if (trace_row[j] && b < NB) trace_row[j][b] = p;
         }
-        const float d = b < NB ? cur[j].d : 0.0f;
+        const float d = b < NB ? cur[j].dm.x : 0.0f;
         acc[j] = __builtin_fmaf((float)p, d, acc[j]);
         cur[j] = nxt[j];
       }
@@ -179,61 +226,75 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ wbase, uint
 
 // Runs stream_rows for the nt (1..MAXT) tokens of one pass.
 template <int MAXT, int PF, bool TRACE>
-__device__ __forceinline__ void stream_pass(int nt, const char* __restrict__ wbase, uint32_t loff,
-                                            int NB,
-                                            const cptr<int>* xrow, const cptr<float>* drow,
-                                            const cptr<int>* srow, float* acc,
-                                            int32_t* const* trace_row) {
+__device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, const TokenLds* tok,
+                                            float* acc, int32_t* const* trace_row) {
   if (MAXT >= 8 && nt > 4) {
-    stream_rows<(MAXT >= 8 ? 8 : 1), PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+    stream_rows<(MAXT >= 8 ? 8 : 1), PF, TRACE>(ring, tok, acc, trace_row);
   } else if (MAXT >= 4 && nt > 2) {
-    stream_rows<(MAXT >= 4 ? 4 : 1), PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+    stream_rows<(MAXT >= 4 ? 4 : 1), PF, TRACE>(ring, tok, acc, trace_row);
   } else if (MAXT >= 2 && nt == 2) {
-    stream_rows<(MAXT >= 2 ? 2 : 1), PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+    stream_rows<(MAXT >= 2 ? 2 : 1), PF, TRACE>(ring, tok, acc, trace_row);
   } else {
-    stream_rows<1, PF, TRACE>(wbase, loff, NB, xrow, drow, srow, acc, trace_row);
+    stream_rows<1, PF, TRACE>(ring, tok, acc, trace_row);
   }
+}
+
+// Dynamic LDS of a GEMV workgroup: MAXT token records of NB blocks.
+__device__ __forceinline__ TokenLds token_lds(int j, int NB) {
+  extern __shared__ __align__(16) unsigned char coli_lds[];
+  unsigned char* base = coli_lds + (size_t)j * NB * 40;
+  TokenLds t;
+  t.xs = reinterpret_cast<uint4*>(base);
+  t.dm = reinterpret_cast<float2*>(base + (size_t)NB * 32);
+  return t;
 }
 
 template <int MAXT, int PF, bool TRACE>
 __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
   const int grp = blockIdx.x;
   const int slot = blockIdx.y;
-  if (slot >= *as_const(a.n_active)) return;
-  const int e = as_const(a.active)[slot];
-  const int cnt = as_const(a.counts)[e];
+  const int n_active = *as_const(a.n_active);   // both loads in flight together;
+  const int e = as_const(a.active)[slot];        // e is used only once slot is valid
+  if (slot >= n_active) return;
   const int lane = threadIdx.x;
   const int NB = (int)(a.D / 32);
   const int64_t G = a.F / 32;
   const int KS = a.k + a.S;
   const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)e * G + grp) * (size_t)NB * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
+  Ring<PF> ring;
+  ring.start(wbase, loff, NB);          // the weight stream starts before anything else
+  const int cnt = as_const(a.counts)[e];
   const float rs = a.gu_s[((size_t)e * G + grp) * kWave + lane];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
   for (int c0 = 0; c0 < cnt; c0 += MAXT) {
     const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
     int pair[MAXT];
-    cptr<int> xrow[MAXT];
-    cptr<float> drow[MAXT];
-    cptr<int> srow[MAXT];
+    TokenLds tok[MAXT];
     int32_t* trow[MAXT];
+    if (c0 > 0) {
+      __syncthreads();                // the previous pass has finished reading the LDS records
+      ring.start(wbase, loff, NB);    // each pass streams the row group again
+    }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       pair[j] = list[c0 + (j < nt ? j : nt - 1)];
-      const int64_t tok = __builtin_amdgcn_readfirstlane(pair[j] / KS);
-      xrow[j] = as_const(reinterpret_cast<const int*>(a.xq + tok * a.D));
-      drow[j] = as_const(a.xd + tok * NB);
-      srow[j] = as_const(a.xsum8 + tok * NB);
+      tok[j] = token_lds(j < nt ? j : nt - 1, NB);
       trow[j] = nullptr;
       if (TRACE) {
         int32_t* base = lane < 32 ? a.tr_pg : a.tr_pu;
         if (base) trow[j] = base + ((size_t)pair[j] * a.F + 32 * (size_t)grp + (lane & 31)) * NB;
       }
     }
+    for (int j = 0; j < nt; ++j) {
+      const int64_t t = __builtin_amdgcn_readfirstlane(pair[j] / KS);
+      stage_token(tok[j], a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB, lane);
+    }
+    __syncthreads();
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, TRACE>(nt, wbase, loff, NB, xrow, drow, srow, acc, trow);
+    stream_pass<MAXT, PF, TRACE>(nt, ring, tok, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       if (j < nt) {
@@ -267,46 +328,69 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
   }
 }
 
+// One output row of the layer for token t: y = o_shared + sum_j w_j o_j,
+// accumulated as y = fmaf(w_j, o_j, y) in slot order (shared expert first).
+__device__ __forceinline__ float combine_row(const float* __restrict__ o,
+                                             const int32_t* __restrict__ idx,
+                                             const float* __restrict__ w, int64_t t, int64_t r,
+                                             int64_t D, int k, int E, int S) {
+  const int KS = k + S;
+  const float* ot = o + (size_t)t * KS * D;
+  float acc = S ? ot[(size_t)k * D + r] : 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e < 0 || e >= E) continue;
+    acc = __builtin_fmaf(w[t * k + j], ot[(size_t)j * D + r], acc);
+  }
+  return acc;
+}
+
 template <int MAXT, int PF, bool TRACE>
 __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
   const int grp = blockIdx.x;
   const int slot = blockIdx.y;
-  if (slot >= *as_const(a.n_active)) return;
-  const int e = as_const(a.active)[slot];
-  const int cnt = as_const(a.counts)[e];
+  const int n_active = *as_const(a.n_active);   // both loads in flight together;
+  const int e = as_const(a.active)[slot];        // e is used only once slot is valid
+  if (slot >= n_active) return;
   const int lane = threadIdx.x;
   const int NB = (int)(a.F / 32);
-  const int KS = a.k + a.S;
   const char* wbase =
       reinterpret_cast<const char*>(a.dn_q + ((size_t)e * (a.D / 64) + grp) * (size_t)NB * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
+  Ring<PF> ring;
+  ring.start(wbase, loff, NB);          // the weight stream starts before anything else
+  const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
   const float rs = a.dn_s[(size_t)e * a.D + row];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
   for (int c0 = 0; c0 < cnt; c0 += MAXT) {
     const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
     int pair[MAXT];
-    cptr<int> xrow[MAXT];
-    cptr<float> drow[MAXT];
-    cptr<int> srow[MAXT];
+    TokenLds tok[MAXT];
     int32_t* trow[MAXT];
+    if (c0 > 0) {
+      __syncthreads();
+      ring.start(wbase, loff, NB);
+    }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       pair[j] = list[c0 + (j < nt ? j : nt - 1)];
-      xrow[j] = as_const(reinterpret_cast<const int*>(a.hq + (size_t)pair[j] * a.F));
-      drow[j] = as_const(a.hd + (size_t)pair[j] * NB);
-      srow[j] = as_const(a.hsum8 + (size_t)pair[j] * NB);
+      tok[j] = token_lds(j < nt ? j : nt - 1, NB);
       trow[j] = (TRACE && a.tr_pd) ? a.tr_pd + ((size_t)pair[j] * a.D + row) * NB : nullptr;
     }
+    for (int j = 0; j < nt; ++j) {
+      const size_t p = (size_t)__builtin_amdgcn_readfirstlane(pair[j]);
+      stage_token(tok[j], a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB, lane);
+    }
+    __syncthreads();
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, TRACE>(nt, wbase, loff, NB, xrow, drow, srow, acc, trow);
+    stream_pass<MAXT, PF, TRACE>(nt, ring, tok, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j)
       if (j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
   }
-  (void)KS;
 }
 
 // y[t][r] = o_shared + sum_j w_j o_j, as y = fmaf(w_j, o_j, y) in slot order.
@@ -318,16 +402,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const int64_t t = blockIdx.y;
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= D) return;
-  const int KS = k + S;
-  const float* ot = o + (size_t)t * KS * D;
-  float acc = S ? ot[(size_t)k * D + r] : 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if (e < 0 || e >= E) continue;
-    acc = __builtin_fmaf(w[t * k + j], ot[(size_t)j * D + r], acc);
-  }
+  const float v = combine_row(o, idx, w, t, r, D, k, E, S);
   float* yt = y + t * D + r;
-  *yt = accumulate ? *yt + acc : acc;
+  *yt = accumulate ? *yt + v : v;
 }
 
 // Stage events (profiled forward only; not for stream capture, where a record
@@ -336,28 +413,43 @@ hipError_t record(void* ev, hipStream_t s) {
   return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
 }
 
-constexpr int kPfGateUp = 16;
-constexpr int kPfDown = 16;
+constexpr int kPfGateUp = 16;       // weight loads in flight per wavefront
+constexpr int kPfDown = 8;
+constexpr int kLdsBytesPerBlock = 40;
+constexpr size_t kLdsLimit = 65536;
 
 template <int MAXT, bool TRACE>
 hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
+  const size_t lds_gu = (size_t)MAXT * (size_t)(g.D / 32) * kLdsBytesPerBlock;
+  const size_t lds_dn = (size_t)MAXT * (size_t)(d.F / 32) * kLdsBytesPerBlock;
   hipLaunchKernelGGL((gate_up_kernel<MAXT, kPfGateUp, TRACE>), dim3((unsigned)(g.F / 32), maxA),
-                     dim3(kWave), 0, s, g);
+                     dim3(kWave), lds_gu, s, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev_down, s)) != hipSuccess) return rc;
-  hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, TRACE>), dim3((unsigned)(d.D / 64), maxA),
-                     dim3(kWave), 0, s, d);
+  hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, TRACE>),
+                     dim3((unsigned)(d.D / 64), maxA), dim3(kWave), lds_dn, s, d);
   return hipGetLastError();
+}
+
+// Tokens per pass: the batch (a power of two up to 8), capped so that the
+// pass's LDS token records fit in 64 KB.
+int pass_tokens(int64_t T, int64_t D, int64_t F) {
+  const int64_t nb = (D > F ? D : F) / 32;
+  int m = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
+  while (m > 1 && (size_t)m * nb * kLdsBytesPerBlock > kLdsLimit) m /= 2;
+  return m;
 }
 
 template <bool TRACE>
 hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, void* ev_down,
                        hipStream_t s) {
-  if (T <= 1) return launch_pair<1, TRACE>(g, d, maxA, ev_down, s);
-  if (T <= 2) return launch_pair<2, TRACE>(g, d, maxA, ev_down, s);
-  if (T <= 4) return launch_pair<4, TRACE>(g, d, maxA, ev_down, s);
-  return launch_pair<8, TRACE>(g, d, maxA, ev_down, s);
+  switch (pass_tokens(T, g.D, g.F)) {
+    case 1: return launch_pair<1, TRACE>(g, d, maxA, ev_down, s);
+    case 2: return launch_pair<2, TRACE>(g, d, maxA, ev_down, s);
+    case 4: return launch_pair<4, TRACE>(g, d, maxA, ev_down, s);
+    default: return launch_pair<8, TRACE>(g, d, maxA, ev_down, s);
+  }
 }
 
 }  // namespace
@@ -372,9 +464,11 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   const coli_moe_events& ev = f.events ? *f.events : no_events;
   hipError_t rc = record(ev.begin, s);
   if (rc != hipSuccess) return rc;
-  rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active,
-                                  ws.active, ws.err, f.xq, D, ws.xsum8, s);
-  if (rc != hipSuccess) return rc;
+  if (!f.dispatched) {
+    rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active, ws.active, ws.err,
+                         f.xq, D, ws.xsum8, s);
+    if (rc != hipSuccess) return rc;
+  }
   const int64_t maxA = (T * f.k < E ? T * f.k : E) + S;
 
   GuArgs g = {};
@@ -411,6 +505,7 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   d.F = F;
   d.k = f.k;
   d.S = S;
+  d.E = E;
   if ((rc = record(ev.gate_up, s)) != hipSuccess) return rc;
   const coli_moe_trace* tr = f.trace;
   if (tr) {
@@ -442,6 +537,10 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
       {tr->hq, ws.hq, (size_t)(P * F)},
       {tr->hd, ws.hd, sizeof(float) * P * (F / 32)},
       {tr->o, ws.o, sizeof(float) * P * D},
+      {f.dispatched ? tr->xq : nullptr, f.xq, (size_t)(T * D)},
+      {f.dispatched ? tr->xd : nullptr, f.xd, sizeof(float) * T * (D / 32)},
+      {f.dispatched ? tr->idx : nullptr, f.idx, sizeof(int32_t) * T * f.k},
+      {f.dispatched ? tr->w : nullptr, f.w, sizeof(float) * T * f.k},
   };
   for (const Copy& c : copies) {
     if (!c.dst) continue;

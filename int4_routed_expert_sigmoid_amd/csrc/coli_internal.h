@@ -48,6 +48,26 @@ __device__ __forceinline__ int q8_code(float v, float d) {
   return (int)q;
 }
 
+// Q8_0 of 4 consecutive values held by one lane; 8 consecutive lanes form one
+// 32-value block.  Returns the 4 codes packed little-endian in an int32, the
+// block scale and the block's code sum (all identical in the 8 lanes).
+__device__ __forceinline__ int q8_quad(float4 v, float* d_out, int* sum_out) {
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+  const float d = amax / 127.0f;
+  *d_out = d;
+  const int q0 = q8_code(v.x, d), q1 = q8_code(v.y, d), q2 = q8_code(v.z, d),
+            q3 = q8_code(v.w, d);
+  int sum = q0 + q1 + q2 + q3;
+  sum += __shfl_xor(sum, 1, 8);
+  sum += __shfl_xor(sum, 2, 8);
+  sum += __shfl_xor(sum, 4, 8);
+  *sum_out = sum;
+  return (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((int)((unsigned)q3 << 24));
+}
+
 // Read-only data that is uniform across a wavefront (the token's Q8 block,
 // dispatch lists) is read through the constant address space: the compiler
 // then issues scalar loads, which complete on lgkmcnt and leave the vector
@@ -101,6 +121,17 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, i
                            int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
                            const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s);
 
+// Fused front of a small batch (one workgroup): Q8_0 of x (+ block sums),
+// routing, dispatch lists, compaction and the index check.
+hipError_t launch_prologue_small(const float* x, const float* logits, const float* bias, int64_t T,
+                                 int E, int S, int k, float routed_scale, int64_t D, int8_t* xq,
+                                 float* xd, int32_t* xsum8, int32_t* idx, float* w,
+                                 int32_t* counts, int32_t* lists, int32_t* n_active,
+                                 int32_t* active, int32_t* err, hipStream_t s);
+// Largest batch the fused front handles.
+constexpr int64_t kPrologueMaxEntries = 1024;   // T * k
+constexpr int64_t kPrologueMaxTokens = 64;
+
 struct ForwardArgs {
   const coli_expert_table* table;
   const int8_t* xq;
@@ -114,6 +145,7 @@ struct ForwardArgs {
   MoeWorkspace ws;
   const coli_moe_trace* trace;   // may be null
   const coli_moe_events* events; // may be null
+  bool dispatched;               // the workspace already holds dispatch + xsum8
 };
 hipError_t launch_moe_forward(const ForwardArgs& a, hipStream_t s);
 

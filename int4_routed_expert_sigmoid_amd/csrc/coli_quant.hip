@@ -19,22 +19,6 @@ namespace {
 
 constexpr int kWave = 64;
 
-// ---------------------------------------------------------------------------
-// Q8_0 of 4 consecutive values held by one lane; 8 consecutive lanes form one
-// 32-value block.  Returns the 4 codes packed in a little-endian int32 and the
-// block scale (identical in the 8 lanes).
-__device__ __forceinline__ int q8_quad(float4 v, float* d_out) {
-  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-  const float d = amax / 127.0f;
-  *d_out = d;
-  const int q0 = q8_code(v.x, d), q1 = q8_code(v.y, d), q2 = q8_code(v.z, d),
-            q3 = q8_code(v.w, d);
-  return (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((int)((unsigned)q3 << 24));
-}
-
 __global__ void __launch_bounds__(256) quant_act_q8_kernel(const float4* __restrict__ x,
                                                            int64_t n4, int* __restrict__ q,
                                                            float* __restrict__ d) {
@@ -43,7 +27,8 @@ __global__ void __launch_bounds__(256) quant_act_q8_kernel(const float4* __restr
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     float dv;
-    const int packed = q8_quad(x[i], &dv);
+    int sum;
+    const int packed = q8_quad(x[i], &dv, &sum);
     q[i] = packed;
     if ((i & 7) == 0) d[i >> 3] = dv;
   }
@@ -187,7 +172,8 @@ __global__ void __launch_bounds__(256) rmsnorm_q8_kernel(const float* __restrict
     const float4 v = hr[c];
     const float4 xh = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
     float dv;
-    const int packed = q8_quad(xh, &dv);
+    int sum;
+    const int packed = q8_quad(xh, &dv, &sum);
     q[row * (D / 4) + c] = packed;
     if ((c & 7) == 0) d[row * (D / 32) + (c >> 3)] = dv;
   }

@@ -4,7 +4,7 @@
 // attention-and-kernels section): sigmoid scores, a per-expert bias that only
 // steers selection, top-k, weights normalised over the selected set.  One
 // wavefront routes one token: each lane holds up to 4 of the <= 256 experts,
-// and each of the k rounds is a 64-lane arg-max under a strict total order
+// and each of the k rounds is a 64-lane max under a strict total order
 // (larger score first, lower index on ties), so the result is independent of
 // the reduction order.
 //
@@ -15,13 +15,60 @@
 // prefix popcounts: stable and deterministic without atomics.
 #include "coli_internal.h"
 
+// Wavefront max of a 64-bit value (ROCm device library, DPP-based).
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(
+    unsigned long long);
+
 namespace coli {
 namespace {
 
 constexpr int kWave = 64;
 
-__device__ __forceinline__ bool better(float ca, int ea, float cb, int eb) {
-  return ca > cb || (ca == cb && ea < eb);
+// Order-preserving unsigned image of a float (for finite values and +0;
+// the selection score c = sigmoid + bias is never -0).
+__device__ __forceinline__ uint32_t ordered_bits(float c) {
+  const uint32_t b = __float_as_uint(c);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Routes one token with one wavefront: lane j < k receives the j-th selected
+// expert and its weight.  Each candidate is one 64-bit key, the ordered bits
+// of its selection score above the inverted expert index, so that a larger
+// key is a larger score or, on a tie, the lower index: the strict order of
+// the selection.  Each of the k rounds is one wavefront max (DPP) of the
+// lanes' best remaining keys; the winner is struck out.  The selected
+// experts' sigmoid scores are recomputed by their slot lanes and summed in
+// slot order through readlane.
+__device__ __forceinline__ void route_token(const float* __restrict__ lg,
+                                            const float* __restrict__ bias, int E, int k,
+                                            float routed_scale, int lane, int* out_idx,
+                                            float* out_w) {
+  uint64_t key[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = 0;   // below every real key
+    if (e < E) {
+      const float c = sigmoid_f32(lg[e]) + (bias ? bias[e] : 0.0f);
+      key[i] = ((uint64_t)ordered_bits(c) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    }
+  }
+  int my_idx = -1;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0] > key[1] ? key[0] : key[1];
+    const uint64_t b23 = key[2] > key[3] ? key[2] : key[3];
+    best = best > b23 ? best : b23;
+    const uint64_t win = __ockl_wfred_max_u64((unsigned long long)best);   // wavefront max
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = key[i] == win ? 0 : key[i];
+    if (lane == j) my_idx = (int)(0xFFFFFFFFu - (uint32_t)win);
+  }
+  const float my_s = lane < k ? sigmoid_f32(lg[my_idx]) : 0.0f;
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j)
+    sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+  *out_idx = my_idx;
+  *out_w = (my_s / sum) * routed_scale;
 }
 
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits,
@@ -33,51 +80,33 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
   const int lane = threadIdx.x % kWave;
   const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  float s[4], c[4];
-  bool live[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + kWave * i;
-    live[i] = e < E;
-    s[i] = 0.0f;
-    c[i] = -__builtin_inff();
-    if (live[i]) {
-      s[i] = sigmoid_f32(logits[t * E + e]);
-      c[i] = s[i] + (bias ? bias[e] : 0.0f);
-    }
-  }
-  int my_idx = -1;
-  float my_s = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bc = -__builtin_inff();
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (live[i] && better(c[i], lane + kWave * i, bc, be)) { bc = c[i]; be = lane + kWave * i; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float oc = __shfl_xor(bc, off);
-      const int oe = __shfl_xor(be, off);
-      if (better(oc, oe, bc, be)) { bc = oc; be = oe; }
-    }
-    // be is now the same winner in every lane
-    const int wl = be % kWave, wi = be / kWave;
-    float ws = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) if (i == wi) ws = s[i];
-    ws = __shfl(ws, wl);
-    if (lane == wl) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) if (i == wi) live[i] = false;
-    }
-    if (lane == j) { my_idx = be; my_s = ws; }
-  }
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum = sum + __shfl(my_s, j);
+  int my_idx;
+  float my_w;
+  route_token(logits + t * E, bias, E, k, routed_scale, lane, &my_idx, &my_w);
   if (lane < k) {
     idx[t * k + lane] = my_idx;
-    w[t * k + lane] = (my_s / sum) * routed_scale;
+    w[t * k + lane] = my_w;
   }
+}
+
+// One wavefront builds expert e's list of pairs from the n = T*k routing
+// entries (entry i is token i/k, slot i%k), in entry order = token order.
+// Returns the count (capped at T, the list capacity).
+template <class Entry>
+__device__ __forceinline__ int expert_list(int e, int64_t T, int k, int S, Entry entry,
+                                           int32_t* __restrict__ le, int lane) {
+  const int64_t n = T * k;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int64_t base = 0;
+  for (int64_t i0 = 0; i0 < n; i0 += kWave) {
+    const int64_t i = i0 + lane;
+    const bool hit = i < n && entry(i) == e;
+    const uint64_t m = __ballot(hit);
+    const int64_t pos = base + __popcll(m & lt);
+    if (hit && pos < T) le[pos] = (int32_t)((i / k) * (k + S) + i % k);
+    base += __popcll(m);
+  }
+  return (int)(base < T ? base : T);
 }
 
 // One wavefront per expert e in [0, E+S).
@@ -94,18 +123,8 @@ __global__ void __launch_bounds__(256) dispatch_lists_kernel(const int32_t* __re
     if (lane == 0) counts[e] = (int32_t)T;
     return;
   }
-  const int64_t n = T * k;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int64_t base = 0;
-  for (int64_t i0 = 0; i0 < n; i0 += kWave) {
-    const int64_t i = i0 + lane;
-    const bool hit = i < n && idx[i] == e;
-    const uint64_t m = __ballot(hit);
-    const int64_t pos = base + __popcll(m & lt);
-    if (hit && pos < T) le[pos] = (int32_t)((i / k) * (k + S) + i % k);
-    base += __popcll(m);
-  }
-  if (lane == 0) counts[e] = (int32_t)(base < T ? base : T);
+  const int cnt = expert_list(e, T, k, S, [&](int64_t i) { return idx[i]; }, le, lane);
+  if (lane == 0) counts[e] = cnt;
 }
 
 // Workgroup 0: compact the active-expert list and check the indices.
@@ -157,7 +176,128 @@ __global__ void __launch_bounds__(256) dispatch_finish_kernel(
   }
 }
 
+struct PrologueArgs {
+  const float* x;
+  const float* logits;
+  const float* bias;
+  int64_t T, D;
+  int E, S, k;
+  float routed_scale;
+  int8_t* xq;
+  float* xd;
+  int32_t* xsum8;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* lists;
+  int32_t* n_active;
+  int32_t* active;
+  int32_t* err;
+};
+
+// The whole front of a small batch.  Workgroup 0 (4 wavefronts): routing (one
+// wavefront per token), then the dispatch lists (one thread per routing
+// entry, entries from LDS), the active-expert compaction and the index check.
+// Workgroups 1..: Q8_0 of every token with its block sums, in parallel.
+__global__ void __launch_bounds__(256) prologue_small_kernel(PrologueArgs a) {
+  __shared__ int ent[kPrologueMaxEntries];
+  __shared__ bool valid[kPrologueMaxEntries];
+  __shared__ int cnt_lds[COLI_MAX_EXPERTS + 1];
+  __shared__ int bad_any;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  if (tid == 0) bad_any = 0;
+  if (blockIdx.x > 0) {
+    // workgroups 1..: Q8_0 of x in groups of 4 values, 8 lanes per 32-value
+    // block (groups never straddle a block: 256-thread strides, n4 % 8 == 0)
+    const int64_t n4 = a.T * a.D / 4;
+    const float4* x4 = reinterpret_cast<const float4*>(a.x);
+    int* q4 = reinterpret_cast<int*>(a.xq);
+    const int64_t stride = (int64_t)(gridDim.x - 1) * 256;
+    for (int64_t g = (int64_t)(blockIdx.x - 1) * 256 + tid; g < n4; g += stride) {
+      float dv;
+      int sum;
+      q4[g] = q8_quad(x4[g], &dv, &sum);
+      if ((g & 7) == 0) {
+        a.xd[g >> 3] = dv;
+        a.xsum8[g >> 3] = -8 * sum;
+      }
+    }
+    return;
+  }
+  // workgroup 0: routing, one wavefront per token, then the dispatch
+  for (int64_t t = wave; t < a.T; t += 4) {
+    int my_idx;
+    float my_w;
+    route_token(a.logits + t * a.E, a.bias, a.E, a.k, a.routed_scale, lane, &my_idx, &my_w);
+    if (lane < a.k) {
+      a.idx[t * a.k + lane] = my_idx;
+      a.w[t * a.k + lane] = my_w;
+      ent[t * a.k + lane] = my_idx;
+    }
+  }
+  for (int e = tid; e < a.E + a.S; e += 256) cnt_lds[e] = 0;
+  __syncthreads();
+  // dispatch, one thread per routing entry: its position in its expert's list
+  // is the number of earlier entries (= earlier tokens) that chose the same
+  // expert, so the lists come out in token order with no ordering pass
+  const int64_t n = a.T * a.k;
+  int bad = 0;
+  for (int64_t i = tid; i < n; i += 256) {   // an entry is listed if in range and first in its token
+    const int e = ent[i];
+    bool ok = e >= 0 && e < a.E;
+    for (int64_t j = (i / a.k) * a.k; ok && j < i; ++j) ok = ent[j] != e;
+    valid[i] = ok;
+    bad |= !ok;
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 256) {
+    if (!valid[i]) continue;
+    const int e = ent[i];
+    const int64_t t0 = (i / a.k) * a.k;
+    int pos = 0;                               // valid entries of earlier tokens: pos <= t < T
+    for (int64_t j = 0; j < t0; ++j) pos += valid[j] && ent[j] == e;
+    atomicAdd(&cnt_lds[e], 1);
+    a.lists[(int64_t)e * a.T + pos] = (int32_t)((i / a.k) * (a.k + a.S) + i % a.k);
+  }
+  if (a.S) {
+    for (int64_t t = tid; t < a.T; t += 256)
+      a.lists[(int64_t)a.E * a.T + t] = (int32_t)(t * (a.k + a.S) + a.k);
+    if (tid == 0) cnt_lds[a.E] = (int)a.T;
+  }
+  if (bad) atomicOr(&bad_any, 1);
+  __syncthreads();
+  for (int e = tid; e < a.E + a.S; e += 256) a.counts[e] = cnt_lds[e];
+  if (wave == 0) {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
+    for (int e0 = 0; e0 < a.E + a.S; e0 += kWave) {
+      const int e = e0 + lane;
+      const bool on = e < a.E + a.S && cnt_lds[e] > 0;
+      const uint64_t m = __ballot(on);
+      if (on) a.active[base + __popcll(m & lt)] = e;
+      base += __popcll(m);
+    }
+    if (lane == 0) {
+      *a.n_active = base;
+      *a.err = bad_any ? (int)COLI_E_INDEX : 0;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prologue_small(const float* x, const float* logits, const float* bias, int64_t T,
+                                 int E, int S, int k, float routed_scale, int64_t D, int8_t* xq,
+                                 float* xd, int32_t* xsum8, int32_t* idx, float* w,
+                                 int32_t* counts, int32_t* lists, int32_t* n_active,
+                                 int32_t* active, int32_t* err, hipStream_t s) {
+  PrologueArgs a = {x, logits, bias, T, D, E, S, k, routed_scale, xq, xd, xsum8, idx, w,
+                    counts, lists, n_active, active, err};
+  int64_t qgroups = (T * D / 4 + 255) / 256;   // one group of 4 values per thread
+  if (qgroups > 256) qgroups = 256;
+  hipLaunchKernelGGL(prologue_small_kernel, dim3((unsigned)(1 + qgroups)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, int E, int k,
                              float routed_scale, int32_t* idx, float* w, hipStream_t s) {

@@ -123,3 +123,20 @@ def test_workspace_grows_with_tokens():
     assert 0 < a < b
     # per-pair outputs dominate: T (k+S) D fp32
     assert b >= 2048 * 9 * 6144 * 4
+
+
+def test_validation_layer():
+    L = coli.lib()
+    t = _table()
+    ws = L.coli_moe_layer_workspace_bytes(ctypes.byref(t), 4, 2)
+    assert ws > L.coli_moe_workspace_bytes(ctypes.byref(t), 4, 2)
+    f = L.coli_moe_layer
+    args = lambda tab, T=4, k=2, sc=1.0, acc=0, wsb=ws, x=FAKE: (
+        ctypes.byref(tab), x, FAKE, None, T, k, sc, FAKE, acc, FAKE, wsb, None)
+    assert f(*args(t, wsb=ws - 1)) == coli.COLI_E_WORKSPACE
+    assert f(*args(t, k=3 * 0)) == coli.COLI_E_SHAPE
+    assert f(*args(t, sc=float("nan"))) == coli.COLI_E_INVAL
+    assert f(*args(t, x=None)) == coli.COLI_E_INVAL
+    assert f(*args(t, x=FAKE + 4)) == coli.COLI_E_INVAL     # x must be 16-byte aligned
+    assert f(*args(t, acc=5)) == coli.COLI_E_INVAL
+    assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK

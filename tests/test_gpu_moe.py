@@ -224,3 +224,75 @@ def test_prefill_layer_sampled(big):
                              idx[sample], wt[sample])
     assert_bitexact("y sample", g["y"][sample], ys)
     assert_within_tol("y sample", g["y"][sample], ys, A)
+
+
+# ---------------------------------------------------------------- coli_moe_layer (fused front)
+def run_layer(table, w, x, logits, bias, trace=False, y0=None, accumulate=False):
+    T = x.shape[0]
+    ws = torch.empty(coli.coli_moe_layer_workspace_bytes(table, T, w.k), dtype=torch.uint8,
+                     device=dev)
+    y = to_dev(y0) if y0 is not None else torch.empty((T, w.D), dtype=torch.float32, device=dev)
+    tr = None
+    if trace:
+        P, A = T * (w.k + w.S), w.E + w.S
+        shapes = {"counts": ((A,), torch.int32), "lists": ((A, T), torch.int32),
+                  "n_active": ((1,), torch.int32), "active": ((A,), torch.int32),
+                  "p_gate": ((P, w.F, w.D // 32), torch.int32),
+                  "p_up": ((P, w.F, w.D // 32), torch.int32),
+                  "p_down": ((P, w.D, w.F // 32), torch.int32),
+                  "g": ((P, w.F), torch.float32), "u": ((P, w.F), torch.float32),
+                  "h": ((P, w.F), torch.float32), "hq": ((P, w.F), torch.int8),
+                  "hd": ((P, w.F // 32), torch.float32), "o": ((P, w.D), torch.float32),
+                  "xq": ((T, w.D), torch.int8), "xd": ((T, w.D // 32), torch.float32),
+                  "idx": ((T, w.k), torch.int32), "w": ((T, w.k), torch.float32)}
+        tr = {k: torch.empty(s, dtype=d, device=dev) for k, (s, d) in shapes.items()}
+    coli.coli_moe_layer(table, to_dev(x), to_dev(logits), to_dev(bias), w.k, y, ws,
+                        accumulate=accumulate, trace=tr)
+    assert coli.coli_moe_status(ws) == coli.COLI_OK
+    out = {"y": y.cpu().numpy()}
+    if tr:
+        out.update({k: v.cpu().numpy() for k, v in tr.items()})
+    return out
+
+
+def test_layer_entry_tiny_traced(tiny):
+    """Fused front (Q8 + route + dispatch in one workgroup): every intermediate."""
+    w, table, ox = tiny
+    x, lg, b = synth.activations(w, w.T, 300), synth.logits(w, w.T, 300), synth.router_bias(w)
+    g = run_layer(table, w, x, lg, b, trace=True)
+    r = oracle_layer(ox, w, x, lg, b)
+    check_front(g, r)
+    check_trace(g, ox, w, r)
+    assert_bitexact("y", g["y"], r["y"])
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 200, 512])
+def test_layer_entry_batch_sizes(tiny, T):
+    """Both sides of the fused-front threshold (T <= 64 and T*k <= 1024)."""
+    w, table, ox = tiny
+    x, lg, b = synth.activations(w, T, 400), synth.logits(w, T, 400), synth.router_bias(w)
+    y0 = synth.normal(999, T * w.D, 1.0).reshape(T, w.D)
+    g = run_layer(table, w, x, lg, b, y0=y0, accumulate=True)
+    r = oracle_layer(ox, w, x, lg, b, y0=y0, accumulate=True)
+    assert_bitexact("y", g["y"], r["y"])
+
+
+def test_layer_entry_decode_traced(big):
+    table, ox = big
+    w = synth.WORKLOADS[1]
+    x, lg, b = synth.activations(w, 1, 5), synth.logits(w, 1, 5), synth.router_bias(w)
+    g = run_layer(table, w, x, lg, b, trace=True)
+    r = oracle_layer(ox, w, x, lg, b)
+    check_front(g, r)
+    check_trace(g, ox, w, r)
+    assert_bitexact("y", g["y"], r["y"])
+    assert_within_tol("y", g["y"], r["y"], r["absterm"])
+
+
+def test_layer_entry_verify(big):
+    table, ox = big
+    w = synth.WORKLOADS[2]
+    x, lg, b = synth.activations(w, 4, 8), synth.logits(w, 4, 8), synth.router_bias(w)
+    g = run_layer(table, w, x, lg, b)
+    r = oracle_layer(ox, w, x, lg, b)
+    assert_bitexact("y", g["y"], r["y"])
