@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of MI355X
 METRIC = "MoE-layer decode tok/s + achieved HBM GB/s (int4 experts); prefill int8 TOPS"
 
 
@@ -113,6 +114,71 @@ def cpu_baseline(w, synth, seconds):
                       f"({tokens} token-layers); quantise+route+MoE per token"}
 
 
+def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
+    """2048 tokens through the same layer in one coli_moe_layer call (the
+    grouped matrix-core path): pass time, int8-equivalent TOPS of the expert
+    matmuls, and the per-stage split measured with HIP events."""
+    w = synth.WORKLOADS[3]
+    T = w.T
+    x = torch.from_numpy(synth.activations(w, T)).cuda()
+    lg = torch.from_numpy(synth.logits(w, T)).cuda()
+    b = torch.from_numpy(synth.router_bias(w)).cuda()
+    if bias_free:
+        b.zero_()
+    y = torch.empty((T, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(coli.coli_moe_layer_workspace_bytes(table, T, w.k), dtype=torch.uint8,
+                     device="cuda")
+    tr = {"counts": torch.empty(w.E + w.S, dtype=torch.int32, device="cuda")}
+
+    def once(events=None, trace=None):
+        coli.coli_moe_layer(table, x, lg, b, w.k, y, ws, events=events, trace=trace)
+
+    once(trace=tr)
+    torch.cuda.synchronize()
+    if coli.coli_moe_status(ws) != coli.COLI_OK:
+        raise RuntimeError("device-side index check failed (prefill)")
+    counts = tr["counts"].cpu().numpy()[: w.E]
+    for _ in range(warmup):
+        once()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        once()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    names = ("begin", "gate_up", "down", "combine", "end")
+    evs = [{k: hev.create() for k in names} for _ in range(3)]
+    for e in evs:
+        once(events=e)
+    torch.cuda.synchronize()
+
+    def avg(a, c):
+        return sum(hev.elapsed_ms(e[a], e[c]) for e in evs) / len(evs)
+
+    gu_ms, dn_ms = avg("gate_up", "down"), avg("down", "combine")
+    fr_ms, cb_ms = avg("begin", "gate_up"), avg("combine", "end")
+    pairs = T * (w.k + w.S)
+    ops_gu = 2.0 * pairs * 2 * w.F * w.D
+    ops_dn = 2.0 * pairs * w.D * w.F
+    tops = (ops_gu + ops_dn) / (ms * 1e-3) / 1e12
+    used = int((counts > 0).sum())
+    return {
+        "workload": w.name + (" (router bias 0)" if bias_free else ""),
+        "tokens": T, "experts_used": used + w.S, "max_tokens_per_expert": int(counts.max()),
+        "ms_per_pass": round(ms, 4), "tok_s": round(T / (ms * 1e-3), 1),
+        "int8_tops": round(tops, 1), "int8_peak_tops": INT8_PEAK_TOPS,
+        "frac_of_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+        "kernels_ms": {"front": round(fr_ms, 4), "gate_up": round(gu_ms, 4),
+                       "down": round(dn_ms, 4), "combine": round(cb_ms, 4)},
+        "gate_up_tops": round(ops_gu / (gu_ms * 1e-3) / 1e12, 1),
+        "down_tops": round(ops_dn / (dn_ms * 1e-3) / 1e12, 1),
+        "weight_gbps": round((used + w.S) * sum(expert_bytes(w)) / (ms * 1e-3) / 1e9, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +188,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps directly, no HIP graph")
+    ap.add_argument("--prefill-steps", type=int, default=20,
+                    help="timed 2048-token passes of the prefill leg (0: skip it)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -257,6 +325,10 @@ def main():
         "wall_s": round(wall, 3),
         "setup_s": round(setup_s, 1),
     }
+    if args.prefill_steps > 0:
+        out["prefill"] = [prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3),
+                          prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3,
+                                      bias_free=True)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -464,11 +464,20 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   const coli_moe_events& ev = f.events ? *f.events : no_events;
   hipError_t rc = record(ev.begin, s);
   if (rc != hipSuccess) return rc;
+  const bool grouped = T >= kMfmaMinTokens && mfma_path_fits(T, D, F, f.k, S);
   if (!f.dispatched) {
+    // the GEMV path also needs the code sums of x; the grouped path does not
     rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active, ws.active, ws.err,
-                         f.xq, D, ws.xsum8, s);
+                         grouped ? nullptr : f.xq, D, ws.xsum8, s);
     if (rc != hipSuccess) return rc;
   }
+  const coli_moe_trace* tr = f.trace;
+  if (grouped) {
+    if ((rc = launch_mfma_front(t, f.xq, T, ws, s)) != hipSuccess) return rc;
+    if ((rc = record(ev.gate_up, s)) != hipSuccess) return rc;
+    rc = launch_mfma_ffn(t, f.xd, T, f.k, ws, tr, ev.down, s);
+  }
+  if (!grouped) {
   const int64_t maxA = (T * f.k < E ? T * f.k : E) + S;
 
   GuArgs g = {};
@@ -507,7 +516,6 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   d.S = S;
   d.E = E;
   if ((rc = record(ev.gate_up, s)) != hipSuccess) return rc;
-  const coli_moe_trace* tr = f.trace;
   if (tr) {
     g.tr_pg = tr->p_gate;
     g.tr_pu = tr->p_up;
@@ -518,6 +526,7 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
     rc = launch_gemv<true>(g, d, (int)maxA, T, ev.down, s);
   } else {
     rc = launch_gemv<false>(g, d, (int)maxA, T, ev.down, s);
+  }
   }
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev.combine, s)) != hipSuccess) return rc;

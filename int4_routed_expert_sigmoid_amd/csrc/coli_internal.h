@@ -97,6 +97,12 @@ struct MoeWorkspace {
   float* hd;         // [P][F/32]
   int32_t* hsum8;    // [P][F/32]   -8 * sum of each Q8 block of h
   float* o;          // [P][D]
+  // grouped (matrix-core) path only
+  uint16_t* xh;      // [T][D/32][32] f16 codes of xq in MFMA operand order
+  uint16_t* h16;     // [P][F/32][32] f16 codes of Q8(h) in MFMA operand order
+  int32_t* gu_items; // [chunks * gate/up quads][2] work items
+  int32_t* dn_items; // [chunks * down quads][2]
+  int32_t* totals;   // [2] item counts
   size_t bytes;
 };
 
@@ -148,5 +154,20 @@ struct ForwardArgs {
   bool dispatched;               // the workspace already holds dispatch + xsum8
 };
 hipError_t launch_moe_forward(const ForwardArgs& a, hipStream_t s);
+
+// Grouped (matrix-core) expert FFN, used from kMfmaMinTokens tokens per pass.
+constexpr int64_t kMfmaMinTokens = 128;
+bool mfma_path_fits(int64_t T, int64_t D, int64_t F, int k, int S);
+int64_t mfma_max_chunks(int64_t T, int k, int E, int S);
+int mfma_quads_gate_up(int64_t F);
+int mfma_quads_down(int64_t D);
+// Work lists and f16 activation codes; needs the dispatch lists.
+hipError_t launch_mfma_front(const coli_expert_table& t, const int8_t* xq, int64_t T,
+                             const MoeWorkspace& ws, hipStream_t s);
+// gate/up + SwiGLU + Q8(h), then down, writing ws.o; ev_down (may be null) is
+// recorded between the two.
+hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t T, int k,
+                           const MoeWorkspace& ws, const coli_moe_trace* tr, void* ev_down,
+                           hipStream_t s);
 
 }  // namespace coli
