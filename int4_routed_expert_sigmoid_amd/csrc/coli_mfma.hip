@@ -110,10 +110,16 @@ __device__ __forceinline__ f32x16 mfma(half8 a, half8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// The ordered rescale acc = fmaf(P, d, acc) of every element of a tile.
-__device__ __forceinline__ void rescale(f32x16& acc, const f32x16& p, float d) {
+// The ordered rescale acc = fmaf(P, d, acc) of every element of a tile, kept
+// where it is written: the empty volatile asm statements make P an input
+// produced at this point and acc an output consumed here, so the compiler
+// neither hoists the fmaf group above the preceding MFMAs nor sinks it into
+// the next block.
+__device__ __forceinline__ void rescale(f32x16& acc, f32x16 p, float d) {
+  asm volatile("" : "+v"(p));
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(p[i], d, acc[i]);
+  asm volatile("" : "+v"(acc));
 }
 
 // Row of a 32x32 tile held by register i of lane l; the lane's column (token)
@@ -248,45 +254,80 @@ struct Acc {
   f32x16 t0[NSUB], t1[NSUB];   // tile 0 (rows 0-31 of the group), tile 1 (rows 32-63)
 };
 
-// Block b = b0 + J of stage slot `slot`: MFMAs with the operands unpacked one
-// block earlier, the next block's operands, then the ordered rescale.
+// Token operands (two K-halves per subtile) of block J of a stage slot.
+template <int NSUB>
+struct BOps {
+  half8 k0[NSUB], k1[NSUB];
+};
+
+template <int NSUB>
+__device__ __forceinline__ void read_bops(const StageLds& L, int slot, int J, int p0, int p1,
+                                          int lane, BOps<NSUB>& o) {
+  const uint4* xs = &L.x[slot][J][0][0];
+  const int n = lane & 31;
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    o.k0[s] = __builtin_bit_cast(half8, xs[(32 * s + n) * 4 + p0]);
+    o.k1[s] = __builtin_bit_cast(half8, xs[(32 * s + n) * 4 + p1]);
+  }
+}
+
+#define COLI_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Block b = b0 + J of stage slot `slot`, in an order that keeps the matrix
+// pipe and the VALU busy together: the MFMAs of subtile 0, the first half of
+// the next block's nibble expansion, the rescale of tile 0, the MFMAs of
+// subtile 1, the rescale of tile 1, the second half of the expansion, then
+// the rescales of subtile 1.  The next block's token operands are read from
+// LDS while this block computes (within a stage).
 template <int NSUB, bool TRACE, int J>
 __device__ __forceinline__ void block_step(const StageLds& L, int slot, int b0, int NB,
                                            const WeightRows& wr, u32x4 (&wq)[kPfW], TileOps& cur,
-                                           const UnpackConsts& uc, const float (&dv)[NSUB][kStage],
-                                           int p0, int p1, Acc<NSUB>& acc,
-                                           int32_t* const (&tr0)[NSUB],
+                                           BOps<NSUB>& bo, const UnpackConsts& uc,
+                                           const float (&dv)[NSUB][kStage], int p0, int p1,
+                                           Acc<NSUB>& acc, int32_t* const (&tr0)[NSUB],
                                            int32_t* const (&tr1)[NSUB], int lane) {
   const int b = b0 + J;
-  const uint4* xs = &L.x[slot][J][0][0];
-  const int n = lane & 31;
-  half8 bx0[NSUB], bx1[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    bx0[s] = __builtin_bit_cast(half8, xs[(32 * s + n) * 4 + p0]);
-    bx1[s] = __builtin_bit_cast(half8, xs[(32 * s + n) * 4 + p1]);
-  }
   const f32x16 z = {};
   f32x16 p[NSUB][2];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    p[s][0] = mfma(cur.t0a, bx0[s], z);
-    p[s][1] = mfma(cur.t1a, bx0[s], z);
-  }
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    p[s][0] = mfma(cur.t0b, bx1[s], p[s][0]);
-    p[s][1] = mfma(cur.t1b, bx1[s], p[s][1]);
-  }
+  p[0][0] = mfma(cur.t0a, bo.k0[0], z);
+  p[0][1] = mfma(cur.t1a, bo.k0[0], z);
+  p[0][0] = mfma(cur.t0b, bo.k1[0], p[0][0]);
+  p[0][1] = mfma(cur.t1b, bo.k1[0], p[0][1]);
+  COLI_FENCE();
+  BOps<NSUB> bn = bo;
+  if (J + 1 < kStage) read_bops<NSUB>(L, slot, J + 1, p0, p1, lane, bn);
   constexpr int JN = (J + 1) % kPfW;   // ring slot of block b + 1
-  cur = tile_operands(wq[JN], uc);
-  const int bn = b + 1 + kPfW < NB ? b + 1 + kPfW : NB - 1;
-  wq[JN] = __builtin_amdgcn_raw_buffer_load_b128(wr.rs, wr.off + 1024u * (uint32_t)bn, 0, 0);
+  const u32x4 w = wq[JN];
+  const auto sa = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+  TileOps nx;
+  nx.t0a = nibbles_to_f16(sa[0], uc);
+  nx.t1a = nibbles_to_f16(sa[1], uc);
+  COLI_FENCE();
+  rescale(acc.t0[0], p[0][0], dv[0][J]);
+  COLI_FENCE();
+  if (NSUB > 1) {
+    p[NSUB - 1][0] = mfma(cur.t0a, bo.k0[NSUB - 1], z);
+    p[NSUB - 1][1] = mfma(cur.t1a, bo.k0[NSUB - 1], z);
+    p[NSUB - 1][0] = mfma(cur.t0b, bo.k1[NSUB - 1], p[NSUB - 1][0]);
+    p[NSUB - 1][1] = mfma(cur.t1b, bo.k1[NSUB - 1], p[NSUB - 1][1]);
+    COLI_FENCE();
+  }
+  rescale(acc.t1[0], p[0][1], dv[0][J]);
+  COLI_FENCE();
+  const auto sb = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+  nx.t0b = nibbles_to_f16(sb[0], uc);
+  nx.t1b = nibbles_to_f16(sb[1], uc);
+  const int bnx = b + 1 + kPfW < NB ? b + 1 + kPfW : NB - 1;
+  wq[JN] = __builtin_amdgcn_raw_buffer_load_b128(wr.rs, wr.off + 1024u * (uint32_t)bnx, 0, 0);
+  COLI_FENCE();
+  if (NSUB > 1) {
+    rescale(acc.t0[NSUB - 1], p[NSUB - 1][0], dv[NSUB - 1][J]);
+    rescale(acc.t1[NSUB - 1], p[NSUB - 1][1], dv[NSUB - 1][J]);
+  }
+  if (TRACE) {
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    rescale(acc.t0[s], p[s][0], dv[s][J]);
-    rescale(acc.t1[s], p[s][1], dv[s][J]);
-    if (TRACE) {
+    for (int s = 0; s < NSUB; ++s) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rr = tile_row(i, lane);
@@ -295,38 +336,65 @@ __device__ __forceinline__ void block_step(const StageLds& L, int slot, int b0, 
       }
     }
   }
+  cur = nx;
+  bo = bn;
 }
 
-template <int NSUB, bool TRACE, int J>
+template <int NSUB, bool TRACE, bool GUARD, int J>
 __device__ __forceinline__ void stage_steps(const StageLds& L, int slot, int b0, int NB,
-                                            bool guard, const WeightRows& wr, u32x4 (&wq)[kPfW],
-                                            TileOps& cur, const UnpackConsts& uc,
+                                            const WeightRows& wr, u32x4 (&wq)[kPfW],
+                                            TileOps& cur, BOps<NSUB>& bo, const UnpackConsts& uc,
                                             const float (&dv)[NSUB][kStage], int p0, int p1,
                                             Acc<NSUB>& acc, int32_t* const (&tr0)[NSUB],
                                             int32_t* const (&tr1)[NSUB], int lane) {
   if constexpr (J < kStage) {
-    if (!guard || b0 + J < NB)
-      block_step<NSUB, TRACE, J>(L, slot, b0, NB, wr, wq, cur, uc, dv, p0, p1, acc, tr0, tr1,
+    if (!GUARD || b0 + J < NB)
+      block_step<NSUB, TRACE, J>(L, slot, b0, NB, wr, wq, cur, bo, uc, dv, p0, p1, acc, tr0, tr1,
                                  lane);
-    stage_steps<NSUB, TRACE, J + 1>(L, slot, b0, NB, guard, wr, wq, cur, uc, dv, p0, p1, acc,
-                                    tr0, tr1, lane);
+    stage_steps<NSUB, TRACE, GUARD, J + 1>(L, slot, b0, NB, wr, wq, cur, bo, uc, dv, p0, p1, acc,
+                                           tr0, tr1, lane);
   }
+}
+
+template <int NSUB, bool TRACE, bool GUARD>
+__device__ __forceinline__ void stage_compute(const StageLds& L, int slot, int b0, int NB,
+                                              const WeightRows& wr, u32x4 (&wq)[kPfW],
+                                              TileOps& cur, const UnpackConsts& uc, int p0, int p1,
+                                              Acc<NSUB>& acc, int32_t* const (&tr0)[NSUB],
+                                              int32_t* const (&tr1)[NSUB], int lane) {
+  const int n = lane & 31;
+  float dv[NSUB][kStage];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(&L.d[slot][32 * s + n][0]);
+    dv[s][0] = v.x;
+    dv[s][1] = v.y;
+    dv[s][2] = v.z;
+    dv[s][3] = v.w;
+  }
+  BOps<NSUB> bo;
+  read_bops<NSUB>(L, slot, 0, p0, p1, lane, bo);
+  stage_steps<NSUB, TRACE, GUARD, 0>(L, slot, b0, NB, wr, wq, cur, bo, uc, dv, p0, p1, acc, tr0,
+                                     tr1, lane);
 }
 
 // All NB blocks of one row group against NSUB subtiles of the chunk's tokens.
 // Every wavefront of the workgroup takes part in the staging and barriers;
-// `compute` is false for a wavefront whose row group is past the matrix.
-template <int NSUB, bool TRACE>
-__device__ __forceinline__ void stream_group(StageLds& L, const WeightRows& wr,
-                                             const TokenRows& tk, bool compute, Acc<NSUB>& acc,
-                                             int32_t* const (&tr0)[NSUB],
-                                             int32_t* const (&tr1)[NSUB], int wave, int lane) {
+// COMPUTE is false for a wavefront whose row group is past the matrix.  The
+// loop over full stages issues the same loads on every path (indices past the
+// end are clamped), so the compiler's memory-counter waits stay exact and the
+// weight and stage prefetches stay in flight; a partial last stage runs after it.
+template <int NSUB, bool TRACE, bool COMPUTE>
+__device__ __forceinline__ void stream_loop(StageLds& L, const WeightRows& wr,
+                                            const TokenRows& tk, Acc<NSUB>& acc,
+                                            int32_t* const (&tr0)[NSUB],
+                                            int32_t* const (&tr1)[NSUB], int wave, int lane) {
   const int NB = tk.NB;
-  const int NS = (NB + kStage - 1) / kStage;
+  const int NS = (NB + kStage - 1) / kStage, NSF = NB / kStage;
   const UnpackConsts uc = unpack_consts();
   u32x4 wq[kPfW];
   TileOps cur = {};
-  if (compute) {
+  if (COMPUTE) {
 #pragma unroll
     for (int j = 0; j < kPfW; ++j) {
       const int b = j < NB ? j : NB - 1;
@@ -336,8 +404,8 @@ __device__ __forceinline__ void stream_group(StageLds& L, const WeightRows& wr,
   StageRegs R;
   stage_load(tk, 0, lane, R);
   stage_store(L, 0, wave, lane, R);
-  if (NS > 1) stage_load(tk, kStage, lane, R);
-  if (compute) {
+  stage_load(tk, kStage, lane, R);
+  if (COMPUTE) {
     cur = tile_operands(wq[0], uc);
     const int b = kPfW < NB ? kPfW : NB - 1;
     wq[0] = __builtin_amdgcn_raw_buffer_load_b128(wr.rs, wr.off + 1024u * (uint32_t)b, 0, 0);
@@ -345,25 +413,28 @@ __device__ __forceinline__ void stream_group(StageLds& L, const WeightRows& wr,
   __syncthreads();
   const int n = lane & 31, h = lane >> 5, sw = (n >> 2) & 3;
   const int p0 = (2 * h) ^ sw, p1 = (2 * h + 1) ^ sw;
-  for (int st = 0; st < NS; ++st) {
-    const int slot = st & 1, b0 = st * kStage;
-    if (compute) {
-      float dv[NSUB][kStage];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const float4 v = *reinterpret_cast<const float4*>(&L.d[slot][32 * s + n][0]);
-        dv[s][0] = v.x;
-        dv[s][1] = v.y;
-        dv[s][2] = v.z;
-        dv[s][3] = v.w;
-      }
-      stage_steps<NSUB, TRACE, 0>(L, slot, b0, NB, b0 + kStage > NB, wr, wq, cur, uc, dv, p0,
-                                  p1, acc, tr0, tr1, lane);
-    }
-    if (st + 1 < NS) stage_store(L, slot ^ 1, wave, lane, R);
-    if (st + 2 < NS) stage_load(tk, (st + 2) * kStage, lane, R);
+  int st = 0;
+  for (; st < NSF; ++st) {
+    const int slot = st & 1;
+    if (COMPUTE)
+      stage_compute<NSUB, TRACE, false>(L, slot, st * kStage, NB, wr, wq, cur, uc, p0, p1, acc,
+                                        tr0, tr1, lane);
+    stage_store(L, slot ^ 1, wave, lane, R);
+    stage_load(tk, (st + 2) * kStage, lane, R);
     __syncthreads();
   }
+  if (COMPUTE && st < NS)
+    stage_compute<NSUB, TRACE, true>(L, st & 1, st * kStage, NB, wr, wq, cur, uc, p0, p1, acc,
+                                     tr0, tr1, lane);
+}
+
+template <int NSUB, bool TRACE>
+__device__ __forceinline__ void stream_group(StageLds& L, const WeightRows& wr,
+                                             const TokenRows& tk, bool compute, Acc<NSUB>& acc,
+                                             int32_t* const (&tr0)[NSUB],
+                                             int32_t* const (&tr1)[NSUB], int wave, int lane) {
+  if (compute) stream_loop<NSUB, TRACE, true>(L, wr, tk, acc, tr0, tr1, wave, lane);
+  else stream_loop<NSUB, TRACE, false>(L, wr, tk, acc, tr0, tr1, wave, lane);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
