@@ -190,6 +190,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch steps directly, no HIP graph")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="timed 2048-token passes of the prefill leg (0: skip it)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 8 device-to-device copies of this many bytes (the known-size "
+                         "kernel that scales the HBM byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -198,6 +201,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.rand(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "copies": 8}), flush=True)
+        return
     import synth
     import int4_routed_expert_sigmoid_amd as coli
 
