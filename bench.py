@@ -29,6 +29,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# HBM bytes per launch of the decode gate/up kernel, from rocprofv3 FETCH_SIZE (x2.0) and
+# WRITE_SIZE (x1.0) runs, each scale taken from a copy of known size
+# (profiles/decode_gate_up_hbm_traffic.md); valid for the kernel as measured there.
+GATE_UP_TRAFFIC_BYTES = 113_705_984
 INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of MI355X
 METRIC = "MoE-layer decode tok/s + achieved HBM GB/s (int4 experts); prefill int8 TOPS"
 
@@ -333,7 +337,8 @@ def main():
         "down_gbps": round(active * dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "gate_up_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": GATE_UP_TRAFFIC_BYTES,
+                     "algorithmic_bytes": gu_alg},
         "wall_s": round(wall, 3),
         "setup_s": round(setup_s, 1),
     }
