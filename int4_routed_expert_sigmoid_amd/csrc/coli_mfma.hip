@@ -676,11 +676,18 @@ struct FrontArgs {
 __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
   if (blockIdx.x == 0) {
     __shared__ int pre[512 + 1];
+    __shared__ int act[512];
     __shared__ int wsum[4];
     const int nact = *a.n_active;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int c0 = 2 * t < nact ? (a.counts[a.active[2 * t]] + kChunk - 1) / kChunk : 0;
-    const int c1 = 2 * t + 1 < nact ? (a.counts[a.active[2 * t + 1]] + kChunk - 1) / kChunk : 0;
+    // active experts and their chunk counts, two per thread
+    const int e0 = 2 * t < nact ? a.active[2 * t] : 0;
+    const int e1 = 2 * t + 1 < nact ? a.active[2 * t + 1] : 0;
+    const int n0 = 2 * t < nact ? a.counts[e0] : 0;
+    const int n1 = 2 * t + 1 < nact ? a.counts[e1] : 0;
+    act[2 * t] = e0;
+    act[2 * t + 1] = e1;
+    const int c0 = (n0 + kChunk - 1) / kChunk, c1 = (n1 + kChunk - 1) / kChunk;
     int v = c0 + c1;   // inclusive scan of the pair sums across the workgroup
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -702,7 +709,7 @@ __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
       a.totals[1] = chunks * a.qd;
     }
     for (int s = wave; s < nact; s += 4) {
-      const int e = a.active[s];
+      const int e = act[s];
       const int c = pre[s + 1] - pre[s];
       for (int i = lane; i < c * a.qg; i += kWave)
         a.gu_items[pre[s] * a.qg + i] = make_int2(e | ((i / c) << 16), i % c);

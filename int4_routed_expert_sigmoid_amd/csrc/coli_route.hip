@@ -10,9 +10,9 @@
 //
 // Dispatch is the batch-union grouping of the alphamatch.ai page
 // ("기술적 우수성"): per expert, the (token, slot) pairs that chose it, in
-// ascending token order.  One wavefront owns one expert and sweeps the index
-// array 64 entries at a time with a ballot, so list positions come from
-// prefix popcounts: stable and deterministic without atomics.
+// ascending token order.  One workgroup owns one expert and sweeps the index
+// array with ballots, so list positions come from prefix popcounts: stable and
+// deterministic without atomics.
 #include "coli_internal.h"
 
 // Wavefront max of a 64-bit value (ROCm device library, DPP-based).
@@ -89,42 +89,67 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
   }
 }
 
-// One wavefront builds expert e's list of pairs from the n = T*k routing
-// entries (entry i is token i/k, slot i%k), in entry order = token order.
-// Returns the count (capped at T, the list capacity).
-template <class Entry>
-__device__ __forceinline__ int expert_list(int e, int64_t T, int k, int S, Entry entry,
-                                           int32_t* __restrict__ le, int lane) {
-  const int64_t n = T * k;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int64_t base = 0;
-  for (int64_t i0 = 0; i0 < n; i0 += kWave) {
-    const int64_t i = i0 + lane;
-    const bool hit = i < n && entry(i) == e;
-    const uint64_t m = __ballot(hit);
-    const int64_t pos = base + __popcll(m & lt);
-    if (hit && pos < T) le[pos] = (int32_t)((i / k) * (k + S) + i % k);
-    base += __popcll(m);
-  }
-  return (int)(base < T ? base : T);
-}
+// One workgroup per expert e in [0, E+S).  Its four wavefronts split the
+// routing entries into four contiguous ranges; each counts its matches
+// (ballot popcounts over batches of 8 x 64 entries whose loads are in flight
+// together), a workgroup prefix of the four counts gives each wavefront its
+// first list position, and a second pass writes the positions.  The list is
+// in entry order = token order, as with one sweep.
+constexpr int kListBatch = 8;
 
-// One wavefront per expert e in [0, E+S).
 __global__ void __launch_bounds__(256) dispatch_lists_kernel(const int32_t* __restrict__ idx,
                                                              int64_t T, int k, int E, int S,
                                                              int32_t* __restrict__ counts,
                                                              int32_t* __restrict__ lists) {
-  const int lane = threadIdx.x % kWave;
-  const int e = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (e >= E + S) return;
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   int32_t* le = lists + (int64_t)e * T;
   if (e == E) {   // the shared expert serves every token, in slot k
-    for (int64_t t = lane; t < T; t += kWave) le[t] = (int32_t)(t * (k + S) + k);
-    if (lane == 0) counts[e] = (int32_t)T;
+    for (int64_t t = threadIdx.x; t < T; t += blockDim.x) le[t] = (int32_t)(t * (k + S) + k);
+    if (threadIdx.x == 0) counts[e] = (int32_t)T;
     return;
   }
-  const int cnt = expert_list(e, T, k, S, [&](int64_t i) { return idx[i]; }, le, lane);
-  if (lane == 0) counts[e] = cnt;
+  __shared__ int wcnt[4];
+  const int64_t n = T * k;
+  const int64_t span = (n + 4 * kWave - 1) / (4 * kWave) * kWave;   // entries per wavefront
+  const int64_t lo = wave * span, hi = lo + span < n ? lo + span : n;
+  int cnt = 0;
+  for (int64_t i0 = lo; i0 < hi; i0 += kWave * kListBatch) {
+    int v[kListBatch];
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int64_t i = i0 + (int64_t)u * kWave + lane;
+      v[u] = i < hi ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) cnt += __popcll(__ballot(v[u] == e));
+  }
+  if (lane == 0) wcnt[wave] = cnt;
+  __syncthreads();
+  int64_t base = 0, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    base += w < wave ? wcnt[w] : 0;
+    total += wcnt[w];
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t i0 = lo; i0 < hi; i0 += kWave * kListBatch) {
+    int v[kListBatch];
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int64_t i = i0 + (int64_t)u * kWave + lane;
+      v[u] = i < hi ? idx[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int64_t i = i0 + (int64_t)u * kWave + lane;
+      const bool hit = v[u] == e;
+      const uint64_t m = __ballot(hit);
+      const int64_t pos = base + __popcll(m & lt);
+      if (hit && pos < T) le[pos] = (int32_t)((i / k) * (k + S) + i % k);
+      base += __popcll(m);
+    }
+  }
+  if (threadIdx.x == 0) counts[e] = (int32_t)(total < T ? total : T);
 }
 
 // Workgroup 0: compact the active-expert list and check the indices.
@@ -139,12 +164,22 @@ __global__ void __launch_bounds__(256) dispatch_finish_kernel(
     __shared__ int bad_any;
     if (threadIdx.x == 0) bad_any = 0;
     __syncthreads();
+    // the index check, over chunks of whole tokens staged in LDS: an entry is
+    // bad if out of range or equal to an earlier entry of its token
+    __shared__ int ent[4096];
     int bad = 0;
-    for (int64_t i = threadIdx.x; i < T * k; i += blockDim.x) {
-      const int e = idx[i];
-      if (e < 0 || e >= E) { bad = 1; continue; }
-      const int64_t t0 = (i / k) * k;
-      for (int64_t j = t0; j < i; ++j) if (idx[j] == e) bad = 1;
+    const int64_t n = T * k, chunk = (4096 / k) * k;
+    for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+      const int64_t m = n - c0 < chunk ? n - c0 : chunk;
+#pragma unroll 16
+      for (int64_t i = threadIdx.x; i < m; i += blockDim.x) ent[i] = idx[c0 + i];
+      __syncthreads();
+      for (int64_t i = threadIdx.x; i < m; i += blockDim.x) {
+        const int e = ent[i];
+        if (e < 0 || e >= E) { bad = 1; continue; }
+        for (int64_t j = (i / k) * k; j < i; ++j) bad |= ent[j] == e;
+      }
+      __syncthreads();
     }
     if (bad) atomicOr(&bad_any, 1);
     if (threadIdx.x < kWave) {
@@ -310,8 +345,8 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, int32_t* counts,
                            int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
                            const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_lists_kernel, dim3((unsigned)((E + S + 3) / 4)), dim3(256), 0, s,
-                     idx, T, k, E, S, counts, lists);
+  hipLaunchKernelGGL(dispatch_lists_kernel, dim3((unsigned)(E + S)), dim3(256), 0, s, idx, T, k,
+                     E, S, counts, lists);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   int64_t blocks = 1;
