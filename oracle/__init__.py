@@ -42,6 +42,7 @@ _SIG = {
     "orc_moe_layer": ([_P, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P,
                        ctypes.c_int, _P], ctypes.c_int),
     "orc_rmsnorm": ([_P, _I64, _I64, _F, _P, _P], None),
+    "orc_router_logits": ([_P, _P, _I64, _I64, _I32, _P], None),
     "orc_dispatch": ([_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P], ctypes.c_int),
 }
 
@@ -266,6 +267,16 @@ class Oracle:
         if rc != 0:
             raise ValueError("orc_moe_layer: a selected expert is missing or an index is invalid")
         return out, absterm
+
+    def router_logits(self, x, wr):
+        """logits [T][E] = x [T][D] . wr [E][D]^T, fp64 sum in ascending d, rounded once."""
+        x = _c(x, np.float32)
+        wr = _c(wr, np.float32)
+        T, D = x.shape
+        E = wr.shape[0]
+        out = np.empty((T, E), dtype=np.float32)
+        self.L.orc_router_logits(_ptr(x), _ptr(wr), T, D, E, _ptr(out))
+        return out
 
     def rmsnorm(self, h, eps):
         h = _c(h, np.float32)

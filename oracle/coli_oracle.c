@@ -326,6 +326,23 @@ void orc_rmsnorm(const float* h, int64_t T, int64_t D, float eps, float* out, fl
 }
 
 /* ------------------------------------------------------------------------
+ * Router projection: the F32 router weight matrix applied to the hidden
+ * state.  A product of two floats has at most 48 significant bits, so it is
+ * exact in fp64; the sum runs in fp64 in ascending d and is rounded to fp32
+ * once.
+ */
+void orc_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int32_t E,
+                       float* logits) {
+#pragma omp parallel for schedule(static) if (T * (int64_t)E * D > (1 << 22))
+  for (int64_t te = 0; te < T * (int64_t)E; ++te) {
+    const int64_t t = te / E, e = te % E;
+    double s = 0.0;
+    for (int64_t d = 0; d < D; ++d) s += (double)wr[e * D + d] * (double)x[t * D + d];
+    logits[te] = (float)s;
+  }
+}
+
+/* ------------------------------------------------------------------------
  * Batch-union dispatch: the expert-major view of the routing so that each
  * selected expert's weights are read once per pass.
  */

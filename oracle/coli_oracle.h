@@ -78,6 +78,13 @@ int orc_moe_layer(const void* const* experts, int32_t E, int32_t S, int64_t D, i
 /* RMSNorm with unit gain: ss in fp64, r = (float)(1/sqrt(ss/D + eps)), out = h * r. */
 void orc_rmsnorm(const float* h, int64_t T, int64_t D, float eps, float* out, float* r_out);
 
+/* Router projection (jeff.news, attention-and-kernels section: the router is
+ * part of the DeepSeek-V3-style MoE; aitrends.kr "알아두면 좋은 것": router
+ * weights stay F32): logits[t][e] = sum_d wr[e][d] * x[t][d], each product
+ * exact in fp64, summed in fp64 in ascending d, rounded once to fp32. */
+void orc_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int32_t E,
+                       float* logits);
+
 /* Batch-union dispatch.  For every expert e in [0, E+S): counts[e] and the
  * list lists[e*T .. e*T+counts[e]) of pair ids p = t*(k+S) + slot in
  * ascending token order (the shared expert E takes slot k of every token).

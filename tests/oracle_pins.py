@@ -389,6 +389,28 @@ def pin_rmsnorm(orc):
     assert np.allclose(np.sqrt((out.astype(np.float64) ** 2).mean(1)), 1.0, atol=1e-5)
 
 
+def pin_router_logits(orc):
+    """Router projection: closed form, exact small-integer dots, and the
+    correctly rounded exact sum (math.fsum) within half an fp32 ulp plus the
+    fp64 rounding of the ascending sum."""
+    # constant inputs: 6144 * 0.5 * 0.25 = 768 exactly
+    lg = orc.router_logits(np.full((2, 6144), 0.25, np.float32), np.full((3, 6144), 0.5, np.float32))
+    assert lg.shape == (2, 3) and np.all(lg == 768.0)
+    # small integers: every partial sum is an exact integer
+    rng = np.random.default_rng(21)
+    xi = rng.integers(-3, 4, size=(3, 1000))
+    wi = rng.integers(-3, 4, size=(5, 1000))
+    lg = orc.router_logits(xi.astype(np.float32), wi.astype(np.float32))
+    assert np.array_equal(lg, (xi @ wi.T).astype(np.float32)), "integer router logits"
+    # random fp32 inputs at the page shape (T != E, so a transposed operand fails)
+    x = rng.standard_normal((3, 6144)).astype(np.float32)
+    w = (rng.standard_normal((7, 6144)) * 0.02).astype(np.float32)
+    lg = orc.router_logits(x, w)
+    ref = np.array([[math.fsum((x[t].astype(np.float64) * w[e].astype(np.float64)).tolist())
+                     for e in range(7)] for t in range(3)])
+    assert np.all(ulp_dist(lg, ref) <= 0.5 + 1e-3), "router logits vs the exact sum"
+
+
 def pin_dispatch(orc):
     rng = np.random.default_rng(9)
     for T, E, k, S in ((4, 16, 2, 1), (37, 256, 8, 1), (5, 16, 3, 0)):
@@ -411,4 +433,4 @@ def pin_dispatch(orc):
 
 ALL_PINS = [pin_nibble_codec, pin_rint_ties, pin_quant_closed_forms, pin_partials_bruteforce,
             pin_dot_fp64, pin_exp, pin_route, pin_expert_fp64, pin_moe_invariants, pin_rmsnorm,
-            pin_dispatch]
+            pin_dispatch, pin_router_logits]

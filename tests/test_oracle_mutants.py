@@ -67,6 +67,12 @@ MUTANTS = {
                                "lists[(int64_t)e * T + counts[e]++] = (int32_t)(t * (k + S));"),
     "dispatch accepts repeats": ("if (idx[t * k + i] == idx[t * k + j]) return -1;",
                                  "if (0) return -1;"),
+    "router logits summed in fp32":
+        ("    double s = 0.0;\n    for (int64_t d = 0; d < D; ++d) s += (double)wr[e * D + d] * (double)x[t * D + d];",
+         "    float s = 0.0f;\n    for (int64_t d = 0; d < D; ++d) s += wr[e * D + d] * x[t * D + d];"),
+    "router weights transposed":
+        ("s += (double)wr[e * D + d] * (double)x[t * D + d];",
+         "s += (double)wr[d * E + e] * (double)x[t * D + d];"),
 }
 
 
