@@ -183,6 +183,32 @@ def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
     }
 
 
+def router_leg(coli, synth, torch, steps=50):
+    """The router projection (F32 weights [256][6144], fp64 sum) for 1 and 2048 tokens."""
+    w = synth.WORKLOADS[1]
+    wr = torch.from_numpy(synth.router_weights(w)).cuda()
+    res = {}
+    for T in (1, 2048):
+        x = torch.from_numpy(synth.activations(w, T, 900)).cuda()
+        out = torch.empty((T, w.E), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            coli.coli_router_logits(x, wr, out)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            coli.coli_router_logits(x, wr, out)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / steps * 1e3
+        nbytes = 4 * (w.E * w.D + T * w.D + T * w.E)
+        res[f"t{T}_us"] = round(us, 2)
+        res[f"t{T}_gbps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        res[f"t{T}_fp64_tflops"] = round(2.0 * T * w.E * w.D / (us * 1e-6) / 1e12, 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +372,7 @@ def main():
         out["prefill"] = [prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3),
                           prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3,
                                       bias_free=True)]
+    out["router_logits"] = router_leg(coli, synth, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out), flush=True)

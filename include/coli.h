@@ -147,6 +147,19 @@ int coli_rmsnorm_q8(const float* h, int64_t T, int64_t D, float eps, int8_t* q, 
 int coli_route_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
                     float routed_scale, int32_t* idx, float* w, void* stream);
 
+/* Router projection: the logits of coli_route_topk from the hidden state and
+ * the F32 router weights (the router is the DeepSeek-V3-style gate of
+ * jeff.news, attention-and-kernels section; its weights stay F32, aitrends.kr
+ * "알아두면 좋은 것").  logits[t][e] = sum_d wr[e][d] * x[t][d]: each product
+ * exact in fp64, summed in fp64, rounded to fp32 once (the summation order
+ * inside fp64 is the kernel's; it changes the fp32 result only when the fp64
+ * sum lies within ~2^-29 relative of a rounding boundary).
+ * x [T][D] f32, wr [E][D] f32 (caller-owned device buffers, 16-byte aligned)
+ * -> logits [T][E] f32.  D % 64 == 0, 1 <= E <= 256.  Errors: COLI_E_SHAPE,
+ * COLI_E_INVAL (null or misaligned pointer), COLI_E_DEVICE, COLI_E_HIP. */
+int coli_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int32_t E,
+                       float* logits, void* stream);
+
 /* ------------------------------------------------------------------------
  * Batch-union dispatch (alphamatch.ai page, "기술적 우수성": prefill groups
  * tokens by expert; discuss.pytorch.kr: the batched verify pass).  From

@@ -28,7 +28,8 @@ COLI_MAX_TOPK = 64
 
 EXPORTED = [
     "coli_table_bytes", "coli_table_set_expert", "coli_quant_act_q8", "coli_quant_weight_q4",
-    "coli_rmsnorm_q8", "coli_route_topk", "coli_dispatch", "coli_moe_workspace_bytes",
+    "coli_rmsnorm_q8", "coli_route_topk", "coli_router_logits", "coli_dispatch",
+    "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
     "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex",
     "coli_moe_status", "coli_status_string", "coli_last_hip_error",
@@ -85,6 +86,7 @@ def lib():
             "coli_rmsnorm_q8": ([_P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
             "coli_route_topk": ([_P, _P, _I64, _I32, _I32, ctypes.c_float, _P, _P, _P],
                                 ctypes.c_int),
+            "coli_router_logits": ([_P, _P, _I64, _I64, _I32, _P, _P], ctypes.c_int),
             "coli_dispatch": ([_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P], ctypes.c_int),
             "coli_moe_workspace_bytes": ([_P, _I64, _I32], sz),
             "coli_moe_forward": ([_P, _P, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P, sz, _P],
@@ -195,6 +197,17 @@ def coli_rmsnorm_q8(h, eps, q, d, r_out=None, stream=None):
 
 
 # --------------------------------------------------------------------------- routing
+def coli_router_logits(x, wr, logits, stream=None):
+    """logits [T][E] = x [T][D] . wr [E][D]^T (F32 router weights, fp64 sum)."""
+    import torch
+    _dtype(x, torch.float32, "x"); _dtype(wr, torch.float32, "wr")
+    _dtype(logits, torch.float32, "logits")
+    T, D = x.shape
+    E = wr.shape[0]
+    _check("coli_router_logits", lib().coli_router_logits(_ptr(x), _ptr(wr), T, D, E, _ptr(logits),
+                                                          _stream(stream)))
+
+
 def coli_route_topk(logits, bias, k, idx, w, routed_scale=1.0, stream=None):
     import torch
     _dtype(logits, torch.float32, "logits"); _dtype(bias, torch.float32, "bias")

@@ -202,6 +202,20 @@ int coli_route_topk(const float* logits, const float* bias, int64_t T, int32_t E
   return e == hipSuccess ? COLI_OK : hip_fail(e);
 }
 
+int coli_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int32_t E,
+                       float* logits, void* stream) {
+  if (E < 1 || E > COLI_MAX_EXPERTS) return COLI_E_SHAPE;
+  if (D < 64 || D % 64 != 0 || D > COLI_MAX_DIM) return COLI_E_SHAPE;
+  if (T < 0 || T > 0x7FFFFFFF / 4) return COLI_E_SHAPE;
+  if (T == 0) return COLI_OK;
+  if (!x || !wr || !logits) return COLI_E_INVAL;
+  if (!al16(x) || !al16(wr) || !al4(logits)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_router_logits(x, wr, T, D, E, logits, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
 int coli_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S, int32_t* counts,
                   int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
                   void* stream) {

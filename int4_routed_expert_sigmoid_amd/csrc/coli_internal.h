@@ -120,6 +120,9 @@ hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const
                                    const uint8_t* down_q, const float* down_s, hipStream_t s);
 hipError_t launch_rmsnorm_q8(const float* h, int64_t T, int64_t D, float eps, int8_t* q, float* d,
                              float* r_out, hipStream_t s);
+// logits[t][e] = sum_d wr[e][d] x[t][d], fp64 sum rounded once (D % 64 == 0).
+hipError_t launch_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int E,
+                                float* out, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, int E, int k,
                              float routed_scale, int32_t* idx, float* w, hipStream_t s);
 // Dispatch lists + compaction + index check; xq != nullptr also fills xsum8.

@@ -361,3 +361,145 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, i
 }
 
 }  // namespace coli
+
+// ---------------------------------------------------------------------------
+// Router projection: logits[t][e] = sum_d wr[e][d] * x[t][d] with F32 router
+// weights (jeff.news attention-and-kernels section: DeepSeek-V3-style router;
+// aitrends.kr "알아두면 좋은 것": the router stays F32).  Every product of two
+// floats is exact in fp64; the sum runs in fp64 and is rounded to fp32 once.
+// The summation order differs from a sequential one only inside fp64, which
+// moves the fp32 result only when the fp64 sum lies within about 2^-29 of a
+// rounding boundary.
+namespace coli {
+namespace {
+
+// Few tokens: one wavefront per expert row streams the row once (float4
+// loads, eight in flight per lane) and reuses it for each token; four
+// independent fp64 chains per lane, then a fixed butterfly over the lanes.
+__global__ void __launch_bounds__(256) router_rows_kernel(const float* __restrict__ x,
+                                                          const float* __restrict__ wr,
+                                                          int64_t T, int64_t D, int E,
+                                                          float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)e * D);
+  const int64_t n4 = D / 4;   // a multiple of 16
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * D);
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int64_t i0 = lane; i0 < n4; i0 += 64 * 8) {
+      float4 a[8], b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + 64 * u;
+        a[u] = i < n4 ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        b[u] = i < n4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s[0] = __builtin_fma((double)a[u].x, (double)b[u].x, s[0]);
+        s[1] = __builtin_fma((double)a[u].y, (double)b[u].y, s[1]);
+        s[2] = __builtin_fma((double)a[u].z, (double)b[u].z, s[2]);
+        s[3] = __builtin_fma((double)a[u].w, (double)b[u].w, s[3]);
+      }
+    }
+    double v = (s[0] + s[1]) + (s[2] + s[3]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) out[(size_t)t * E + e] = (float)v;
+  }
+}
+
+// Many tokens: a workgroup owns 64 experts x 32 tokens; a thread owns 4
+// experts x 2 tokens (8 fp64 accumulators).  64-column slices of the weight
+// rows and of the tokens are staged in LDS (rows padded to 65 floats); per
+// column a thread reads 4 weights and 2 token values for 8 fmas.
+constexpr int kRtE = 64, kRtT = 32, kRtK = 64;
+
+__global__ void __launch_bounds__(256) router_tiles_kernel(const float* __restrict__ x,
+                                                           const float* __restrict__ wr,
+                                                           int64_t T, int64_t D, int E,
+                                                           float* __restrict__ out) {
+  __shared__ float ws[kRtE][kRtK + 1];
+  __shared__ float xs[kRtT][kRtK + 1];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int e0 = blockIdx.x * kRtE;
+  const int64_t t0 = (int64_t)blockIdx.y * kRtT;
+  double acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.0;
+  // the next 64-column slice is loaded into registers (float4, 4 of the
+  // weights and 2 of the tokens per thread) while the current one is used
+  float4 rw[4], rx[2];
+  auto load_slice = [&](int64_t k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + 256 * j, r = q >> 4, c4 = q & 15;
+      rw[j] = e0 + r < E ? *reinterpret_cast<const float4*>(wr + (size_t)(e0 + r) * D + k0 + 4 * c4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = tid + 256 * j, r = q >> 4, c4 = q & 15;
+      rx[j] = t0 + r < T ? *reinterpret_cast<const float4*>(x + (size_t)(t0 + r) * D + k0 + 4 * c4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_slice(0);
+  for (int64_t k0 = 0; k0 < D; k0 += kRtK) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + 256 * j, r = q >> 4, c = 4 * (q & 15);
+      ws[r][c] = rw[j].x; ws[r][c + 1] = rw[j].y; ws[r][c + 2] = rw[j].z; ws[r][c + 3] = rw[j].w;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = tid + 256 * j, r = q >> 4, c = 4 * (q & 15);
+      xs[r][c] = rx[j].x; xs[r][c + 1] = rx[j].y; xs[r][c + 2] = rx[j].z; xs[r][c + 3] = rx[j].w;
+    }
+    __syncthreads();
+    if (k0 + kRtK < D) load_slice(k0 + kRtK);
+#pragma unroll 4
+    for (int c = 0; c < kRtK; ++c) {
+      double wv[4], xv[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = (double)ws[4 * tx + i][c];
+      xv[0] = (double)xs[2 * ty][c];
+      xv[1] = (double)xs[2 * ty + 1][c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][0] = __builtin_fma(wv[i], xv[0], acc[i][0]);
+        acc[i][1] = __builtin_fma(wv[i], xv[1], acc[i][1]);
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 4 * tx + i;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t t = t0 + 2 * ty + j;
+      if (e < E && t < T) out[(size_t)t * E + e] = (float)acc[i][j];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int E,
+                                float* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T < 16) {
+    hipLaunchKernelGGL(router_rows_kernel, dim3((unsigned)((E + 3) / 4), (unsigned)T), dim3(256),
+                       0, s, x, wr, T, D, E, out);
+  } else {
+    hipLaunchKernelGGL(router_tiles_kernel,
+                       dim3((unsigned)((E + kRtE - 1) / kRtE), (unsigned)((T + kRtT - 1) / kRtT)),
+                       dim3(256), 0, s, x, wr, T, D, E, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace coli

@@ -39,6 +39,7 @@ KIND_BIAS = 4
 KIND_HIDDEN = 5
 KIND_PERM = 6
 KIND_GUMBEL = 7
+KIND_ROUTER = 8
 
 SEED = 0
 W_SIGMA = 0.02
@@ -217,6 +218,11 @@ def zipf_logits(w: Workload, layer: int, T: int, token0: int = 0) -> np.ndarray:
                 offset=token0 * w.E).reshape(T, w.E)
     g = -np.log(-np.log(u))
     return (-ZIPF_S * np.log(ranks.astype(np.float64))[None, :] + g).astype(np.float32)
+
+
+def router_weights(w: Workload, layer: int = 0) -> np.ndarray:
+    """F32 router projection [E][D] of one layer: N(0, 0.02)."""
+    return normal(stream_id(KIND_ROUTER, w.family, layer, 0), w.E * w.D, W_SIGMA).reshape(w.E, w.D)
 
 
 def hidden0(w: Workload, T: int, token0: int = 0) -> np.ndarray:

@@ -72,6 +72,18 @@ def test_validation_quant():
     assert L.coli_rmsnorm_q8(FAKE, 1, 64, float("nan"), FAKE, FAKE, None, None) == coli.COLI_E_INVAL
 
 
+def test_validation_router_logits():
+    L = coli.lib()
+    f = L.coli_router_logits
+    assert f(FAKE, FAKE, 1, 6144, 257, FAKE, None) == coli.COLI_E_SHAPE     # E > 256
+    assert f(FAKE, FAKE, 1, 6144, 0, FAKE, None) == coli.COLI_E_SHAPE       # E = 0
+    assert f(FAKE, FAKE, 1, 96, 16, FAKE, None) == coli.COLI_E_SHAPE        # D % 64
+    assert f(FAKE, FAKE, -1, 64, 16, FAKE, None) == coli.COLI_E_SHAPE
+    assert f(None, FAKE, 1, 64, 16, FAKE, None) == coli.COLI_E_INVAL
+    assert f(FAKE + 4, FAKE, 1, 64, 16, FAKE, None) == coli.COLI_E_INVAL    # x not 16-byte aligned
+    assert f(None, None, 0, 64, 16, None, None) == coli.COLI_OK             # T = 0
+
+
 def test_validation_route_and_dispatch():
     L = coli.lib()
     r = L.coli_route_topk
