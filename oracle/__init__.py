@@ -32,14 +32,16 @@ _SIG = {
     "orc_q8_quant": ([_P, _I64, _P, _P], None),
     "orc_q4_quant_row": ([_P, _I64, _P, _P], None),
     "orc_q4_quant": ([_P, _I64, _I64, _P, _P], None),
+    "orc_q8w_quant_row": ([_P, _I64, _P, _P], None),
+    "orc_q8w_quant": ([_P, _I64, _I64, _P, _P], None),
     "orc_pack_q4": ([_P, _I64, _P], None),
     "orc_unpack_q4": ([_P, _I64, _P], None),
     "orc_route": ([_P, _P, _I64, _I32, _I32, _F, _P, _P], None),
-    "orc_row_partials": ([_P, _P, _I64, _P], None),
+    "orc_row_partials": ([_P, ctypes.c_int, _P, _I64, _P], None),
     "orc_rescale": ([_P, _P, _I64, _F], _F),
-    "orc_matvec": ([_P, _P, _I64, _I64, _P, _P, _P, _P, _P], None),
-    "orc_expert": ([_P] * 6 + [_I64, _I64] + [_P] * 12, None),
-    "orc_moe_layer": ([_P, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P,
+    "orc_matvec": ([_P, ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P, _P], None),
+    "orc_expert": ([_P] * 6 + [ctypes.c_int, _I64, _I64] + [_P] * 12, None),
+    "orc_moe_layer": ([_P, ctypes.c_int, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P,
                        ctypes.c_int, _P], ctypes.c_int),
     "orc_rmsnorm": ([_P, _I64, _I64, _F, _P, _P], None),
     "orc_router_logits": ([_P, _P, _I64, _I64, _I32, _P], None),
@@ -56,25 +58,39 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-class Expert:
-    """One expert's canonical int4 container (host arrays)."""
+def _container(q, bits):
+    """A weight container as the C side reads it: uint8 nibble pairs (bits 4)
+    or int8 codes (bits 8)."""
+    if bits == 4:
+        assert q.dtype == np.uint8, "the nibble container is uint8"
+        return _c(q, np.uint8)
+    assert bits == 8 and q.dtype == np.int8, "the int8 container is int8"
+    return _c(q, np.int8)
 
-    def __init__(self, gate_q, gate_s, up_q, up_s, down_q, down_s):
-        self.gate_q = _c(gate_q, np.uint8)
+
+class Expert:
+    """One expert's canonical container (host arrays): the int4 nibble
+    container (bits 4, uint8 [rows][k/2]) or the int8 one (bits 8, int8
+    [rows][k]), with one f32 scale per row."""
+
+    def __init__(self, gate_q, gate_s, up_q, up_s, down_q, down_s, bits=4):
+        self.bits = bits
+        self.gate_q = _container(np.asarray(gate_q), bits)
         self.gate_s = _c(gate_s, np.float32)
-        self.up_q = _c(up_q, np.uint8)
+        self.up_q = _container(np.asarray(up_q), bits)
         self.up_s = _c(up_s, np.float32)
-        self.down_q = _c(down_q, np.uint8)
+        self.down_q = _container(np.asarray(down_q), bits)
         self.down_s = _c(down_s, np.float32)
 
     @classmethod
-    def quantize(cls, w_gate, w_up, w_down, orc=None):
-        """Quantise fp32 matrices with the oracle's per-row int4 rule."""
+    def quantize(cls, w_gate, w_up, w_down, orc=None, bits=4):
+        """Quantise fp32 matrices with the oracle's per-row rule for `bits`."""
         orc = orc or get()
-        gq, gs = orc.q4_quant(w_gate)
-        uq, us = orc.q4_quant(w_up)
-        dq, ds = orc.q4_quant(w_down)
-        return cls(gq, gs, uq, us, dq, ds)
+        quant = orc.q4_quant if bits == 4 else orc.q8w_quant
+        gq, gs = quant(w_gate)
+        uq, us = quant(w_up)
+        dq, ds = quant(w_down)
+        return cls(gq, gs, uq, us, dq, ds, bits=bits)
 
     def ptrs(self):
         return [_ptr(self.gate_q), _ptr(self.gate_s), _ptr(self.up_q), _ptr(self.up_s),
@@ -82,7 +98,7 @@ class Expert:
 
     @property
     def D(self):
-        return self.gate_q.shape[1] * 2
+        return self.gate_q.shape[1] * (8 // self.bits)
 
     @property
     def F(self):
@@ -159,6 +175,22 @@ class Oracle:
         self.L.orc_q4_quant(_ptr(w), rows, k, _ptr(packed), _ptr(s))
         return packed, s
 
+    def q8w_quant_row(self, w):
+        w = _c(w, np.float32)
+        q = np.empty(w.shape, dtype=np.int8)
+        s = np.empty(1, dtype=np.float32)
+        self.L.orc_q8w_quant_row(_ptr(w), w.size, _ptr(q), _ptr(s))
+        return q, float(s[0])
+
+    def q8w_quant(self, w):
+        """w [rows][k] fp32 -> (int8 container [rows][k], s fp32 [rows])."""
+        w = _c(w, np.float32)
+        rows, k = w.shape
+        q = np.empty((rows, k), dtype=np.int8)
+        s = np.empty(rows, dtype=np.float32)
+        self.L.orc_q8w_quant(_ptr(w), rows, k, _ptr(q), _ptr(s))
+        return q, s
+
     def pack_q4(self, q):
         q = _c(q, np.int8)
         out = np.empty(q.shape[:-1] + (q.shape[-1] // 2,), dtype=np.uint8)
@@ -195,11 +227,11 @@ class Oracle:
         return counts, lists, int(n_active[0]), active[: int(n_active[0])]
 
     # ---------------------------------------------------------------- dots
-    def row_partials(self, wrow_packed, xq):
-        wrow_packed = _c(wrow_packed, np.uint8)
+    def row_partials(self, wrow, xq, bits=4):
+        wrow = _container(np.asarray(wrow), bits)
         xq = _c(xq, np.int8)
         P = np.empty(xq.size // 32, dtype=np.int32)
-        self.L.orc_row_partials(_ptr(wrow_packed), _ptr(xq), xq.size, _ptr(P))
+        self.L.orc_row_partials(_ptr(wrow), bits, _ptr(xq), xq.size, _ptr(P))
         return P
 
     def rescale(self, P, d, s):
@@ -207,17 +239,18 @@ class Oracle:
         d = _c(d, np.float32)
         return self.L.orc_rescale(_ptr(P), _ptr(d), P.size, s)
 
-    def matvec(self, Wq, Ws, xq, xd, want_partials=False, want_absterm=False):
-        Wq = _c(Wq, np.uint8)
+    def matvec(self, Wq, Ws, xq, xd, want_partials=False, want_absterm=False, bits=4):
+        Wq = _container(np.asarray(Wq), bits)
         Ws = _c(Ws, np.float32)
         xq = _c(xq, np.int8)
         xd = _c(xd, np.float32)
         rows = Wq.shape[0]
-        k = Wq.shape[1] * 2
+        k = Wq.shape[1] * (8 // bits)
         y = np.empty(rows, dtype=np.float32)
         P = np.empty((rows, k // 32), dtype=np.int32) if want_partials else None
         A = np.empty(rows, dtype=np.float64) if want_absterm else None
-        self.L.orc_matvec(_ptr(Wq), _ptr(Ws), rows, k, _ptr(xq), _ptr(xd), _ptr(y), _ptr(P), _ptr(A))
+        self.L.orc_matvec(_ptr(Wq), bits, _ptr(Ws), rows, k, _ptr(xq), _ptr(xd), _ptr(y), _ptr(P),
+                          _ptr(A))
         return y, P, A
 
     def expert_forward(self, ex: Expert, xq, xd, want_partials=False):
@@ -234,7 +267,8 @@ class Oracle:
             out["P_gate"] = np.empty((F, D // 32), np.int32)
             out["P_up"] = np.empty((F, D // 32), np.int32)
             out["P_down"] = np.empty((D, F // 32), np.int32)
-        self.L.orc_expert(*ex.ptrs(), D, F, _ptr(xq), _ptr(xd), _ptr(out["g"]), _ptr(out["u"]),
+        self.L.orc_expert(*ex.ptrs(), ex.bits, D, F, _ptr(xq), _ptr(xd), _ptr(out["g"]),
+                          _ptr(out["u"]),
                          _ptr(out["h"]), _ptr(out["hq"]), _ptr(out["hd"]), _ptr(out["o"]),
                          _ptr(out.get("P_gate")), _ptr(out.get("P_up")), _ptr(out.get("P_down")),
                          _ptr(out["abs_o"]))
@@ -250,11 +284,12 @@ class Oracle:
         w = _c(w, np.float32)
         T, k = idx.shape
         any_ex = next(iter(experts.values())) if isinstance(experts, dict) else experts[0]
-        D, F = any_ex.D, any_ex.F
+        D, F, bits = any_ex.D, any_ex.F, any_ex.bits
         table = (ctypes.c_void_p * (6 * (E + S)))()
         for e in range(E + S):
             ex = experts.get(e) if isinstance(experts, dict) else experts[e]
             if ex is not None:
+                assert ex.bits == bits, "one container kind per layer"
                 for m, p in enumerate(ex.ptrs()):
                     table[6 * e + m] = p
         if out is None:
@@ -262,8 +297,8 @@ class Oracle:
         else:
             out = np.array(out, dtype=np.float32, copy=True, order="C")
         absterm = np.empty((T, D), dtype=np.float64)
-        rc = self.L.orc_moe_layer(table, E, S, D, F, T, _ptr(xq), _ptr(xd), _ptr(idx), _ptr(w), k,
-                                 _ptr(out), int(bool(accumulate)), _ptr(absterm))
+        rc = self.L.orc_moe_layer(table, bits, E, S, D, F, T, _ptr(xq), _ptr(xd), _ptr(idx),
+                                 _ptr(w), k, _ptr(out), int(bool(accumulate)), _ptr(absterm))
         if rc != 0:
             raise ValueError("orc_moe_layer: a selected expert is missing or an index is invalid")
         return out, absterm

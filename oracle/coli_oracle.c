@@ -28,7 +28,9 @@
  *
  * Readings where the pages are silent (each is the plainest one the rest
  * supports): Q8 blocks hold 32 values with an F32 scale max|x|/127; int4
- * rows use s = max|w|/7 and codes in [-7, 7]; the low nibble holds the even
+ * rows use s = max|w|/7 and codes in [-7, 7]; int8 rows (the container of
+ * the speculative head) use s = max|w|/127 and codes in [-127, 127], one
+ * byte per column, through the same dot; the low nibble holds the even
  * column; the expert FFN is SwiGLU; the combine is shared + sum_j w_j o_j;
  * the hidden vector is re-quantised with Q8_0 before the down projection;
  * fp32 accumulation runs over blocks in ascending order with one fused
@@ -164,6 +166,36 @@ void orc_q4_quant(const float* w, int64_t rows, int64_t k, uint8_t* packed, floa
 }
 
 /* ------------------------------------------------------------------------
+ * Per-row symmetric int8, the container of the speculative-decoding head
+ * (discuss.pytorch.kr, "colibri의 주요 기능": that head has to stay int8,
+ * and the int8 container is what the packed forms are checked against;
+ * jeff.news, MTP section).  Same rule as int4 with 127 levels a side:
+ * s = max|w| / 127, q = lrintf(w / s) clamped to [-127, 127]; an all-zero
+ * row gets s = 0, q = 0.  The container is rows x k int8 + rows f32 scales.
+ */
+void orc_q8w_quant_row(const float* w, int64_t k, int8_t* q, float* s) {
+  float amax = 0.0f;
+  for (int64_t j = 0; j < k; ++j) {
+    const float a = fabsf(w[j]);
+    if (a > amax) amax = a;
+  }
+  const float sw = amax / 127.0f;
+  *s = sw;
+  for (int64_t j = 0; j < k; ++j) {
+    long v = 0;
+    if (sw != 0.0f) v = lrintf(w[j] / sw);
+    if (v > 127) v = 127;
+    if (v < -127) v = -127;
+    q[j] = (int8_t)v;
+  }
+}
+
+void orc_q8w_quant(const float* w, int64_t rows, int64_t k, int8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) orc_q8w_quant_row(w + r * k, k, q + r * k, s + r);
+}
+
+/* ------------------------------------------------------------------------
  * Sigmoid top-k routing (DeepSeek-V3 style, jeff.news attention-and-kernels
  * section).  Per token: s_e = sigma(logit_e); the selection score is
  * c_e = s_e + bias_e (the bias steers selection only); the k largest c are
@@ -201,12 +233,20 @@ void orc_route(const float* logits, const float* bias, int64_t T, int32_t E, int
 }
 
 /* ------------------------------------------------------------------------
- * Integer dot of one packed int4 row with a Q8 vector, per block of 32:
- * P_b = sum_j q_w * q_x, exact in int32 (|P_b| <= 32*8*127).
+ * Integer dot of one weight row with a Q8 vector, per block of 32:
+ * P_b = sum_j q_w * q_x, exact in int32 (|P_b| <= 32*127*127).  bits = 4:
+ * the row is the nibble container (k/2 bytes); bits = 8: the int8 container
+ * (k bytes, one code per column).
  */
-void orc_row_partials(const uint8_t* wrow, const int8_t* xq, int64_t k, int32_t* P) {
+void orc_row_partials(const uint8_t* wrow, int bits, const int8_t* xq, int64_t k, int32_t* P) {
   for (int64_t b = 0; b < k / 32; ++b) {
     int32_t acc = 0;
+    if (bits == 8) {
+      const int8_t* w8 = (const int8_t*)wrow + 32 * b;
+      for (int j = 0; j < 32; ++j) acc += (int32_t)w8[j] * (int32_t)xq[32 * b + j];
+      P[b] = acc;
+      continue;
+    }
     for (int j = 0; j < 16; ++j) {
       const uint8_t byte = wrow[16 * b + j];
       const int lo = byte & 0x0F, hi = byte >> 4;
@@ -225,7 +265,8 @@ float orc_rescale(const int32_t* P, const float* d, int64_t nb, float s) {
   return acc * s;
 }
 
-void orc_matvec(const uint8_t* Wq, const float* Ws, int64_t rows, int64_t k,
+/* y = W x for a weight matrix in either container (bits 4 or 8). */
+void orc_matvec(const uint8_t* Wq, int bits, const float* Ws, int64_t rows, int64_t k,
                 const int8_t* xq, const float* xd, float* y, int32_t* P, double* absterm) {
   const int64_t nb = k / 32;
 #pragma omp parallel
@@ -233,7 +274,7 @@ void orc_matvec(const uint8_t* Wq, const float* Ws, int64_t rows, int64_t k,
     int32_t* Pl = (int32_t*)malloc(sizeof(int32_t) * (size_t)nb);
 #pragma omp for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-      orc_row_partials(Wq + r * (k / 2), xq, k, Pl);
+      orc_row_partials(Wq + r * (k * bits / 8), bits, xq, k, Pl);
       y[r] = orc_rescale(Pl, xd, nb, Ws[r]);
       if (P) memcpy(P + r * nb, Pl, sizeof(int32_t) * (size_t)nb);
       if (absterm) {
@@ -251,23 +292,23 @@ void orc_matvec(const uint8_t* Wq, const float* Ws, int64_t rows, int64_t k,
  * h = silu(g) * u, (hq, hd) = Q8_0(h), o = W_down hq.
  */
 void orc_expert(const uint8_t* gate_q, const float* gate_s, const uint8_t* up_q,
-                const float* up_s, const uint8_t* down_q, const float* down_s, int64_t D,
-                int64_t F, const int8_t* xq, const float* xd, float* g, float* u, float* h,
-                int8_t* hq, float* hd, float* o, int32_t* P_gate, int32_t* P_up,
+                const float* up_s, const uint8_t* down_q, const float* down_s, int bits,
+                int64_t D, int64_t F, const int8_t* xq, const float* xd, float* g, float* u,
+                float* h, int8_t* hq, float* hd, float* o, int32_t* P_gate, int32_t* P_up,
                 int32_t* P_down, double* abs_down) {
-  orc_matvec(gate_q, gate_s, F, D, xq, xd, g, P_gate, NULL);
-  orc_matvec(up_q, up_s, F, D, xq, xd, u, P_up, NULL);
+  orc_matvec(gate_q, bits, gate_s, F, D, xq, xd, g, P_gate, NULL);
+  orc_matvec(up_q, bits, up_s, F, D, xq, xd, u, P_up, NULL);
   for (int64_t r = 0; r < F; ++r) h[r] = orc_siluf(g[r]) * u[r];
   orc_q8_quant(h, F, hq, hd);
-  orc_matvec(down_q, down_s, D, F, hq, hd, o, P_down, abs_down);
+  orc_matvec(down_q, bits, down_s, D, F, hq, hd, o, P_down, abs_down);
 }
 
 /* ------------------------------------------------------------------------
  * The MoE layer, token by token: y = o_shared (0 without a shared expert),
  * then y = fmaf(w_j, o_idx_j, y) for j = 0..k-1; out = y or out + y.
  */
-int orc_moe_layer(const void* const* experts, int32_t E, int32_t S, int64_t D, int64_t F,
-                  int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
+int orc_moe_layer(const void* const* experts, int bits, int32_t E, int32_t S, int64_t D,
+                  int64_t F, int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
                   const float* w, int32_t k, float* out, int accumulate, double* absterm) {
   float* g = (float*)malloc(sizeof(float) * (size_t)F);
   float* u = (float*)malloc(sizeof(float) * (size_t)F);
@@ -289,8 +330,8 @@ int orc_moe_layer(const void* const* experts, int32_t E, int32_t S, int64_t D, i
       const void* const* ex = experts + 6 * (int64_t)e;
       if (!ex[0] || !ex[1] || !ex[2] || !ex[3] || !ex[4] || !ex[5]) { rc = -1; break; }
       orc_expert((const uint8_t*)ex[0], (const float*)ex[1], (const uint8_t*)ex[2],
-                 (const float*)ex[3], (const uint8_t*)ex[4], (const float*)ex[5], D, F, xt, dt,
-                 g, u, h, hq, hd, o, NULL, NULL, NULL, m);
+                 (const float*)ex[3], (const uint8_t*)ex[4], (const float*)ex[5], bits, D, F,
+                 xt, dt, g, u, h, hq, hd, o, NULL, NULL, NULL, m);
       if (j < 0) {
         for (int64_t r = 0; r < D; ++r) { y[r] = o[r]; my[r] = m[r]; }
       } else {

@@ -39,6 +39,11 @@ void orc_q4_quant_row(const float* w, int64_t k, int8_t* q, float* s);
 /* rows x k fp32 -> canonical container: rows x k/2 bytes + rows f32 scales. */
 void orc_q4_quant(const float* w, int64_t rows, int64_t k, uint8_t* packed, float* s);
 
+/* per-row symmetric int8 (the int8 container): s = max|w| / 127,
+ * q = lrintf(w / s) in [-127, 127]; rows x k int8 + rows f32 scales. */
+void orc_q8w_quant_row(const float* w, int64_t k, int8_t* q, float* s);
+void orc_q8w_quant(const float* w, int64_t rows, int64_t k, int8_t* q, float* s);
+
 /* nibble container: byte i = (q[2i] & 15) | (q[2i+1] & 15) << 4. */
 void orc_pack_q4(const int8_t* q, int64_t n, uint8_t* out);
 void orc_unpack_q4(const uint8_t* in, int64_t n, int8_t* q);
@@ -48,31 +53,36 @@ void orc_unpack_q4(const uint8_t* in, int64_t n, int8_t* q);
 void orc_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
                float routed_scale, int32_t* idx, float* w);
 
-/* int32 block partials of one packed row with a Q8 vector: P[k/32]. */
-void orc_row_partials(const uint8_t* wrow, const int8_t* xq, int64_t k, int32_t* P);
+/* Weight matrices come in one of two containers, named by `bits`: 4 = the
+ * nibble container (k/2 bytes per row), 8 = the int8 container (k bytes per
+ * row, one int8 code per column).  Scales are one f32 per row in both. */
+
+/* int32 block partials of one weight row with a Q8 vector: P[k/32]. */
+void orc_row_partials(const uint8_t* wrow, int bits, const int8_t* xq, int64_t k, int32_t* P);
 /* acc = 0; for b ascending: acc = fmaf((float)P[b], d[b], acc); return acc * s. */
 float orc_rescale(const int32_t* P, const float* d, int64_t nb, float s);
-/* y[r] for every row of a packed matrix; P (rows x k/32) and absterm (fp64
+/* y[r] for every row of a weight matrix; P (rows x k/32) and absterm (fp64
  * sum over blocks of |s * d_b * P_b|) are optional (NULL to skip). */
-void orc_matvec(const uint8_t* Wq, const float* Ws, int64_t rows, int64_t k,
+void orc_matvec(const uint8_t* Wq, int bits, const float* Ws, int64_t rows, int64_t k,
                 const int8_t* xq, const float* xd, float* y, int32_t* P, double* absterm);
 
 /* One SwiGLU expert on one Q8 token.  Every output is required except the
  * optional partial/absterm dumps (NULL to skip). */
 void orc_expert(const uint8_t* gate_q, const float* gate_s, const uint8_t* up_q,
-                const float* up_s, const uint8_t* down_q, const float* down_s, int64_t D,
-                int64_t F, const int8_t* xq, const float* xd, float* g, float* u, float* h,
-                int8_t* hq, float* hd, float* o, int32_t* P_gate, int32_t* P_up,
+                const float* up_s, const uint8_t* down_q, const float* down_s, int bits,
+                int64_t D, int64_t F, const int8_t* xq, const float* xd, float* g, float* u,
+                float* h, int8_t* hq, float* hd, float* o, int32_t* P_gate, int32_t* P_up,
                 int32_t* P_down, double* abs_down);
 
-/* The MoE layer for T tokens.  experts[e*6 + m] holds, for expert e in
+/* The MoE layer for T tokens, every expert in the container `bits`.
+ * experts[e*6 + m] holds, for expert e in
  * [0, E+S), the six container pointers gate_q, gate_s, up_q, up_s, down_q,
  * down_s (NULL rows are allowed for experts no token selects).  The shared
  * expert is index E.  out[T][D] = moe (accumulate = 0) or out + moe (1).
  * absterm[T][D] (optional) receives the fp64 sum of |terms| of each output.
  * Returns 0, or -1 if a selected expert is missing / an index is invalid. */
-int orc_moe_layer(const void* const* experts, int32_t E, int32_t S, int64_t D, int64_t F,
-                  int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
+int orc_moe_layer(const void* const* experts, int bits, int32_t E, int32_t S, int64_t D,
+                  int64_t F, int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
                   const float* w, int32_t k, float* out, int accumulate, double* absterm);
 
 /* RMSNorm with unit gain: ss in fp64, r = (float)(1/sqrt(ss/D + eps)), out = h * r. */

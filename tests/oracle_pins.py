@@ -59,9 +59,14 @@ def load_golden(name):
     return rows
 
 
-def dot_ref64(Wq, Ws, xq, xd):
+def codes_of(Wq, bits=4):
+    """The integer codes of a weight container: nibbles (bits 4) or int8 (bits 8)."""
+    return unpack_ref(Wq) if bits == 4 else Wq.view(np.int8).astype(np.int64)
+
+
+def dot_ref64(Wq, Ws, xq, xd, bits=4):
     """fp64 dequantised matmul and its sum of |terms|, from int64 brute force."""
-    qw = unpack_ref(Wq)                         # rows x k
+    qw = codes_of(Wq, bits)                     # rows x k
     rows, k = qw.shape
     P = (qw.reshape(rows, k // 32, 32) * xq.astype(np.int64).reshape(1, k // 32, 32)).sum(-1)
     terms = Ws.astype(np.float64)[:, None] * xd.astype(np.float64)[None, :] * P
@@ -284,11 +289,11 @@ def pin_route(orc):
         assert np.all(np.abs(w.astype(np.float64).sum(1) - scale) <= k * 1.2e-7 * scale)
 
 
-def _tiny_expert(orc, rng, D, F, sigma=0.02):
+def _tiny_expert(orc, rng, D, F, sigma=0.02, bits=4):
     from oracle import Expert
     ws = [(rng.standard_normal(shape) * sigma).astype(np.float32)
           for shape in ((F, D), (F, D), (D, F))]
-    return Expert.quantize(*ws, orc=orc)
+    return Expert.quantize(*ws, orc=orc, bits=bits)
 
 
 def _silu64(g):
@@ -296,14 +301,18 @@ def _silu64(g):
 
 
 def pin_expert_fp64(orc):
-    rng = np.random.default_rng(6)
+    for bits, seed in ((4, 6), (8, 16)):
+        _expert_fp64(orc, bits, np.random.default_rng(seed))
+
+
+def _expert_fp64(orc, bits, rng):
     D, F = 256, 128
-    ex = _tiny_expert(orc, rng, D, F)
+    ex = _tiny_expert(orc, rng, D, F, bits=bits)
     x = rng.standard_normal(D).astype(np.float32)
     xq, xd = orc.q8_quant(x)
     r = orc.expert_forward(ex, xq, xd, want_partials=True)
-    g64, ga, Pg = dot_ref64(ex.gate_q, ex.gate_s, xq, xd)
-    u64, ua, Pu = dot_ref64(ex.up_q, ex.up_s, xq, xd)
+    g64, ga, Pg = dot_ref64(ex.gate_q, ex.gate_s, xq, xd, bits)
+    u64, ua, Pu = dot_ref64(ex.up_q, ex.up_s, xq, xd, bits)
     assert np.array_equal(r["P_gate"], Pg) and np.array_equal(r["P_up"], Pu)
     within_tol(r["g"], g64, ga, "gate")
     within_tol(r["u"], u64, ua, "up")
@@ -316,7 +325,7 @@ def pin_expert_fp64(orc):
     ratio = (hb / r["hd"][:, None]).astype(np.float32).astype(np.float64)
     assert np.all(np.abs(ratio - r["hq"].reshape(-1, 32)) <= 0.5)
     # the down projection of the oracle's Q8(h), in fp64
-    o64, oa, Pd = dot_ref64(ex.down_q, ex.down_s, r["hq"], r["hd"])
+    o64, oa, Pd = dot_ref64(ex.down_q, ex.down_s, r["hq"], r["hd"], bits)
     assert np.array_equal(r["P_down"], Pd)
     within_tol(r["o"], o64, oa, "down")
     assert np.allclose(r["abs_o"], oa, rtol=1e-12)
@@ -431,6 +440,79 @@ def pin_dispatch(orc):
         raise AssertionError(f"dispatch accepted {bad}")
 
 
+def pin_int8_quant(orc):
+    """Per-row int8 weights: scale 2^-3 makes every quotient exact, so the
+    codes of half-integer multiples are the textbook round-half-to-even."""
+    mult = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, 125.5, 126.5, -126.5, 127.0, -3.0]
+    want = [0, 2, 2, 4, 0, -2, -2, 126, 126, -126, 127, -3]
+    q, s = orc.q8w_quant_row(np.array(mult, np.float32) * np.float32(2.0 ** -3))
+    assert s == 2.0 ** -3, f"int8 scale {s}"
+    assert [int(v) for v in q] == want, f"int8 ties -> {list(q)}"
+    for c in (0.02, -1.5, 3e-30):
+        q, s = orc.q8w_quant_row(np.full(48, c, np.float32))
+        assert np.all(q == (127 if c > 0 else -127))
+        assert s == np.float32(abs(np.float32(c))) / np.float32(127)
+    q, s = orc.q8w_quant_row(np.zeros(64, np.float32))
+    assert s == 0.0 and np.all(q == 0), "int8 zero row"
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    qi, sc = orc.q8w_quant(w)
+    qi = qi.astype(np.int64)
+    assert np.all(np.abs(qi) <= 127) and np.all(np.abs(qi).max(1) == 127), "int8 range / max"
+    ratio = (w / sc[:, None]).astype(np.float32).astype(np.float64)
+    assert np.all(np.abs(ratio - qi) <= 0.5), "int8 not nearest"
+    assert np.all(qi[np.abs(ratio - qi) == 0.5] % 2 == 0), "int8 tie not to even"
+    assert np.all(sc == np.abs(w).max(1) / np.float32(127)), "int8 scale"
+    # each row is the same rule applied alone
+    q0, s0 = orc.q8w_quant_row(w[5])
+    assert np.array_equal(q0.astype(np.int64), qi[5]) and s0 == sc[5]
+
+
+def pin_int8_container(orc):
+    """The int8 container through the dot: brute-force int64 partials over the
+    full code range, fp64 dequantised matvec, and the pages' invariant that the
+    nibble container and the int8 container holding the same codes give
+    identical results, from the partials up to the layer output."""
+    from oracle import Expert
+    rng = np.random.default_rng(18)
+    for rows, k in ((7, 32), (33, 256), (64, 2048)):
+        q = rng.integers(-127, 128, size=(rows, k)).astype(np.int8)
+        Ws = rng.uniform(0.5, 2.0, rows).astype(np.float32)
+        xq = rng.integers(-127, 128, size=k).astype(np.int8)
+        xd = rng.uniform(0.01, 0.1, k // 32).astype(np.float32)
+        _, P, _ = orc.matvec(q, Ws, xq, xd, want_partials=True, bits=8)
+        ref = np.einsum("rbj,bj->rb", q.astype(np.int64).reshape(rows, -1, 32),
+                        xq.astype(np.int64).reshape(-1, 32))
+        assert np.array_equal(P.astype(np.int64), ref), f"int8 partials {rows}x{k}"
+    P = orc.row_partials(np.full(64, 127, np.int8), np.full(64, -127, np.int8), bits=8)
+    assert np.all(P == -32 * 127 * 127), "int8 extreme block"
+    for rows, k in ((16, 256), (64, 6144)):
+        w = (rng.standard_normal((rows, k)) * 0.02).astype(np.float32)
+        Wq, Ws = orc.q8w_quant(w)
+        xq, xd = orc.q8_quant(rng.standard_normal(k).astype(np.float32))
+        y, _, _ = orc.matvec(Wq, Ws, xq, xd, bits=8)
+        ref, absterm, _ = dot_ref64(Wq, Ws, xq, xd, bits=8)
+        within_tol(y, ref, absterm, f"int8 matvec {rows}x{k}")
+    # same codes in both containers -> identical results
+    D, F, E, k, T = 256, 128, 6, 2, 5
+    pair = {}
+    for e in range(E + 1):
+        mats = [rng.integers(-8, 8, size=shape).astype(np.int8) for shape in ((F, D), (F, D), (D, F))]
+        sc = [rng.uniform(1e-3, 1e-2, m.shape[0]).astype(np.float32) for m in mats]
+        pair[e] = (Expert(orc.pack_q4(mats[0]), sc[0], orc.pack_q4(mats[1]), sc[1],
+                          orc.pack_q4(mats[2]), sc[2], bits=4),
+                   Expert(mats[0], sc[0], mats[1], sc[1], mats[2], sc[2], bits=8))
+    xq, xd = orc.q8_quant(rng.standard_normal((T, D)).astype(np.float32))
+    r4 = orc.expert_forward(pair[0][0], xq[0], xd[0], want_partials=True)
+    r8 = orc.expert_forward(pair[0][1], xq[0], xd[0], want_partials=True)
+    for key in r4:
+        assert np.array_equal(r4[key], r8[key]), f"container identity: {key}"
+    idx, w = orc.route(rng.standard_normal((T, E)).astype(np.float32), np.zeros(E, np.float32), k)
+    y4, _ = orc.moe_layer({e: p[0] for e, p in pair.items()}, E, 1, xq, xd, idx, w)
+    y8, _ = orc.moe_layer({e: p[1] for e, p in pair.items()}, E, 1, xq, xd, idx, w)
+    assert np.array_equal(y4, y8), "container identity: layer output"
+
+
 ALL_PINS = [pin_nibble_codec, pin_rint_ties, pin_quant_closed_forms, pin_partials_bruteforce,
             pin_dot_fp64, pin_exp, pin_route, pin_expert_fp64, pin_moe_invariants, pin_rmsnorm,
-            pin_dispatch, pin_router_logits]
+            pin_dispatch, pin_router_logits, pin_int8_quant, pin_int8_container]

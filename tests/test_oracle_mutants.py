@@ -54,8 +54,16 @@ MUTANTS = {
                                    "(s[idx[t * k + j]] / sum);"),
     "swiglu uses the gate twice": ("h[r] = orc_siluf(g[r]) * u[r];", "h[r] = orc_siluf(g[r]) * g[r];"),
     "down projection skips Q8(h) scale":
-        ("orc_matvec(down_q, down_s, D, F, hq, hd, o, P_down, abs_down);",
-         "orc_matvec(down_q, gate_s, D, F, hq, hd, o, P_down, abs_down);"),
+        ("orc_matvec(down_q, bits, down_s, D, F, hq, hd, o, P_down, abs_down);",
+         "orc_matvec(down_q, bits, gate_s, D, F, hq, hd, o, P_down, abs_down);"),
+    "int8 weights scale over 128": ("const float sw = amax / 127.0f;",
+                                    "const float sw = amax / 128.0f;"),
+    "int8 weights round half away from zero": ("v = lrintf(w[j] / sw);", "v = lroundf(w[j] / sw);"),
+    "int8 weights clamp at 63": ("    if (v > 127) v = 127;\n    if (v < -127) v = -127;\n    q[j]",
+                                 "    if (v > 63) v = 63;\n    if (v < -127) v = -127;\n    q[j]"),
+    "int8 partials read unsigned codes":
+        ("const int8_t* w8 = (const int8_t*)wrow + 32 * b;", "const uint8_t* w8 = wrow + 32 * b;"),
+    "int8 rows at the nibble stride": ("Wq + r * (k * bits / 8)", "Wq + r * (k / 2)"),
     "combine drops the shared expert": ("for (int64_t r = 0; r < D; ++r) { y[r] = o[r]; my[r] = m[r]; }",
                                         "for (int64_t r = 0; r < D; ++r) { y[r] = 0.0f; my[r] = m[r]; }"),
     "combine ignores routing weights": ("y[r] = fmaf(wj, o[r], y[r]);", "y[r] = y[r] + o[r];"),
