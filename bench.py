@@ -37,21 +37,27 @@ INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of MI355X
 METRIC = "MoE-layer decode tok/s + achieved HBM GB/s (int4 experts); prefill int8 TOPS"
 
 
-def build_table(w, coli, synth, torch):
-    """Device table from device-generated seeded weights, quantised by the library."""
-    table = coli.ExpertTable(w.E, w.S, w.D, w.F)
+HEAD_LAYER = 78   # the int8 speculative head sits after the 78 main layers
+
+
+def build_table(w, coli, synth, torch, layer=0, bits=4):
+    """Device table from device-generated seeded weights, quantised by the library
+    (int4, or int8 for the speculative head)."""
+    table = coli.ExpertTable(w.E, w.S, w.D, w.F, weight_bits=bits)
     F, D = w.F, w.D
     scratch = torch.empty(F * D, dtype=torch.float32, device="cuda")
-    q = [torch.empty((F, D // 2), dtype=torch.uint8, device="cuda") for _ in range(2)]
-    q.append(torch.empty((D, F // 2), dtype=torch.uint8, device="cuda"))
+    per, qdt = (2, torch.uint8) if bits == 4 else (1, torch.int8)
+    quant = coli.coli_quant_weight_q4 if bits == 4 else coli.coli_quant_weight_q8
+    q = [torch.empty((F, D // per), dtype=qdt, device="cuda") for _ in range(2)]
+    q.append(torch.empty((D, F // per), dtype=qdt, device="cuda"))
     s = [torch.empty(F, dtype=torch.float32, device="cuda") for _ in range(2)]
     s.append(torch.empty(D, dtype=torch.float32, device="cuda"))
     sp = torch.cuda.current_stream().cuda_stream
     for e in range(w.E + w.S):
         for m in range(3):
             rows, cols = synth.weight_shape(w, m)
-            synth.weight_device(w, 0, e, m, scratch.data_ptr(), sp)
-            coli.coli_quant_weight_q4(scratch[: rows * cols].view(rows, cols), q[m], s[m])
+            synth.weight_device(w, layer, e, m, scratch.data_ptr(), sp)
+            quant(scratch[: rows * cols].view(rows, cols), q[m], s[m])
         coli.coli_table_set_expert(table, e, q[0], s[0], q[1], s[1], q[2], s[2])
     torch.cuda.synchronize()
     return table
@@ -84,9 +90,9 @@ class HipEvents:
         return ms.value
 
 
-def expert_bytes(w):
-    gate_up = 2 * (w.F * w.D // 2 + 4 * w.F)
-    down = w.D * w.F // 2 + 4 * w.D
+def expert_bytes(w, bits=4):
+    gate_up = 2 * (w.F * w.D * bits // 8 + 4 * w.F)
+    down = w.D * w.F * bits // 8 + 4 * w.D
     return gate_up, down
 
 
@@ -183,6 +189,77 @@ def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
     }
 
 
+def head_leg(coli, synth, torch, hev, replays=4, pool=64):
+    """The int8 speculative head (its own 6144 x 2048, 256 + 1 expert layer,
+    int8 weights, 9.7 GB) at decode (1 token per pass) and in the batched
+    verify pass (4 tokens per pass, batch union): coli_moe_layer passes over a
+    pool of 64 seeded passes, graph-captured; weight GB/s counts each pass's
+    expert union once; the gate/up kernel is timed with HIP events."""
+    w2 = synth.WORKLOADS[2]
+    table = build_table(w2, coli, synth, torch, layer=HEAD_LAYER, bits=8)
+    gu_bytes, dn_bytes = expert_bytes(w2, bits=8)
+    res = {"workload": "int8 head d6144 f2048 e256+1 top8", "table_bytes": table.bytes}
+    for wid in (1, 2):
+        w = synth.WORKLOADS[wid]
+        T, P = w.T, pool
+        x = torch.from_numpy(synth.activations(w, P * T, 3000)).cuda()
+        lg = torch.from_numpy(synth.logits(w, P * T, 3000)).cuda()
+        b = torch.from_numpy(synth.router_bias(w)).cuda()
+        y = torch.empty((P * T, w.D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(coli.coli_moe_layer_workspace_bytes(table, T, w.k), dtype=torch.uint8,
+                         device="cuda")
+        idx = torch.empty((P * T, w.k), dtype=torch.int32, device="cuda")
+        wt = torch.empty((P * T, w.k), dtype=torch.float32, device="cuda")
+        coli.coli_route_topk(lg, b, w.k, idx, wt)
+        ih = idx.cpu().numpy()
+        union = [len(set(ih[j * T:(j + 1) * T].reshape(-1).tolist())) + w.S for j in range(P)]
+
+        def step(j, events=None):
+            sl = slice(j * T, (j + 1) * T)
+            coli.coli_moe_layer(table, x[sl], lg[sl], b, w.k, y[sl], ws, events=events)
+
+        for j in range(P):
+            step(j)
+        torch.cuda.synchronize()
+        if coli.coli_moe_status(ws) != coli.COLI_OK:
+            raise RuntimeError("device-side index check failed (int8 head)")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(P):
+                step(j)
+        g.replay()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(replays):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / (replays * P)
+        evs = [{k: hev.create() for k in ("begin", "gate_up", "down", "combine", "end")}
+               for _ in range(P)]
+        for _ in range(2):
+            g.replay()
+        for j in range(P):
+            step(j, evs[j])
+        torch.cuda.synchronize()
+        gu_ms = sum(hev.elapsed_ms(e["gate_up"], e["down"]) for e in evs) / P
+        dn_ms = sum(hev.elapsed_ms(e["down"], e["combine"]) for e in evs) / P
+        u = sum(union) / P
+        res[f"t{T}"] = {
+            "tokens_per_pass": T, "passes": replays * P, "ms_per_pass": round(ms, 5),
+            "tok_s": round(T / (ms * 1e-3), 1), "experts_per_pass": round(u, 2),
+            "weight_gbps": round(u * (gu_bytes + dn_bytes) / (ms * 1e-3) / 1e9, 1),
+            "gate_up_ms": round(gu_ms, 5), "down_ms": round(dn_ms, 5),
+            "gate_up_gbps": round(u * gu_bytes / (gu_ms * 1e-3) / 1e9, 1),
+            "down_gbps": round(u * dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
+        }
+    del table
+    torch.cuda.empty_cache()
+    return res
+
+
 def router_leg(coli, synth, torch, steps=50):
     """The router projection (F32 weights [256][6144], fp64 sum) for 1 and 2048 tokens."""
     w = synth.WORKLOADS[1]
@@ -220,6 +297,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch steps directly, no HIP graph")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="timed 2048-token passes of the prefill leg (0: skip it)")
+    ap.add_argument("--no-head", action="store_true", help="skip the int8 head leg")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 8 device-to-device copies of this many bytes (the known-size "
                          "kernel that scales the HBM byte counters under rocprofv3 --pmc)")
@@ -373,6 +451,8 @@ def main():
                           prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3,
                                       bias_free=True)]
     out["router_logits"] = router_leg(coli, synth, torch)
+    if not args.no_head:
+        out["int8_head"] = head_leg(coli, synth, torch, hev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -86,30 +86,48 @@ typedef enum {
  * Within a 16-byte chunk, 32-bit word k (0..3) holds columns 8k..8k+7 of
  * the block: byte j (0..3) has column 8k+j in its low nibble and column
  * 8k+4+j in its high nibble; each nibble stores q + 8 (0..15).
+ *
+ * int8 tables (weight_bits = 8): the container of the int8 speculative head
+ * (discuss.pytorch.kr colibri summary, "colibri의 주요 기능", MTP bullet:
+ * that head must be int8; jeff.news, MTP section).  Codes are int8 in
+ * [-127, 127] with the same per-row F32 scales and the same Q8_0 block dot.
+ * A block of 32 columns is two 16-byte chunks, so the chunk index runs over
+ * half-blocks:
+ *   gu_q  [E+S][F/32][D/16][64][16], chunk c of lane l = columns
+ *         16c..16c+15 of the lane's row (gate rows l < 32, up rows l >= 32);
+ *   dn_q  [E+S][D/64][F/16][64][16];
+ * byte j of a chunk is column 16c+j as a two's-complement int8.  gu_s and
+ * dn_s are as above.  int8 tables run the GEMV kernels at every batch size.
+ *
  * The shared expert (when S = 1) is index E.  E <= 256, S in {0, 1},
- * D % 64 == 0, F % 32 == 0, D and F <= COLI_MAX_DIM.
+ * D % 64 == 0, F % 32 == 0, D and F <= COLI_MAX_DIM, weight_bits 4 or 8.
  */
 typedef struct {
-  int32_t n_routed; /* E */
-  int32_t n_shared; /* S */
-  int32_t d_model;  /* D */
-  int32_t d_ff;     /* F */
+  int32_t n_routed;    /* E */
+  int32_t n_shared;    /* S */
+  int32_t d_model;     /* D */
+  int32_t d_ff;        /* F */
+  int32_t weight_bits; /* 4: nibble-packed int4 codes; 8: int8 codes */
   uint8_t* gu_q;
   float* gu_s;
   uint8_t* dn_q;
   float* dn_s;
 } coli_expert_table;
 
-/* Sizes in bytes of the four table arrays for (E, S, D, F).  Returns the
- * total, or 0 for an unsupported shape.  Output pointers may be NULL. */
+/* Sizes in bytes of the four table arrays for (E, S, D, F, weight_bits).
+ * Returns the total, or 0 for an unsupported shape.  Output pointers may be
+ * NULL. */
 size_t coli_table_bytes(int32_t n_routed, int32_t n_shared, int64_t d_model, int64_t d_ff,
-                        size_t* gu_q, size_t* gu_s, size_t* dn_q, size_t* dn_s);
+                        int32_t weight_bits, size_t* gu_q, size_t* gu_s, size_t* dn_q,
+                        size_t* dn_s);
 
 /* Copies one expert, given as the pages' canonical containers (device
- * pointers: gate_q, up_q [F][D/2] bytes with scales [F]; down_q [D][F/2]
- * with scales [D]; low nibble = even column, two's complement), into slot
- * `expert` (0..E+S-1) of the table.  The codes are unchanged; only their
- * placement and nibble encoding change (see above). */
+ * pointers), into slot `expert` (0..E+S-1) of the table.  weight_bits 4:
+ * gate_q, up_q [F][D/2] bytes with scales [F], down_q [D][F/2] with scales
+ * [D]; low nibble = even column, two's complement.  weight_bits 8: gate_q,
+ * up_q [F][D] int8 codes, down_q [D][F] int8 codes (pass them as bytes).
+ * The codes are unchanged; only their placement (and the nibble encoding)
+ * change (see above). */
 int coli_table_set_expert(const coli_expert_table* table, int32_t expert, const uint8_t* gate_q,
                           const float* gate_s, const uint8_t* up_q, const float* up_s,
                           const uint8_t* down_q, const float* down_s, void* stream);
@@ -126,6 +144,14 @@ int coli_quant_act_q8(const float* x, int64_t rows, int64_t k, int8_t* q, float*
  * w [rows][k] f32 -> q [rows][k/2] bytes (low nibble = even column, two's
  * complement) and s [rows] f32.  k % 32 == 0. */
 int coli_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, float* s,
+                         void* stream);
+
+/* Per-row symmetric int8 quantisation into the int8 container of the
+ * speculative head (discuss.pytorch.kr colibri summary, "colibri의 주요
+ * 기능", MTP bullet): s = max|w| / 127.0f, q = clamp(rint_half_even(w / s),
+ * -127, 127), an all-zero row gives s = 0 and q = 0.  w [rows][k] f32 ->
+ * q [rows][k] int8 and s [rows] f32.  k % 32 == 0. */
+int coli_quant_weight_q8(const float* w, int64_t rows, int64_t k, int8_t* q, float* s,
                          void* stream);
 
 /* Fused RMSNorm (unit gain) + Q8_0 of the normalised vector, for a pre-norm

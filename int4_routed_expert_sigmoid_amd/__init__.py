@@ -28,6 +28,7 @@ COLI_MAX_TOPK = 64
 
 EXPORTED = [
     "coli_table_bytes", "coli_table_set_expert", "coli_quant_act_q8", "coli_quant_weight_q4",
+    "coli_quant_weight_q8",
     "coli_rmsnorm_q8", "coli_route_topk", "coli_router_logits", "coli_dispatch",
     "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
@@ -50,7 +51,7 @@ class ColiError(RuntimeError):
 class coli_expert_table(ctypes.Structure):
     _fields_ = [("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
-                ("gu_q", ctypes.c_void_p), ("gu_s", ctypes.c_void_p),
+                ("weight_bits", ctypes.c_int32), ("gu_q", ctypes.c_void_p), ("gu_s", ctypes.c_void_p),
                 ("dn_q", ctypes.c_void_p), ("dn_s", ctypes.c_void_p)]
 
 
@@ -79,10 +80,11 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         sz = ctypes.c_size_t
         sig = {
-            "coli_table_bytes": ([_I32, _I32, _I64, _I64, _P, _P, _P, _P], sz),
+            "coli_table_bytes": ([_I32, _I32, _I64, _I64, _I32, _P, _P, _P, _P], sz),
             "coli_table_set_expert": ([_P, _I32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
             "coli_quant_act_q8": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
             "coli_quant_weight_q4": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+            "coli_quant_weight_q8": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
             "coli_rmsnorm_q8": ([_P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
             "coli_route_topk": ([_P, _P, _I64, _I32, _I32, ctypes.c_float, _P, _P, _P],
                                 ctypes.c_int),
@@ -140,22 +142,26 @@ def _dtype(t, dt, name):
 
 # --------------------------------------------------------------------------- table
 class ExpertTable:
-    """A device-resident expert table (torch-allocated) and its C descriptor."""
+    """A device-resident expert table (torch-allocated) and its C descriptor.
+    weight_bits 4: int4 nibble codes; 8: int8 codes (the int8 head)."""
 
-    def __init__(self, n_routed: int, n_shared: int, d_model: int, d_ff: int, device="cuda"):
+    def __init__(self, n_routed: int, n_shared: int, d_model: int, d_ff: int, device="cuda",
+                 weight_bits: int = 4):
         import torch
         sizes = [ctypes.c_size_t() for _ in range(4)]
-        total = lib().coli_table_bytes(n_routed, n_shared, d_model, d_ff,
+        total = lib().coli_table_bytes(n_routed, n_shared, d_model, d_ff, weight_bits,
                                        *[ctypes.byref(s) for s in sizes])
         if total == 0:
             raise ColiError("coli_table_bytes", COLI_E_SHAPE)
         self.E, self.S, self.D, self.F = n_routed, n_shared, d_model, d_ff
+        self.weight_bits = weight_bits
         self.gu_q = torch.empty(sizes[0].value, dtype=torch.uint8, device=device)
         self.gu_s = torch.empty(sizes[1].value // 4, dtype=torch.float32, device=device)
         self.dn_q = torch.empty(sizes[2].value, dtype=torch.uint8, device=device)
         self.dn_s = torch.empty(sizes[3].value // 4, dtype=torch.float32, device=device)
         self.bytes = total
-        self.c = coli_expert_table(n_routed, n_shared, d_model, d_ff, self.gu_q.data_ptr(),
+        self.c = coli_expert_table(n_routed, n_shared, d_model, d_ff, weight_bits,
+                                   self.gu_q.data_ptr(),
                                    self.gu_s.data_ptr(), self.dn_q.data_ptr(),
                                    self.dn_s.data_ptr())
 
@@ -186,6 +192,14 @@ def coli_quant_weight_q4(w, q, s, stream=None):
     rows, k = w.shape
     _check("coli_quant_weight_q4",
            lib().coli_quant_weight_q4(_ptr(w), rows, k, _ptr(q), _ptr(s), _stream(stream)))
+
+
+def coli_quant_weight_q8(w, q, s, stream=None):
+    import torch
+    _dtype(w, torch.float32, "w"); _dtype(q, torch.int8, "q"); _dtype(s, torch.float32, "s")
+    rows, k = w.shape
+    _check("coli_quant_weight_q8",
+           lib().coli_quant_weight_q8(_ptr(w), rows, k, _ptr(q), _ptr(s), _stream(stream)))
 
 
 def coli_rmsnorm_q8(h, eps, q, d, r_out=None, stream=None):

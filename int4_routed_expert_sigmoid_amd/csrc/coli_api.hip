@@ -55,6 +55,7 @@ int table_check(const coli_expert_table* t) {
   if (t->d_model <= 0 || t->d_model % 64 != 0 || t->d_ff <= 0 || t->d_ff % 32 != 0)
     return COLI_E_SHAPE;
   if (t->d_model > COLI_MAX_DIM || t->d_ff > COLI_MAX_DIM) return COLI_E_SHAPE;
+  if (t->weight_bits != 4 && t->weight_bits != 8) return COLI_E_SHAPE;
   if (!t->gu_q || !t->gu_s || !t->dn_q || !t->dn_s) return COLI_E_INVAL;
   if (!al16(t->gu_q) || !al16(t->dn_q) || !al4(t->gu_s) || !al4(t->dn_s)) return COLI_E_INVAL;
   return COLI_OK;
@@ -117,14 +118,14 @@ const char* coli_status_string(int status) {
 
 int coli_last_hip_error(void) { return g_last_hip_error; }
 
-size_t coli_table_bytes(int32_t E, int32_t S, int64_t D, int64_t F, size_t* gu_q, size_t* gu_s,
-                        size_t* dn_q, size_t* dn_s) {
+size_t coli_table_bytes(int32_t E, int32_t S, int64_t D, int64_t F, int32_t bits, size_t* gu_q,
+                        size_t* gu_s, size_t* dn_q, size_t* dn_s) {
   if (E < 1 || E > COLI_MAX_EXPERTS || S < 0 || S > 1 || D <= 0 || D % 64 || F <= 0 || F % 32 ||
-      D > COLI_MAX_DIM || F > COLI_MAX_DIM)
+      D > COLI_MAX_DIM || F > COLI_MAX_DIM || (bits != 4 && bits != 8))
     return 0;
   const size_t n = (size_t)(E + S);
-  const size_t a = n * (size_t)(D * F), b = n * (size_t)(2 * F) * sizeof(float),
-               c = n * (size_t)(D * F / 2), d = n * (size_t)D * sizeof(float);
+  const size_t a = n * (size_t)(D * F * bits / 4), b = n * (size_t)(2 * F) * sizeof(float),
+               c = n * (size_t)(D * F * bits / 8), d = n * (size_t)D * sizeof(float);
   if (gu_q) *gu_q = a;
   if (gu_s) *gu_s = b;
   if (dn_q) *dn_q = c;
@@ -170,6 +171,19 @@ int coli_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, fl
   int rc = check_device();
   if (rc) return rc;
   hipError_t e = coli::launch_quant_weight_q4(w, rows, k, q, s, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_quant_weight_q8(const float* w, int64_t rows, int64_t k, int8_t* q, float* s,
+                         void* stream) {
+  if (rows < 0 || k <= 0 || k % 32) return COLI_E_SHAPE;
+  if (rows > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (rows == 0) return COLI_OK;
+  if (!w || !q || !s) return COLI_E_INVAL;
+  if (!al16(w) || !al4(q) || !al4(s)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_quant_weight_q8(w, rows, k, q, s, as_stream(stream));
   return e == hipSuccess ? COLI_OK : hip_fail(e);
 }
 

@@ -24,6 +24,12 @@
 // Nibbles are stored offset-binary (q + 8), so a dot with them is
 // sum (q+8) x = P + 8 sum x; the -8 sum x term is precomputed per block.
 //
+// int8 tables (the int8 speculative head: discuss.pytorch.kr colibri summary,
+// "colibri의 주요 기능", MTP bullet; jeff.news, MTP section) run the same
+// kernels with two 1 KB wavefront loads per 32-column block (U = 2 chunks):
+// the codes are already signed bytes, so they go to v_dot4_i32_i8 as loaded
+// and the block dot starts from 0.
+//
 // The SwiGLU, the row scale and the Q8_0 re-quantisation of h are fused into
 // the gate/up epilogue; the routing-weighted combine runs as its own kernel in
 // slot order (shared expert first), which keeps it deterministic.  (Folding it
@@ -79,14 +85,16 @@ struct DnArgs {
   int32_t* tr_pd;
 };
 
-// The 32 offset-binary nibbles of one chunk, split into the 8 byte-vectors
-// that line up with the 8 int8 words of the activation block.
+// The 32 weight codes of one block as the 8 byte-vectors that line up with
+// the 8 int8 words of the activation block (offset-binary nibbles for int4,
+// signed bytes for int8).
 struct Unpacked {
   uint32_t v[8];
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// int4: one chunk holds the whole block.
 __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
   Unpacked u;
   u.v[0] = w.x & 0x0F0F0F0Fu;
@@ -98,6 +106,29 @@ __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
   u.v[6] = w.w & 0x0F0F0F0Fu;
   u.v[7] = (w.w >> 4) & 0x0F0F0F0Fu;
   return u;
+}
+
+// int8: two chunks, columns 0-15 and 16-31, bytes in column order.
+__device__ __forceinline__ Unpacked int8_block(u32x4 lo, u32x4 hi) {
+  Unpacked u;
+  u.v[0] = lo.x;
+  u.v[1] = lo.y;
+  u.v[2] = lo.z;
+  u.v[3] = lo.w;
+  u.v[4] = hi.x;
+  u.v[5] = hi.y;
+  u.v[6] = hi.z;
+  u.v[7] = hi.w;
+  return u;
+}
+
+template <int U>
+__device__ __forceinline__ Unpacked take_block(const u32x4* slot) {
+  if constexpr (U == 1) {
+    return unpack_chunk(slot[0]);
+  } else {
+    return int8_block(slot[0], slot[1]);
+  }
 }
 
 // The token blocks of one pass live in LDS: per token, NB blocks of 32 int8
@@ -130,9 +161,11 @@ __device__ __forceinline__ XBlock read_xblock(TokenLds t, int b) {
   return v;
 }
 
-// P_b of one row with one activation block: sum over 32 of q_w * q_x.
+// P_b of one row with one activation block: sum over 32 of q_w * q_x
+// (int4: the offset-binary sum plus the block's -8 sum x).
+template <int U>
 __device__ __forceinline__ int block_dot(const Unpacked& u, const XBlock& xb) {
-  int s = __float_as_int(xb.dm.y);
+  int s = U == 1 ? __float_as_int(xb.dm.y) : 0;
   s = sdot4((int)u.v[0], (int)xb.lo.x, s);
   s = sdot4((int)u.v[1], (int)xb.lo.y, s);
   s = sdot4((int)u.v[2], (int)xb.lo.z, s);
@@ -144,66 +177,63 @@ __device__ __forceinline__ int block_dot(const Unpacked& u, const XBlock& xb) {
   return s;
 }
 
-// Streams the NB chunks of one row group (lane-owned rows) and accumulates
-// exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
-// the ring of PF weight loads in flight: every refill is unconditional (its
-// index is clamped into the row group), and a block past the end of the row
-// (only when PF does not divide NB) is computed on clamped data with scale 0,
-// which leaves the accumulator bit-identical (it starts at +0 and so is
-// never -0).  Buffer loads: the row group is one descriptor (scalar
-// registers), the lane's 16-byte column a constant vector offset and the block
-// a scalar offset; each ring slot is unpacked before it is refilled, so the
-// refill reuses the slot's registers and the ring stays PF deep across the
-// loop back-edge.  Weight loads are non-temporal: each byte is used once.
-// The weight ring of one row group: PF outstanding 16-byte loads per lane.
+// The weight ring of one row group: PF outstanding 16-byte loads per lane,
+// over the NU chunks (1 KB per wavefront each) of the row group.
 template <int PF>
 struct Ring {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t loff;
-  int NB;
+  int NU;
   u32x4 buf[PF];
 
   // Issues the first PF loads, in slot order so that slot 0 lands first.
-  __device__ __forceinline__ void start(const char* wbase, uint32_t lane_off, int nb) {
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, nb * 1024, kBufferConfig);
+  __device__ __forceinline__ void start(const char* wbase, uint32_t lane_off, int nu) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, nu * 1024, kBufferConfig);
     loff = lane_off;
-    NB = nb;
+    NU = nu;
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, (i < NB ? i : NB - 1) * 1024,
+      buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, (i < NU ? i : NU - 1) * 1024,
                                                      kNonTemporal);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
 
-// Streams the NB chunks of one row group (lane-owned rows) and accumulates
+// Streams the NB blocks of one row group (lane-owned rows) and accumulates
 // exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
 // the ring of PF weight loads in flight: every refill is unconditional (its
 // index is clamped into the row group), and a block past the end of the row
-// (only when PF does not divide NB) is computed on clamped data with scale 0,
-// which leaves the accumulator bit-identical (it starts at +0 and so is
-// never -0).  Buffer loads: the row group is one descriptor (scalar
-// registers), the lane's 16-byte column a constant vector offset and the block
-// a scalar offset; each ring slot is unpacked before it is refilled, so the
-// refill reuses the slot's registers and the ring stays PF deep across the
-// loop back-edge.  Weight loads are non-temporal: each byte is used once.
-template <int NT, int PF, bool TRACE>
+// (only when PF / U does not divide NB) is computed on clamped data with
+// scale 0, which leaves the accumulator bit-identical (it starts at +0 and so
+// is never -0).  Buffer loads: the row group is one descriptor (scalar
+// registers), the lane's 16-byte column a constant vector offset and the
+// chunk a scalar offset; each ring slot is consumed before it is refilled, so
+// the ring stays PF deep across the loop back-edge.  Weight loads are
+// non-temporal: each byte is used once.
+// A block is U consecutive chunks, so PF / U blocks are in flight.
+template <int NT, int PF, int U, bool TRACE>
 __device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok, float* acc,
                                             int32_t* const* trace_row) {
-  const int NB = ring.NB;
+  static_assert(PF % U == 0, "the ring holds whole blocks");
+  constexpr int PB = PF / U;
+  const int NU = ring.NU;
+  const int NB = NU / U;
   XBlock cur[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) cur[j] = read_xblock(tok[j], 0);
-  for (int b0 = 0; b0 < NB; b0 += PF) {
+  for (int b0 = 0; b0 < NB; b0 += PB) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
+    for (int i = 0; i < PB; ++i) {
       const int b = b0 + i;
-      const Unpacked u = unpack_chunk(ring.buf[i]);
+      const Unpacked u = take_block<U>(&ring.buf[U * i]);
       __builtin_amdgcn_sched_barrier(0);
-      const int bn = b + PF < NB ? b + PF : NB - 1;
-      ring.buf[i] = __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff, bn * 1024,
-                                                          kNonTemporal);
+#pragma unroll
+      for (int c = 0; c < U; ++c) {
+        const int un = U * (b + PB) + c < NU ? U * (b + PB) + c : NU - 1;
+        ring.buf[U * i + c] = __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff,
+                                                                    un * 1024, kNonTemporal);
+      }
       const int bx = b + 1 < NB ? b + 1 : NB - 1;
       XBlock nxt[NT];
 #pragma unroll
@@ -211,7 +241,7 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int p = block_dot(u, cur[j]);
+        const int p = block_dot<U>(u, cur[j]);
         if (TRACE) {
           if (trace_row[j] && b < NB) trace_row[j][b] = p;
         }
@@ -225,17 +255,17 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok,
 }
 
 // Runs stream_rows for the nt (1..MAXT) tokens of one pass.
-template <int MAXT, int PF, bool TRACE>
+template <int MAXT, int PF, int U, bool TRACE>
 __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, const TokenLds* tok,
                                             float* acc, int32_t* const* trace_row) {
   if (MAXT >= 8 && nt > 4) {
-    stream_rows<(MAXT >= 8 ? 8 : 1), PF, TRACE>(ring, tok, acc, trace_row);
+    stream_rows<(MAXT >= 8 ? 8 : 1), PF, U, TRACE>(ring, tok, acc, trace_row);
   } else if (MAXT >= 4 && nt > 2) {
-    stream_rows<(MAXT >= 4 ? 4 : 1), PF, TRACE>(ring, tok, acc, trace_row);
+    stream_rows<(MAXT >= 4 ? 4 : 1), PF, U, TRACE>(ring, tok, acc, trace_row);
   } else if (MAXT >= 2 && nt == 2) {
-    stream_rows<(MAXT >= 2 ? 2 : 1), PF, TRACE>(ring, tok, acc, trace_row);
+    stream_rows<(MAXT >= 2 ? 2 : 1), PF, U, TRACE>(ring, tok, acc, trace_row);
   } else {
-    stream_rows<1, PF, TRACE>(ring, tok, acc, trace_row);
+    stream_rows<1, PF, U, TRACE>(ring, tok, acc, trace_row);
   }
 }
 
@@ -249,7 +279,7 @@ __device__ __forceinline__ TokenLds token_lds(int j, int NB) {
   return t;
 }
 
-template <int MAXT, int PF, bool TRACE>
+template <int MAXT, int PF, int U, bool TRACE>
 __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
   const int grp = blockIdx.x;
   const int slot = blockIdx.y;
@@ -260,10 +290,11 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
   const int NB = (int)(a.D / 32);
   const int64_t G = a.F / 32;
   const int KS = a.k + a.S;
-  const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)e * G + grp) * (size_t)NB * kWave);
+  const int NU = U * NB;                 // 1 KB chunks in the row group
+  const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)e * G + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
-  ring.start(wbase, loff, NB);          // the weight stream starts before anything else
+  ring.start(wbase, loff, NU);          // the weight stream starts before anything else
   const int cnt = as_const(a.counts)[e];
   const float rs = a.gu_s[((size_t)e * G + grp) * kWave + lane];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
@@ -274,7 +305,7 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
     int32_t* trow[MAXT];
     if (c0 > 0) {
       __syncthreads();                // the previous pass has finished reading the LDS records
-      ring.start(wbase, loff, NB);    // each pass streams the row group again
+      ring.start(wbase, loff, NU);    // each pass streams the row group again
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
@@ -294,7 +325,7 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, TRACE>(nt, ring, tok, acc, trow);
+    stream_pass<MAXT, PF, U, TRACE>(nt, ring, tok, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       if (j < nt) {
@@ -345,7 +376,7 @@ __device__ __forceinline__ float combine_row(const float* __restrict__ o,
   return acc;
 }
 
-template <int MAXT, int PF, bool TRACE>
+template <int MAXT, int PF, int U, bool TRACE>
 __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
   const int grp = blockIdx.x;
   const int slot = blockIdx.y;
@@ -354,11 +385,12 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
   if (slot >= n_active) return;
   const int lane = threadIdx.x;
   const int NB = (int)(a.F / 32);
+  const int NU = U * NB;
   const char* wbase =
-      reinterpret_cast<const char*>(a.dn_q + ((size_t)e * (a.D / 64) + grp) * (size_t)NB * kWave);
+      reinterpret_cast<const char*>(a.dn_q + ((size_t)e * (a.D / 64) + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
-  ring.start(wbase, loff, NB);          // the weight stream starts before anything else
+  ring.start(wbase, loff, NU);          // the weight stream starts before anything else
   const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
   const float rs = a.dn_s[(size_t)e * a.D + row];
@@ -370,7 +402,7 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
     int32_t* trow[MAXT];
     if (c0 > 0) {
       __syncthreads();
-      ring.start(wbase, loff, NB);
+      ring.start(wbase, loff, NU);
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
@@ -386,7 +418,7 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, TRACE>(nt, ring, tok, acc, trow);
+    stream_pass<MAXT, PF, U, TRACE>(nt, ring, tok, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j)
       if (j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
@@ -418,16 +450,16 @@ constexpr int kPfDown = 8;
 constexpr int kLdsBytesPerBlock = 40;
 constexpr size_t kLdsLimit = 65536;
 
-template <int MAXT, bool TRACE>
+template <int MAXT, int U, bool TRACE>
 hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
   const size_t lds_gu = (size_t)MAXT * (size_t)(g.D / 32) * kLdsBytesPerBlock;
   const size_t lds_dn = (size_t)MAXT * (size_t)(d.F / 32) * kLdsBytesPerBlock;
-  hipLaunchKernelGGL((gate_up_kernel<MAXT, kPfGateUp, TRACE>), dim3((unsigned)(g.F / 32), maxA),
+  hipLaunchKernelGGL((gate_up_kernel<MAXT, kPfGateUp, U, TRACE>), dim3((unsigned)(g.F / 32), maxA),
                      dim3(kWave), lds_gu, s, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev_down, s)) != hipSuccess) return rc;
-  hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, TRACE>),
+  hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, U, TRACE>),
                      dim3((unsigned)(d.D / 64), maxA), dim3(kWave), lds_dn, s, d);
   return hipGetLastError();
 }
@@ -441,15 +473,23 @@ int pass_tokens(int64_t T, int64_t D, int64_t F) {
   return m;
 }
 
-template <bool TRACE>
-hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, void* ev_down,
-                       hipStream_t s) {
+template <int U, bool TRACE>
+hipError_t launch_gemv_u(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, void* ev_down,
+                         hipStream_t s) {
   switch (pass_tokens(T, g.D, g.F)) {
-    case 1: return launch_pair<1, TRACE>(g, d, maxA, ev_down, s);
-    case 2: return launch_pair<2, TRACE>(g, d, maxA, ev_down, s);
-    case 4: return launch_pair<4, TRACE>(g, d, maxA, ev_down, s);
-    default: return launch_pair<8, TRACE>(g, d, maxA, ev_down, s);
+    case 1: return launch_pair<1, U, TRACE>(g, d, maxA, ev_down, s);
+    case 2: return launch_pair<2, U, TRACE>(g, d, maxA, ev_down, s);
+    case 4: return launch_pair<4, U, TRACE>(g, d, maxA, ev_down, s);
+    default: return launch_pair<8, U, TRACE>(g, d, maxA, ev_down, s);
   }
+}
+
+// U = 16-byte chunks per 32-column block: 1 for int4 tables, 2 for int8.
+template <bool TRACE>
+hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int bits, int maxA, int64_t T,
+                       void* ev_down, hipStream_t s) {
+  return bits == 8 ? launch_gemv_u<2, TRACE>(g, d, maxA, T, ev_down, s)
+                   : launch_gemv_u<1, TRACE>(g, d, maxA, T, ev_down, s);
 }
 
 }  // namespace
@@ -464,7 +504,8 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   const coli_moe_events& ev = f.events ? *f.events : no_events;
   hipError_t rc = record(ev.begin, s);
   if (rc != hipSuccess) return rc;
-  const bool grouped = T >= kMfmaMinTokens && mfma_path_fits(T, D, F, f.k, S);
+  // the grouped matrix-core kernels read int4 tables only
+  const bool grouped = t.weight_bits == 4 && T >= kMfmaMinTokens && mfma_path_fits(T, D, F, f.k, S);
   if (!f.dispatched) {
     // the GEMV path also needs the code sums of x; the grouped path does not
     rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active, ws.active, ws.err,
@@ -523,9 +564,9 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
     g.tr_u = tr->u;
     g.tr_h = tr->h;
     d.tr_pd = tr->p_down;
-    rc = launch_gemv<true>(g, d, (int)maxA, T, ev.down, s);
+    rc = launch_gemv<true>(g, d, t.weight_bits, (int)maxA, T, ev.down, s);
   } else {
-    rc = launch_gemv<false>(g, d, (int)maxA, T, ev.down, s);
+    rc = launch_gemv<false>(g, d, t.weight_bits, (int)maxA, T, ev.down, s);
   }
   }
   if (rc != hipSuccess) return rc;

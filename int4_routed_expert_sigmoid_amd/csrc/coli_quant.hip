@@ -6,9 +6,13 @@
 //  - per-row int4 weights (aitrends.kr "GLM-5.2-colibri-int4", "TL;DR" and
 //    "기술적 특징": U8-packed nibbles, per-row F32 scale, np.rint = lrintf):
 //    s = max|w| / 7, q = rint_half_even(w / s) in [-7, 7].
+//  - per-row int8 weights, the container of the int8 speculative head
+//    (discuss.pytorch.kr colibri summary, "colibri의 주요 기능", MTP bullet):
+//    s = max|w| / 127, q = rint_half_even(w / s) in [-127, 127].
 //  - RMSNorm with unit gain before Q8 (norm weights stay F32, same page,
 //    "알아두면 좋은 것").
-//  - re-laying a canonical expert container into the GEMV table layout.
+//  - re-laying a canonical expert container (int4 or int8) into the GEMV
+//    table layout.
 //
 // All of these are small, HBM-bound passes; they are written for coalesced
 // 128-bit loads and stores, not for MFMA.
@@ -81,6 +85,38 @@ __global__ void __launch_bounds__(256) quant_weight_q4_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
+// Per-row int8: one 256-thread workgroup per row, 4 columns per 32-bit word.
+__device__ __forceinline__ uint32_t q8w_code(float v, float s) {
+  if (s == 0.0f) return 0;
+  float q = __builtin_rintf(v / s);
+  q = q > 127.0f ? 127.0f : q;
+  q = q < -127.0f ? -127.0f : q;
+  return (uint32_t)(int)q & 0xFFu;
+}
+
+__global__ void __launch_bounds__(256) quant_weight_q8_kernel(const float* __restrict__ w,
+                                                              int64_t k, uint32_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float4* wr = reinterpret_cast<const float4*>(w + row * k);
+  float amax = 0.0f;
+  for (int64_t c = threadIdx.x; c < k / 4; c += 256) {
+    const float4 v = wr[c];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  amax = block_max_256(amax, red);
+  const float sc = amax / 127.0f;
+  if (threadIdx.x == 0) s[row] = sc;
+  uint32_t* qr = q + row * (k / 4);
+  for (int64_t c = threadIdx.x; c < k / 4; c += 256) {   // byte i of the word: column 4c + i
+    const float4 v = wr[c];
+    qr[c] = q8w_code(v.x, sc) | (q8w_code(v.y, sc) << 8) | (q8w_code(v.z, sc) << 16) |
+            (q8w_code(v.w, sc) << 24);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Canonical container chunk (16 bytes, 32 columns, column 2i in the low nibble
 // of byte i, two's complement) -> table chunk (word kk, byte j: column
 // 8kk+j low, 8kk+4+j high; nibble = q + 8).
@@ -103,9 +139,9 @@ __device__ __forceinline__ uint4 retile_chunk(uint4 src) {
 }
 
 struct SetExpertArgs {
-  const uint4* gate_q;  // [F][D/32] chunks
+  const uint4* gate_q;  // [F][D/32] (int4) or [F][D/16] (int8) chunks
   const uint4* up_q;
-  const uint4* down_q;  // [D][F/32] chunks
+  const uint4* down_q;  // [D][F/32] or [D][F/16] chunks
   const float* gate_s;
   const float* up_s;
   const float* down_s;
@@ -116,24 +152,30 @@ struct SetExpertArgs {
   int64_t D, F;
 };
 
+// A canonical row is a run of 16-byte chunks (32 int4 columns, or 16 int8
+// columns, each); the table puts chunk c of every lane's row side by side.
+// int4 chunks are re-encoded (retile_chunk), int8 chunks copied unchanged.
+template <int BITS>
 __global__ void __launch_bounds__(256) table_set_expert_kernel(SetExpertArgs a) {
-  const int64_t nbd = a.D / 32, nbf = a.F / 32;
-  const int64_t n_gu = (a.F / 32) * nbd * 64;   // chunks in the gate/up slot
-  const int64_t n_dn = (a.D / 64) * nbf * 64;
+  constexpr int U = BITS / 4;                       // chunks per 32-column block
+  const int64_t ncd = U * a.D / 32, ncf = U * a.F / 32;   // chunks per row
+  const int64_t n_gu = (a.F / 32) * ncd * 64;   // chunks in the gate/up slot
+  const int64_t n_dn = (a.D / 64) * ncf * 64;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_gu + n_dn; i += stride) {
     if (i < n_gu) {
-      const int64_t lane = i % 64, b = (i / 64) % nbd, g = i / (64 * nbd);
+      const int64_t lane = i % 64, c = (i / 64) % ncd, g = i / (64 * ncd);
       const int64_t row = 32 * g + (lane & 31);
-      const uint4* src = (lane < 32 ? a.gate_q : a.up_q) + row * nbd + b;
-      a.gu_q[i] = retile_chunk(*src);
-      if (b == 0) a.gu_s[g * 64 + lane] = lane < 32 ? a.gate_s[row] : a.up_s[row];
+      const uint4 src = ((lane < 32 ? a.gate_q : a.up_q) + row * ncd)[c];
+      a.gu_q[i] = BITS == 4 ? retile_chunk(src) : src;
+      if (c == 0) a.gu_s[g * 64 + lane] = lane < 32 ? a.gate_s[row] : a.up_s[row];
     } else {
       const int64_t j = i - n_gu;
-      const int64_t lane = j % 64, b = (j / 64) % nbf, g = j / (64 * nbf);
+      const int64_t lane = j % 64, c = (j / 64) % ncf, g = j / (64 * ncf);
       const int64_t row = 64 * g + lane;
-      a.dn_q[j] = retile_chunk(a.down_q[row * nbf + b]);
-      if (b == 0) a.dn_s[row] = a.down_s[row];
+      const uint4 src = a.down_q[row * ncf + c];
+      a.dn_q[j] = BITS == 4 ? retile_chunk(src) : src;
+      if (c == 0) a.dn_s[row] = a.down_s[row];
     }
   }
 }
@@ -204,6 +246,14 @@ hipError_t launch_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8
   return hipGetLastError();
 }
 
+hipError_t launch_quant_weight_q8(const float* w, int64_t rows, int64_t k, int8_t* q, float* sc,
+                                  hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_weight_q8_kernel, dim3((unsigned)rows), dim3(256), 0, s, w, k,
+                     reinterpret_cast<uint32_t*>(q), sc);
+  return hipGetLastError();
+}
+
 hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const uint8_t* gate_q,
                                    const float* gate_s, const uint8_t* up_q, const float* up_s,
                                    const uint8_t* down_q, const float* down_s, hipStream_t s) {
@@ -215,15 +265,19 @@ hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const
   a.gate_s = gate_s;
   a.up_s = up_s;
   a.down_s = down_s;
-  a.gu_q = reinterpret_cast<uint4*>(t.gu_q + (size_t)expert * (size_t)(F * D));
+  const int64_t bits = t.weight_bits;   // 4 or 8, checked by the caller
+  a.gu_q = reinterpret_cast<uint4*>(t.gu_q + (size_t)expert * (size_t)(F * D * bits / 4));
   a.gu_s = t.gu_s + (size_t)expert * (size_t)(2 * F);
-  a.dn_q = reinterpret_cast<uint4*>(t.dn_q + (size_t)expert * (size_t)(D * F / 2));
+  a.dn_q = reinterpret_cast<uint4*>(t.dn_q + (size_t)expert * (size_t)(D * F * bits / 8));
   a.dn_s = t.dn_s + (size_t)expert * (size_t)D;
   a.D = D;
   a.F = F;
-  const int64_t chunks = (F / 32) * (D / 32) * 64 + (D / 64) * (F / 32) * 64;
-  hipLaunchKernelGGL(table_set_expert_kernel, dim3((unsigned)grid_for(chunks, 256, 1 << 16)),
-                     dim3(256), 0, s, a);
+  const int64_t chunks = ((F / 32) * (D / 32) * 64 + (D / 64) * (F / 32) * 64) * (bits / 4);
+  const dim3 grid((unsigned)grid_for(chunks, 256, 1 << 16));
+  if (bits == 8)
+    hipLaunchKernelGGL(table_set_expert_kernel<8>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(table_set_expert_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

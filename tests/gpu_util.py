@@ -17,16 +17,21 @@ def stream_ptr():
     return torch.cuda.current_stream().cuda_stream
 
 
-def build_table(w: synth.Workload, layer: int = 0):
-    """Device table: device-generated fp32 weights, coli_quant_weight_q4, coli_table_set_expert."""
+def build_table(w: synth.Workload, layer: int = 0, bits: int = 4):
+    """Device table: device-generated fp32 weights, coli_quant_weight_q4 (or
+    coli_quant_weight_q8 for an int8 table), coli_table_set_expert."""
     import torch
     import int4_routed_expert_sigmoid_amd as coli
-    table = coli.ExpertTable(w.E, w.S, w.D, w.F)
+    table = coli.ExpertTable(w.E, w.S, w.D, w.F, weight_bits=bits)
     F, D = w.F, w.D
     scratch = torch.empty(F * D, dtype=torch.float32, device="cuda")
-    gq = torch.empty((F, D // 2), dtype=torch.uint8, device="cuda")
+    if bits == 4:
+        quant, qdt, per = coli.coli_quant_weight_q4, torch.uint8, 2
+    else:
+        quant, qdt, per = coli.coli_quant_weight_q8, torch.int8, 1
+    gq = torch.empty((F, D // per), dtype=qdt, device="cuda")
     uq = torch.empty_like(gq)
-    dq = torch.empty((D, F // 2), dtype=torch.uint8, device="cuda")
+    dq = torch.empty((D, F // per), dtype=qdt, device="cuda")
     gs = torch.empty(F, dtype=torch.float32, device="cuda")
     us = torch.empty_like(gs)
     ds = torch.empty(D, dtype=torch.float32, device="cuda")
@@ -35,22 +40,38 @@ def build_table(w: synth.Workload, layer: int = 0):
         for m, (q, s) in enumerate(((gq, gs), (uq, us), (dq, ds))):
             rows, cols = synth.weight_shape(w, m)
             synth.weight_device(w, layer, e, m, scratch.data_ptr(), sp)
-            coli.coli_quant_weight_q4(scratch[: rows * cols].view(rows, cols), q, s)
+            quant(scratch[: rows * cols].view(rows, cols), q, s)
         coli.coli_table_set_expert(table, e, gq, gs, uq, us, dq, ds)
     torch.cuda.synchronize()
     return table
 
 
-class OracleExperts:
-    """The oracle's int4 containers, generated on the host on first use."""
+def table_from_experts(w: synth.Workload, experts, bits: int):
+    """Device table filled from host containers (oracle.Expert, any source)."""
+    import torch
+    import int4_routed_expert_sigmoid_amd as coli
+    table = coli.ExpertTable(w.E, w.S, w.D, w.F, weight_bits=bits)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    for e in range(w.E + w.S):
+        ex = experts[e]
+        assert ex.bits == bits
+        coli.coli_table_set_expert(table, e, dev(ex.gate_q), dev(ex.gate_s), dev(ex.up_q),
+                                   dev(ex.up_s), dev(ex.down_q), dev(ex.down_s))
+    torch.cuda.synchronize()
+    return table
 
-    def __init__(self, w: synth.Workload, layer: int = 0):
-        self.w, self.layer, self.cache = w, layer, {}
+
+class OracleExperts:
+    """The oracle's containers (int4, or int8 with bits=8), generated on the
+    host on first use."""
+
+    def __init__(self, w: synth.Workload, layer: int = 0, bits: int = 4):
+        self.w, self.layer, self.bits, self.cache = w, layer, bits, {}
 
     def __getitem__(self, e: int) -> oracle.Expert:
         if e not in self.cache:
             mats = [synth.weight_host(self.w, self.layer, e, m) for m in range(3)]
-            self.cache[e] = oracle.Expert.quantize(*mats)
+            self.cache[e] = oracle.Expert.quantize(*mats, bits=self.bits)
         return self.cache[e]
 
     def table_for(self, idx) -> dict:
@@ -89,6 +110,20 @@ def decode_table_expert(w: synth.Workload, gu_q, gu_s, dn_q, dn_s, e: int):
     dcodes = chunk_codes(dn).transpose(0, 2, 1, 3).reshape(D, F)
     down_s = dn_s[e * D:(e + 1) * D]
     return gate, up, gate_s, up_s, dcodes, down_s
+
+
+def decode_table_expert8(w: synth.Workload, gu_q, gu_s, dn_q, dn_s, e: int):
+    """Test-side decoder of the documented int8 table layout (chunk c of a
+    lane = columns 16c..16c+15 of its row, bytes in column order)."""
+    D, F = w.D, w.F
+    gu = gu_q[e * 2 * F * D:(e + 1) * 2 * F * D].view(np.int8).reshape(F // 32, D // 16, 64, 16)
+    codes = gu.transpose(0, 2, 1, 3).reshape(F // 32, 64, D).astype(np.int64)
+    gate = codes[:, :32, :].reshape(F, D)
+    up = codes[:, 32:, :].reshape(F, D)
+    s = gu_s[e * 2 * F:(e + 1) * 2 * F].reshape(F // 32, 64)
+    dn = dn_q[e * D * F:(e + 1) * D * F].view(np.int8).reshape(D // 64, F // 16, 64, 16)
+    dcodes = dn.transpose(0, 2, 1, 3).reshape(D, F).astype(np.int64)
+    return gate, up, s[:, :32].reshape(F), s[:, 32:].reshape(F), dcodes, dn_s[e * D:(e + 1) * D]
 
 
 def assert_bitexact(name, got, ref):

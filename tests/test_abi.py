@@ -44,19 +44,26 @@ def test_status_strings():
 def test_table_bytes():
     L = coli.lib()
     sizes = [ctypes.c_size_t() for _ in range(4)]
-    tot = L.coli_table_bytes(256, 1, 6144, 2048, *[ctypes.byref(s) for s in sizes])
+    tot = L.coli_table_bytes(256, 1, 6144, 2048, 4, *[ctypes.byref(s) for s in sizes])
     # 257 experts x (3 * 6144 * 2048 / 2 nibble bytes + 4 * (2 * 2048 + 6144) scale bytes)
     assert tot == 257 * 18915328
     assert [s.value for s in sizes] == [257 * 6144 * 2048, 257 * 2 * 2048 * 4,
                                        257 * 6144 * 1024, 257 * 6144 * 4]
-    assert L.coli_table_bytes(256, 1, 6144 + 32, 2048, None, None, None, None) == 0  # D % 64
-    assert L.coli_table_bytes(257, 1, 6144, 2048, None, None, None, None) == 0
-    assert L.coli_table_bytes(16, 2, 256, 128, None, None, None, None) == 0
-    assert L.coli_table_bytes(16, 0, 256, 128 + 16, None, None, None, None) == 0
+    # int8 tables: one byte per weight, the same scales
+    tot = L.coli_table_bytes(256, 1, 6144, 2048, 8, *[ctypes.byref(s) for s in sizes])
+    assert [s.value for s in sizes] == [257 * 6144 * 4096, 257 * 2 * 2048 * 4,
+                                       257 * 6144 * 2048, 257 * 6144 * 4]
+    assert tot == 257 * (3 * 6144 * 2048 + 4 * (2 * 2048 + 6144))
+    assert L.coli_table_bytes(256, 1, 6144 + 32, 2048, 4, None, None, None, None) == 0  # D % 64
+    assert L.coli_table_bytes(257, 1, 6144, 2048, 4, None, None, None, None) == 0
+    assert L.coli_table_bytes(16, 2, 256, 128, 4, None, None, None, None) == 0
+    assert L.coli_table_bytes(16, 0, 256, 128 + 16, 4, None, None, None, None) == 0
+    for bits in (0, 2, 16):
+        assert L.coli_table_bytes(16, 1, 256, 128, bits, None, None, None, None) == 0
 
 
-def _table(E=16, S=1, D=256, F=128, ptr=FAKE):
-    return coli.coli_expert_table(E, S, D, F, ptr, ptr, ptr, ptr)
+def _table(E=16, S=1, D=256, F=128, ptr=FAKE, bits=4):
+    return coli.coli_expert_table(E, S, D, F, bits, ptr, ptr, ptr, ptr)
 
 
 def test_validation_quant():
@@ -67,6 +74,10 @@ def test_validation_quant():
     assert L.coli_quant_act_q8(None, 0, 32, None, None, None) == coli.COLI_OK      # no work
     assert L.coli_quant_weight_q4(FAKE, 4, 48, FAKE, FAKE, None) == coli.COLI_E_SHAPE
     assert L.coli_quant_weight_q4(FAKE, 4, 64, None, FAKE, None) == coli.COLI_E_INVAL
+    assert L.coli_quant_weight_q8(FAKE, 4, 48, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert L.coli_quant_weight_q8(FAKE, 4, 64, FAKE, None, None) == coli.COLI_E_INVAL
+    assert L.coli_quant_weight_q8(FAKE + 4, 4, 64, FAKE, FAKE, None) == coli.COLI_E_INVAL
+    assert L.coli_quant_weight_q8(None, 0, 64, None, None, None) == coli.COLI_OK
     assert L.coli_rmsnorm_q8(FAKE, 1, 40, 1e-6, FAKE, FAKE, None, None) == coli.COLI_E_SHAPE
     assert L.coli_rmsnorm_q8(FAKE, 1, 64, -1.0, FAKE, FAKE, None, None) == coli.COLI_E_INVAL
     assert L.coli_rmsnorm_q8(FAKE, 1, 64, float("nan"), FAKE, FAKE, None, None) == coli.COLI_E_INVAL
@@ -119,6 +130,8 @@ def test_validation_forward():
     assert f(*args(_table(F=48))) == coli.COLI_E_SHAPE
     assert f(*args(_table(E=300))) == coli.COLI_E_SHAPE
     assert f(*args(_table(ptr=None))) == coli.COLI_E_INVAL
+    assert f(*args(_table(bits=2))) == coli.COLI_E_SHAPE
+    assert f(*args(_table(bits=0))) == coli.COLI_E_SHAPE
     assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK          # empty batch: nothing to do
     assert L.coli_moe_forward_traced(*args(t), None) == coli.COLI_E_INVAL
     assert L.coli_moe_status(None, 64, None) == coli.COLI_E_INVAL
