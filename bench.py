@@ -189,17 +189,25 @@ def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
     }
 
 
-def head_leg(coli, synth, torch, hev, replays=4, pool=64):
-    """The int8 speculative head (its own 6144 x 2048, 256 + 1 expert layer,
-    int8 weights, 9.7 GB) at decode (1 token per pass) and in the batched
-    verify pass (4 tokens per pass, batch union): coli_moe_layer passes over a
-    pool of 64 seeded passes, graph-captured; weight GB/s counts each pass's
-    expert union once; the gate/up kernel is timed with HIP events."""
-    w2 = synth.WORKLOADS[2]
-    table = build_table(w2, coli, synth, torch, layer=HEAD_LAYER, bits=8)
-    gu_bytes, dn_bytes = expert_bytes(w2, bits=8)
+def head_leg(coli, synth, torch, hev):
+    """The int8 speculative head: its own 6144 x 2048, 256 + 1 expert layer with
+    int8 weights (9.7 GB), at decode (1 token per pass) and in the batched
+    verify pass (4 tokens per pass)."""
+    table = build_table(synth.WORKLOADS[2], coli, synth, torch, layer=HEAD_LAYER, bits=8)
     res = {"workload": "int8 head d6144 f2048 e256+1 top8", "table_bytes": table.bytes}
-    for wid in (1, 2):
+    res.update(batch_leg(table, 8, (1, 2), coli, synth, torch, hev))
+    del table
+    torch.cuda.empty_cache()
+    return res
+
+
+def batch_leg(table, bits, wids, coli, synth, torch, hev, replays=4, pool=64):
+    """Passes of T tokens (T of each workload in wids) through coli_moe_layer
+    over a pool of 64 seeded passes, graph-captured; weight GB/s counts each
+    pass's expert union once; gate/up and down are timed with HIP events."""
+    gu_bytes, dn_bytes = expert_bytes(synth.WORKLOADS[wids[0]], bits=bits)
+    res = {}
+    for wid in wids:
         w = synth.WORKLOADS[wid]
         T, P = w.T, pool
         x = torch.from_numpy(synth.activations(w, P * T, 3000)).cuda()
@@ -255,8 +263,6 @@ def head_leg(coli, synth, torch, hev, replays=4, pool=64):
             "gate_up_gbps": round(u * gu_bytes / (gu_ms * 1e-3) / 1e9, 1),
             "down_gbps": round(u * dn_bytes / (dn_ms * 1e-3) / 1e9, 1),
         }
-    del table
-    torch.cuda.empty_cache()
     return res
 
 
@@ -450,6 +456,8 @@ def main():
         out["prefill"] = [prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3),
                           prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3,
                                       bias_free=True)]
+    verify = synth.WORKLOADS[2]
+    out["verify"] = {"workload": verify.name, **batch_leg(table, 4, (2,), coli, synth, torch, hev)}
     out["router_logits"] = router_leg(coli, synth, torch)
     if not args.no_head:
         out["int8_head"] = head_leg(coli, synth, torch, hev)

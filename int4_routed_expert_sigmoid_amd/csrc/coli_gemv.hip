@@ -94,8 +94,30 @@ struct Unpacked {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// A copy into a register distinct from the source ("=&v": early clobber).
+// Taking a ring slot's words through it ends the slot's live range before the
+// slot is refilled, so the refill load can target the same registers.
+// Without it the register allocator keeps the consumed words in the slot
+// registers, sends the refill elsewhere and copies the whole ring back at the
+// loop's back-edge, which first waits for every load in flight (vmcnt(0)):
+// the ring drains once per PF chunks.  Needed for int8 slots (used as
+// loaded) and, under the register pressure of several tokens per pass, for
+// int4 slots too; the one-token int4 loop is free of it without the copy.
+__device__ __forceinline__ uint32_t fresh(uint32_t x) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=&v"(r) : "v"(x));
+  return r;
+}
+
 // int4: one chunk holds the whole block.
+template <bool COPY>
 __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
+  if (COPY) {
+    w.x = fresh(w.x);
+    w.y = fresh(w.y);
+    w.z = fresh(w.z);
+    w.w = fresh(w.w);
+  }
   Unpacked u;
   u.v[0] = w.x & 0x0F0F0F0Fu;
   u.v[1] = (w.x >> 4) & 0x0F0F0F0Fu;
@@ -111,41 +133,79 @@ __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
 // int8: two chunks, columns 0-15 and 16-31, bytes in column order.
 __device__ __forceinline__ Unpacked int8_block(u32x4 lo, u32x4 hi) {
   Unpacked u;
-  u.v[0] = lo.x;
-  u.v[1] = lo.y;
-  u.v[2] = lo.z;
-  u.v[3] = lo.w;
-  u.v[4] = hi.x;
-  u.v[5] = hi.y;
-  u.v[6] = hi.z;
-  u.v[7] = hi.w;
+  u.v[0] = fresh(lo.x);
+  u.v[1] = fresh(lo.y);
+  u.v[2] = fresh(lo.z);
+  u.v[3] = fresh(lo.w);
+  u.v[4] = fresh(hi.x);
+  u.v[5] = fresh(hi.y);
+  u.v[6] = fresh(hi.z);
+  u.v[7] = fresh(hi.w);
   return u;
 }
 
-template <int U>
+// The block in ring slots [slot, slot + U), for a loop serving NT tokens.
+template <int U, int NT>
 __device__ __forceinline__ Unpacked take_block(const u32x4* slot) {
   if constexpr (U == 1) {
-    return unpack_chunk(slot[0]);
+    return unpack_chunk<(NT > 1)>(slot[0]);
   } else {
     return int8_block(slot[0], slot[1]);
   }
 }
 
-// The token blocks of one pass live in LDS: per token, NB blocks of 32 int8
-// (xs) and per block the pair (d, -8 * sum) (dm).  One wavefront stages them
-// once, then reads them with broadcast LDS loads one block ahead of use; LDS
-// returns in order, so those waits never drain the weight ring.
-struct TokenLds {
-  uint4* xs;   // [NB][2] 16-byte halves of each block
-  float2* dm;  // [NB] (d, bitcast(-8 * sum))
+// The token blocks of one pass live in LDS, block-major: record b (R bytes)
+// holds block b's 32 int8 activations of every token slot j of the pass (at
+// 32 j), then each slot's pair (d, bitcast(-8 * sum)) (at 32 MAXT + 8 j).  So
+// one address serves every token of a block, and the blocks of an unrolled
+// ring pass sit at immediate offsets from one base: no per-token address
+// arithmetic in the loop.  One wavefront stages the records once per pass
+// (slots past the pass's token count repeat its last token), then reads them
+// with broadcast LDS loads one block ahead of use; LDS returns in order, so
+// those waits never drain the weight ring.  The records run on past the last
+// block, zero-filled, up to a whole number of ring passes plus one (the
+// read-ahead of the last block): a block past the end of the row then has
+// activations 0 and scale 0 and adds exactly +0, so the loop needs no guard.
+template <int MAXT>
+struct PassLds {
+  static constexpr int R = (40 * MAXT + 15) / 16 * 16;
+  static constexpr int DM = 32 * MAXT;
 };
 
-__device__ __forceinline__ void stage_token(TokenLds t, const int8_t* __restrict__ xrow,
+// Records of a pass over nb blocks, pb blocks per ring pass.
+constexpr int64_t pass_records(int64_t nb, int pb) { return (nb + pb - 1) / pb * pb + 1; }
+
+constexpr size_t pass_lds_bytes(int maxt, int64_t nb, int pb) {
+  return (size_t)pass_records(nb, pb) * (size_t)((40 * maxt + 15) / 16 * 16);
+}
+
+__device__ __forceinline__ unsigned char* gemv_lds() {
+  extern __shared__ __align__(16) unsigned char coli_lds[];
+  return coli_lds;
+}
+
+// Zero-fills the records past the last block (once per kernel: the passes
+// only write records 0..NB-1).
+template <int MAXT>
+__device__ __forceinline__ void clear_tail_records(int NB, int pb, int lane) {
+  constexpr int R = PassLds<MAXT>::R;
+  uint4* tail = reinterpret_cast<uint4*>(gemv_lds() + (size_t)NB * R);
+  const int n = (int)(pass_records(NB, pb) - NB) * (R / 16);
+  for (int i = lane; i < n; i += kWave) tail[i] = make_uint4(0, 0, 0, 0);
+}
+
+template <int MAXT>
+__device__ __forceinline__ void stage_token(unsigned char* lds, int j,
+                                            const int8_t* __restrict__ xrow,
                                             const float* __restrict__ drow,
                                             const int32_t* __restrict__ srow, int NB, int lane) {
+  constexpr int R = PassLds<MAXT>::R;
   const uint4* xg = reinterpret_cast<const uint4*>(xrow);
-  for (int i = lane; i < 2 * NB; i += kWave) t.xs[i] = xg[i];
-  for (int b = lane; b < NB; b += kWave) t.dm[b] = make_float2(drow[b], __int_as_float(srow[b]));
+  for (int i = lane; i < 2 * NB; i += kWave)
+    *reinterpret_cast<uint4*>(lds + (size_t)(i >> 1) * R + 32 * j + 16 * (i & 1)) = xg[i];
+  for (int b = lane; b < NB; b += kWave)
+    *reinterpret_cast<float2*>(lds + (size_t)b * R + PassLds<MAXT>::DM + 8 * j) =
+        make_float2(drow[b], __int_as_float(srow[b]));
 }
 
 struct XBlock {
@@ -153,11 +213,13 @@ struct XBlock {
   float2 dm;
 };
 
-__device__ __forceinline__ XBlock read_xblock(TokenLds t, int b) {
+// Token slot j of the block whose record starts at rec.
+template <int MAXT>
+__device__ __forceinline__ XBlock read_xblock(const unsigned char* rec, int j) {
   XBlock v;
-  v.lo = t.xs[2 * b];
-  v.hi = t.xs[2 * b + 1];
-  v.dm = t.dm[b];
+  v.lo = *reinterpret_cast<const uint4*>(rec + 32 * j);
+  v.hi = *reinterpret_cast<const uint4*>(rec + 32 * j + 16);
+  v.dm = *reinterpret_cast<const float2*>(rec + PassLds<MAXT>::DM + 8 * j);
   return v;
 }
 
@@ -204,29 +266,32 @@ struct Ring {
 // exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
 // the ring of PF weight loads in flight: every refill is unconditional (its
 // index is clamped into the row group), and a block past the end of the row
-// (only when PF / U does not divide NB) is computed on clamped data with
-// scale 0, which leaves the accumulator bit-identical (it starts at +0 and so
-// is never -0).  Buffer loads: the row group is one descriptor (scalar
+// (only when PF / U does not divide NB) is computed on clamped weights and a
+// zero record, which leaves the accumulator bit-identical (it starts at +0
+// and so is never -0).  Buffer loads: the row group is one descriptor (scalar
 // registers), the lane's 16-byte column a constant vector offset and the
 // chunk a scalar offset; each ring slot is consumed before it is refilled, so
 // the ring stays PF deep across the loop back-edge.  Weight loads are
 // non-temporal: each byte is used once.
 // A block is U consecutive chunks, so PF / U blocks are in flight.
-template <int NT, int PF, int U, bool TRACE>
-__device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok, float* acc,
+template <int NT, int MAXT, int PF, int U, bool TRACE>
+__device__ __forceinline__ void stream_rows(Ring<PF>& ring, float* acc,
                                             int32_t* const* trace_row) {
   static_assert(PF % U == 0, "the ring holds whole blocks");
   constexpr int PB = PF / U;
+  constexpr int R = PassLds<MAXT>::R;
+  const unsigned char* lds = gemv_lds();
   const int NU = ring.NU;
   const int NB = NU / U;
   XBlock cur[NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) cur[j] = read_xblock(tok[j], 0);
+  for (int j = 0; j < NT; ++j) cur[j] = read_xblock<MAXT>(lds, j);
   for (int b0 = 0; b0 < NB; b0 += PB) {
+    const unsigned char* rec = lds + (size_t)b0 * R;
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int b = b0 + i;
-      const Unpacked u = take_block<U>(&ring.buf[U * i]);
+      const Unpacked u = take_block<U, NT>(&ring.buf[U * i]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < U; ++c) {
@@ -234,10 +299,9 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok,
         ring.buf[U * i + c] = __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff,
                                                                     un * 1024, kNonTemporal);
       }
-      const int bx = b + 1 < NB ? b + 1 : NB - 1;
       XBlock nxt[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) nxt[j] = read_xblock(tok[j], bx);
+      for (int j = 0; j < NT; ++j) nxt[j] = read_xblock<MAXT>(rec + (i + 1) * R, j);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -245,8 +309,7 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok,
         if (TRACE) {
           if (trace_row[j] && b < NB) trace_row[j][b] = p;
         }
-        const float d = b < NB ? cur[j].dm.x : 0.0f;
-        acc[j] = __builtin_fmaf((float)p, d, acc[j]);
+        acc[j] = __builtin_fmaf((float)p, cur[j].dm.x, acc[j]);
         cur[j] = nxt[j];
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -254,29 +317,23 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, const TokenLds* tok,
   }
 }
 
-// Runs stream_rows for the nt (1..MAXT) tokens of one pass.
-template <int MAXT, int PF, int U, bool TRACE>
-__device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, const TokenLds* tok,
-                                            float* acc, int32_t* const* trace_row) {
-  if (MAXT >= 8 && nt > 4) {
-    stream_rows<(MAXT >= 8 ? 8 : 1), PF, U, TRACE>(ring, tok, acc, trace_row);
-  } else if (MAXT >= 4 && nt > 2) {
-    stream_rows<(MAXT >= 4 ? 4 : 1), PF, U, TRACE>(ring, tok, acc, trace_row);
-  } else if (MAXT >= 2 && nt == 2) {
-    stream_rows<(MAXT >= 2 ? 2 : 1), PF, U, TRACE>(ring, tok, acc, trace_row);
-  } else {
-    stream_rows<1, PF, U, TRACE>(ring, tok, acc, trace_row);
-  }
+// Token slots a pass of nt tokens computes: the next power of two (at most
+// MAXT); slots from nt on repeat the last token and their results are unused.
+template <int MAXT>
+__device__ __forceinline__ int pass_slots(int nt) {
+  return (MAXT >= 8 && nt > 4) ? 8 : (MAXT >= 4 && nt > 2) ? 4 : (MAXT >= 2 && nt == 2) ? 2 : 1;
 }
 
-// Dynamic LDS of a GEMV workgroup: MAXT token records of NB blocks.
-__device__ __forceinline__ TokenLds token_lds(int j, int NB) {
-  extern __shared__ __align__(16) unsigned char coli_lds[];
-  unsigned char* base = coli_lds + (size_t)j * NB * 40;
-  TokenLds t;
-  t.xs = reinterpret_cast<uint4*>(base);
-  t.dm = reinterpret_cast<float2*>(base + (size_t)NB * 32);
-  return t;
+// Runs stream_rows for the nt (1..MAXT) tokens of one pass.
+template <int MAXT, int PF, int U, bool TRACE>
+__device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
+                                            int32_t* const* trace_row) {
+  switch (pass_slots<MAXT>(nt)) {
+    case 8: stream_rows<(MAXT >= 8 ? 8 : 1), MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
+    case 4: stream_rows<(MAXT >= 4 ? 4 : 1), MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
+    case 2: stream_rows<(MAXT >= 2 ? 2 : 1), MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
+    default: stream_rows<1, MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
+  }
 }
 
 template <int MAXT, int PF, int U, bool TRACE>
@@ -295,13 +352,14 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
+  clear_tail_records<MAXT>(NB, PF / U, lane);
   const int cnt = as_const(a.counts)[e];
   const float rs = a.gu_s[((size_t)e * G + grp) * kWave + lane];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
   for (int c0 = 0; c0 < cnt; c0 += MAXT) {
     const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
+    const int ns = pass_slots<MAXT>(nt);
     int pair[MAXT];
-    TokenLds tok[MAXT];
     int32_t* trow[MAXT];
     if (c0 > 0) {
       __syncthreads();                // the previous pass has finished reading the LDS records
@@ -310,22 +368,25 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       pair[j] = list[c0 + (j < nt ? j : nt - 1)];
-      tok[j] = token_lds(j < nt ? j : nt - 1, NB);
       trow[j] = nullptr;
       if (TRACE) {
         int32_t* base = lane < 32 ? a.tr_pg : a.tr_pu;
         if (base) trow[j] = base + ((size_t)pair[j] * a.F + 32 * (size_t)grp + (lane & 31)) * NB;
       }
     }
-    for (int j = 0; j < nt; ++j) {
-      const int64_t t = __builtin_amdgcn_readfirstlane(pair[j] / KS);
-      stage_token(tok[j], a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB, lane);
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      if (j < ns) {
+        const int64_t t = __builtin_amdgcn_readfirstlane(pair[j] / KS);
+        stage_token<MAXT>(gemv_lds(), j, a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB,
+                          lane);
+      }
     }
     __syncthreads();
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, U, TRACE>(nt, ring, tok, acc, trow);
+    stream_pass<MAXT, PF, U, TRACE>(nt, ring, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       if (j < nt) {
@@ -391,14 +452,15 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
+  clear_tail_records<MAXT>(NB, PF / U, lane);
   const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
   const float rs = a.dn_s[(size_t)e * a.D + row];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
   for (int c0 = 0; c0 < cnt; c0 += MAXT) {
     const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
+    const int ns = pass_slots<MAXT>(nt);
     int pair[MAXT];
-    TokenLds tok[MAXT];
     int32_t* trow[MAXT];
     if (c0 > 0) {
       __syncthreads();
@@ -407,18 +469,21 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       pair[j] = list[c0 + (j < nt ? j : nt - 1)];
-      tok[j] = token_lds(j < nt ? j : nt - 1, NB);
       trow[j] = (TRACE && a.tr_pd) ? a.tr_pd + ((size_t)pair[j] * a.D + row) * NB : nullptr;
     }
-    for (int j = 0; j < nt; ++j) {
-      const size_t p = (size_t)__builtin_amdgcn_readfirstlane(pair[j]);
-      stage_token(tok[j], a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB, lane);
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      if (j < ns) {
+        const size_t p = (size_t)__builtin_amdgcn_readfirstlane(pair[j]);
+        stage_token<MAXT>(gemv_lds(), j, a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB,
+                          lane);
+      }
     }
     __syncthreads();
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, U, TRACE>(nt, ring, tok, acc, trow);
+    stream_pass<MAXT, PF, U, TRACE>(nt, ring, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j)
       if (j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
@@ -445,38 +510,42 @@ hipError_t record(void* ev, hipStream_t s) {
   return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
 }
 
-constexpr int kPfGateUp = 16;       // weight loads in flight per wavefront
-constexpr int kPfDown = 8;
-constexpr int kLdsBytesPerBlock = 40;
+// Weight loads (1 KB per wavefront) in flight per wavefront, by tokens per
+// pass and 16-byte chunks per block.
+constexpr int pf_gate_up(int maxt, int u) { return maxt > 0 && u > 0 ? 16 : 0; }
+constexpr int pf_down(int maxt, int u) { return maxt > 0 && u > 0 ? 8 : 0; }
 constexpr size_t kLdsLimit = 65536;
 
 template <int MAXT, int U, bool TRACE>
 hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
-  const size_t lds_gu = (size_t)MAXT * (size_t)(g.D / 32) * kLdsBytesPerBlock;
-  const size_t lds_dn = (size_t)MAXT * (size_t)(d.F / 32) * kLdsBytesPerBlock;
-  hipLaunchKernelGGL((gate_up_kernel<MAXT, kPfGateUp, U, TRACE>), dim3((unsigned)(g.F / 32), maxA),
+  const size_t lds_gu = pass_lds_bytes(MAXT, g.D / 32, pf_gate_up(MAXT, U) / U);
+  const size_t lds_dn = pass_lds_bytes(MAXT, d.F / 32, pf_down(MAXT, U) / U);
+  hipLaunchKernelGGL((gate_up_kernel<MAXT, pf_gate_up(MAXT, U), U, TRACE>), dim3((unsigned)(g.F / 32), maxA),
                      dim3(kWave), lds_gu, s, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev_down, s)) != hipSuccess) return rc;
-  hipLaunchKernelGGL((down_kernel<MAXT, kPfDown, U, TRACE>),
+  hipLaunchKernelGGL((down_kernel<MAXT, pf_down(MAXT, U), U, TRACE>),
                      dim3((unsigned)(d.D / 64), maxA), dim3(kWave), lds_dn, s, d);
   return hipGetLastError();
 }
 
 // Tokens per pass: the batch (a power of two up to 8), capped so that the
-// pass's LDS token records fit in 64 KB.
-int pass_tokens(int64_t T, int64_t D, int64_t F) {
-  const int64_t nb = (D > F ? D : F) / 32;
+// pass's LDS token records fit in 64 KB in both kernels.
+int pass_tokens(int64_t T, int64_t D, int64_t F, int U) {
   int m = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
-  while (m > 1 && (size_t)m * nb * kLdsBytesPerBlock > kLdsLimit) m /= 2;
+  auto fits = [&](int mt) {
+    return pass_lds_bytes(mt, D / 32, pf_gate_up(mt, U) / U) <= kLdsLimit &&
+           pass_lds_bytes(mt, F / 32, pf_down(mt, U) / U) <= kLdsLimit;
+  };
+  while (m > 1 && !fits(m)) m /= 2;
   return m;
 }
 
 template <int U, bool TRACE>
 hipError_t launch_gemv_u(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, void* ev_down,
                          hipStream_t s) {
-  switch (pass_tokens(T, g.D, g.F)) {
+  switch (pass_tokens(T, g.D, g.F, U)) {
     case 1: return launch_pair<1, U, TRACE>(g, d, maxA, ev_down, s);
     case 2: return launch_pair<2, U, TRACE>(g, d, maxA, ev_down, s);
     case 4: return launch_pair<4, U, TRACE>(g, d, maxA, ev_down, s);
