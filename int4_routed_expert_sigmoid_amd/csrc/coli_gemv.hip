@@ -109,16 +109,30 @@ __device__ __forceinline__ uint32_t fresh(uint32_t x) {
   return r;
 }
 
+// lo = w & 0x0F0F0F0F and t = w >> 4, both into registers distinct from w:
+// the split ends w's live range the way fresh() does, without extra moves.
+__device__ __forceinline__ void split_nibbles(uint32_t w, uint32_t& lo, uint32_t& t) {
+  asm volatile("v_and_b32 %0, 0xf0f0f0f, %2\n\tv_lshrrev_b32 %1, 4, %2"
+               : "=&v"(lo), "=&v"(t)
+               : "v"(w));
+}
+
 // int4: one chunk holds the whole block.
 template <bool COPY>
 __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
-  if (COPY) {
-    w.x = fresh(w.x);
-    w.y = fresh(w.y);
-    w.z = fresh(w.z);
-    w.w = fresh(w.w);
-  }
   Unpacked u;
+  if (COPY) {
+    uint32_t t[4];
+    split_nibbles(w.x, u.v[0], t[0]);
+    split_nibbles(w.y, u.v[2], t[1]);
+    split_nibbles(w.z, u.v[4], t[2]);
+    split_nibbles(w.w, u.v[6], t[3]);
+    u.v[1] = t[0] & 0x0F0F0F0Fu;
+    u.v[3] = t[1] & 0x0F0F0F0Fu;
+    u.v[5] = t[2] & 0x0F0F0F0Fu;
+    u.v[7] = t[3] & 0x0F0F0F0Fu;
+    return u;
+  }
   u.v[0] = w.x & 0x0F0F0F0Fu;
   u.v[1] = (w.x >> 4) & 0x0F0F0F0Fu;
   u.v[2] = w.y & 0x0F0F0F0Fu;
@@ -133,14 +147,14 @@ __device__ __forceinline__ Unpacked unpack_chunk(u32x4 w) {
 // int8: two chunks, columns 0-15 and 16-31, bytes in column order.
 __device__ __forceinline__ Unpacked int8_block(u32x4 lo, u32x4 hi) {
   Unpacked u;
-  u.v[0] = fresh(lo.x);
-  u.v[1] = fresh(lo.y);
-  u.v[2] = fresh(lo.z);
-  u.v[3] = fresh(lo.w);
-  u.v[4] = fresh(hi.x);
-  u.v[5] = fresh(hi.y);
-  u.v[6] = fresh(hi.z);
-  u.v[7] = fresh(hi.w);
+  u.v[0] = lo.x;
+  u.v[1] = lo.y;
+  u.v[2] = lo.z;
+  u.v[3] = lo.w;
+  u.v[4] = hi.x;
+  u.v[5] = hi.y;
+  u.v[6] = hi.z;
+  u.v[7] = hi.w;
   return u;
 }
 
@@ -185,25 +199,26 @@ __device__ __forceinline__ unsigned char* gemv_lds() {
 }
 
 // Zero-fills the records past the last block (once per kernel: the passes
-// only write records 0..NB-1).
+// only write records 0..NB-1).  Threads tid of nth of the workgroup.
 template <int MAXT>
-__device__ __forceinline__ void clear_tail_records(int NB, int pb, int lane) {
+__device__ __forceinline__ void clear_tail_records(int NB, int pb, int tid, int nth) {
   constexpr int R = PassLds<MAXT>::R;
   uint4* tail = reinterpret_cast<uint4*>(gemv_lds() + (size_t)NB * R);
   const int n = (int)(pass_records(NB, pb) - NB) * (R / 16);
-  for (int i = lane; i < n; i += kWave) tail[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < n; i += nth) tail[i] = make_uint4(0, 0, 0, 0);
 }
 
 template <int MAXT>
 __device__ __forceinline__ void stage_token(unsigned char* lds, int j,
                                             const int8_t* __restrict__ xrow,
                                             const float* __restrict__ drow,
-                                            const int32_t* __restrict__ srow, int NB, int lane) {
+                                            const int32_t* __restrict__ srow, int NB, int tid,
+                                            int nth) {
   constexpr int R = PassLds<MAXT>::R;
   const uint4* xg = reinterpret_cast<const uint4*>(xrow);
-  for (int i = lane; i < 2 * NB; i += kWave)
+  for (int i = tid; i < 2 * NB; i += nth)
     *reinterpret_cast<uint4*>(lds + (size_t)(i >> 1) * R + 32 * j + 16 * (i & 1)) = xg[i];
-  for (int b = lane; b < NB; b += kWave)
+  for (int b = tid; b < NB; b += nth)
     *reinterpret_cast<float2*>(lds + (size_t)b * R + PassLds<MAXT>::DM + 8 * j) =
         make_float2(drow[b], __int_as_float(srow[b]));
 }
@@ -262,6 +277,19 @@ struct Ring {
   }
 };
 
+// Refills the U slots of ring position i (block b) with the chunks of block
+// b + PB, clamped into the row group.
+template <int PF, int U, int PB>
+__device__ __forceinline__ void refill(Ring<PF>& ring, int b, int i) {
+  const int NU = ring.NU;
+#pragma unroll
+  for (int c = 0; c < U; ++c) {
+    const int un = U * (b + PB) + c < NU ? U * (b + PB) + c : NU - 1;
+    ring.buf[U * i + c] =
+        __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff, un * 1024, kNonTemporal);
+  }
+}
+
 // Streams the NB blocks of one row group (lane-owned rows) and accumulates
 // exactly NT tokens.  The body is branch-free so the waitcnt pass can keep
 // the ring of PF weight loads in flight: every refill is unconditional (its
@@ -293,12 +321,10 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, float* acc,
       const int b = b0 + i;
       const Unpacked u = take_block<U, NT>(&ring.buf[U * i]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = 0; c < U; ++c) {
-        const int un = U * (b + PB) + c < NU ? U * (b + PB) + c : NU - 1;
-        ring.buf[U * i + c] = __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff,
-                                                                    un * 1024, kNonTemporal);
-      }
+      // int4 slots are refilled as soon as they are unpacked; int8 slots feed
+      // the dots as loaded, so they are refilled after the block's dots (the
+      // load can then reuse the slot's registers).
+      if constexpr (U == 1) refill<PF, U, PB>(ring, b, i);
       XBlock nxt[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j) nxt[j] = read_xblock<MAXT>(rec + (i + 1) * R, j);
@@ -313,6 +339,10 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, float* acc,
         cur[j] = nxt[j];
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (U == 2) {
+        refill<PF, U, PB>(ring, b, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -336,23 +366,34 @@ __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
   }
 }
 
+// A workgroup is W wavefronts on W consecutive row groups of one expert:
+// they share one copy of the pass's token records, so a pass needs 1 / W of
+// the LDS per wavefront (the 4- and 8-token records would otherwise cap the
+// resident workgroups per CU below the wavefronts the chip can hold).  A
+// trailing wavefront without a row group of its own recomputes the last one
+// and stores nothing.
+constexpr int gemv_waves(int maxt) { return maxt >= 4 ? 2 : 1; }
+
 template <int MAXT, int PF, int U, bool TRACE>
-__global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
-  const int grp = blockIdx.x;
+__global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a) {
+  constexpr int W = gemv_waves(MAXT);
   const int slot = blockIdx.y;
   const int n_active = *as_const(a.n_active);   // both loads in flight together;
   const int e = as_const(a.active)[slot];        // e is used only once slot is valid
   if (slot >= n_active) return;
-  const int lane = threadIdx.x;
+  const int wave = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave) : 0;
+  const int lane = (int)threadIdx.x % kWave;
   const int NB = (int)(a.D / 32);
   const int64_t G = a.F / 32;
+  const bool live = (int64_t)blockIdx.x * W + wave < G;
+  const int grp = live ? (int)blockIdx.x * W + wave : (int)G - 1;
   const int KS = a.k + a.S;
   const int NU = U * NB;                 // 1 KB chunks in the row group
   const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)e * G + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
-  clear_tail_records<MAXT>(NB, PF / U, lane);
+  clear_tail_records<MAXT>(NB, PF / U, threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const float rs = a.gu_s[((size_t)e * G + grp) * kWave + lane];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
@@ -371,7 +412,8 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
       trow[j] = nullptr;
       if (TRACE) {
         int32_t* base = lane < 32 ? a.tr_pg : a.tr_pu;
-        if (base) trow[j] = base + ((size_t)pair[j] * a.F + 32 * (size_t)grp + (lane & 31)) * NB;
+        if (base && live)
+          trow[j] = base + ((size_t)pair[j] * a.F + 32 * (size_t)grp + (lane & 31)) * NB;
       }
     }
 #pragma unroll
@@ -379,7 +421,7 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
       if (j < ns) {
         const int64_t t = __builtin_amdgcn_readfirstlane(pair[j] / KS);
         stage_token<MAXT>(gemv_lds(), j, a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB,
-                          lane);
+                          threadIdx.x, kWave * W);
       }
     }
     __syncthreads();
@@ -402,7 +444,7 @@ __global__ void __launch_bounds__(64) gate_up_kernel(GuArgs a) {
 #pragma unroll
         for (int off = 16; off >= 1; off >>= 1) qs += __shfl_xor(qs, off, 32);
         const size_t p = (size_t)pair[j];
-        if (lane < 32) {
+        if (live && lane < 32) {
           const size_t r = 32 * (size_t)grp + lane;
           a.hq[p * a.F + r] = (int8_t)q;
           if (lane == 0) {
@@ -438,13 +480,17 @@ __device__ __forceinline__ float combine_row(const float* __restrict__ o,
 }
 
 template <int MAXT, int PF, int U, bool TRACE>
-__global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
-  const int grp = blockIdx.x;
+__global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
+  constexpr int W = gemv_waves(MAXT);
   const int slot = blockIdx.y;
   const int n_active = *as_const(a.n_active);   // both loads in flight together;
   const int e = as_const(a.active)[slot];        // e is used only once slot is valid
   if (slot >= n_active) return;
-  const int lane = threadIdx.x;
+  const int wave = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave) : 0;
+  const int lane = (int)threadIdx.x % kWave;
+  const int64_t G = a.D / 64;
+  const bool live = (int64_t)blockIdx.x * W + wave < G;
+  const int grp = live ? (int)blockIdx.x * W + wave : (int)G - 1;
   const int NB = (int)(a.F / 32);
   const int NU = U * NB;
   const char* wbase =
@@ -452,7 +498,7 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
-  clear_tail_records<MAXT>(NB, PF / U, lane);
+  clear_tail_records<MAXT>(NB, PF / U, threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
   const float rs = a.dn_s[(size_t)e * a.D + row];
@@ -469,14 +515,14 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       pair[j] = list[c0 + (j < nt ? j : nt - 1)];
-      trow[j] = (TRACE && a.tr_pd) ? a.tr_pd + ((size_t)pair[j] * a.D + row) * NB : nullptr;
+      trow[j] = (TRACE && a.tr_pd && live) ? a.tr_pd + ((size_t)pair[j] * a.D + row) * NB : nullptr;
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       if (j < ns) {
         const size_t p = (size_t)__builtin_amdgcn_readfirstlane(pair[j]);
         stage_token<MAXT>(gemv_lds(), j, a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB,
-                          lane);
+                          threadIdx.x, kWave * W);
       }
     }
     __syncthreads();
@@ -486,7 +532,7 @@ __global__ void __launch_bounds__(64) down_kernel(DnArgs a) {
     stream_pass<MAXT, PF, U, TRACE>(nt, ring, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j)
-      if (j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
+      if (live && j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
   }
 }
 
@@ -520,13 +566,14 @@ template <int MAXT, int U, bool TRACE>
 hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
   const size_t lds_gu = pass_lds_bytes(MAXT, g.D / 32, pf_gate_up(MAXT, U) / U);
   const size_t lds_dn = pass_lds_bytes(MAXT, d.F / 32, pf_down(MAXT, U) / U);
-  hipLaunchKernelGGL((gate_up_kernel<MAXT, pf_gate_up(MAXT, U), U, TRACE>), dim3((unsigned)(g.F / 32), maxA),
-                     dim3(kWave), lds_gu, s, g);
+  constexpr int W = gemv_waves(MAXT);
+  hipLaunchKernelGGL((gate_up_kernel<MAXT, pf_gate_up(MAXT, U), U, TRACE>),
+                     dim3((unsigned)((g.F / 32 + W - 1) / W), maxA), dim3(kWave * W), lds_gu, s, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev_down, s)) != hipSuccess) return rc;
   hipLaunchKernelGGL((down_kernel<MAXT, pf_down(MAXT, U), U, TRACE>),
-                     dim3((unsigned)(d.D / 64), maxA), dim3(kWave), lds_dn, s, d);
+                     dim3((unsigned)((d.D / 64 + W - 1) / W), maxA), dim3(kWave * W), lds_dn, s, d);
   return hipGetLastError();
 }
 
