@@ -372,7 +372,7 @@ __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
 // resident workgroups per CU below the wavefronts the chip can hold).  A
 // trailing wavefront without a row group of its own recomputes the last one
 // and stores nothing.
-constexpr int gemv_waves(int maxt) { return maxt >= 4 ? 2 : 1; }
+constexpr int gemv_waves(int maxt) { return maxt >= 4 ? 4 : 1; }
 
 template <int MAXT, int PF, int U, bool TRACE>
 __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a) {
