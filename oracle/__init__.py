@@ -46,6 +46,10 @@ _SIG = {
     "orc_rmsnorm": ([_P, _I64, _I64, _F, _P, _P], None),
     "orc_router_logits": ([_P, _P, _I64, _I64, _I32, _P], None),
     "orc_dispatch": ([_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "orc_tier_init": ([_I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "orc_tier_plan": ([_I32, _I32, _I32, _P, _I64, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _P,
+                       _P, _P, _P], ctypes.c_int),
+    "orc_tier_pin_top": ([_I32, _P, _I32, _P], None),
 }
 
 
@@ -320,6 +324,50 @@ class Oracle:
         r = np.empty(T, dtype=np.float32)
         self.L.orc_rmsnorm(_ptr(h), T, D, eps, _ptr(out), _ptr(r))
         return out, r
+
+
+class Tier:
+    """The oracle's expert tier of one layer (state in numpy arrays)."""
+
+    def __init__(self, orc, E, S, slots, pin=()):
+        self.orc, self.E, self.S, self.slots = orc, E, S, slots
+        self.slot_of = np.empty(E + S, np.int32)
+        self.expert_in = np.empty(slots, np.int32)
+        self.stamp = np.empty(slots, np.int32)
+        self.pinned = np.empty(slots, np.int32)
+        self.usage = np.empty(E + S, np.int32)
+        self.step = 0
+        pin = _c(np.asarray(pin, np.int32), np.int32)
+        loads = np.empty(slots, np.int32)
+        n = np.zeros(1, np.int32)
+        rc = orc.L.orc_tier_init(E, S, slots, _ptr(pin), pin.size, _ptr(self.slot_of),
+                                 _ptr(self.expert_in), _ptr(self.stamp), _ptr(self.pinned),
+                                 _ptr(self.usage), _ptr(loads), _ptr(n))
+        if rc != 0:
+            raise ValueError("orc_tier_init rejected the pin list")
+        self.init_loads = loads[: int(n[0])].copy()
+
+    def plan(self, idx, count_usage=True):
+        """One pass: returns (loads: slots to fill in order, hits)."""
+        idx = _c(idx, np.int32)
+        T, k = idx.shape
+        loads = np.empty(self.slots, np.int32)
+        n = np.zeros(1, np.int32)
+        hits = np.zeros(1, np.int32)
+        rc = self.orc.L.orc_tier_plan(self.E, self.S, self.slots, _ptr(idx), T, k, self.step,
+                                      int(bool(count_usage)), _ptr(self.slot_of),
+                                      _ptr(self.expert_in), _ptr(self.stamp), _ptr(self.pinned),
+                                      _ptr(self.usage), _ptr(loads), _ptr(n), _ptr(hits))
+        if rc != 0:
+            raise ValueError("orc_tier_plan: invalid index or not enough slots")
+        self.step += 1
+        return loads[: int(n[0])].copy(), int(hits[0])
+
+    def pin_top(self, n):
+        out = np.empty(n, np.int32)
+        u = _c(self.usage, np.int32)
+        self.orc.L.orc_tier_pin_top(self.E, _ptr(u), n, _ptr(out))
+        return out
 
 
 _default = None

@@ -412,3 +412,102 @@ int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
   *n_active = na;
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Expert tier of one layer.  The pages keep the routed experts out of the
+ * fast memory and cache them per layer: an LRU cache per layer, a pinned
+ * hot store for the most used experts, and a usage log from which the next
+ * run pins the most frequently selected experts (discuss.pytorch.kr colibri
+ * summary, "colibri의 핵심 아이디어"; jeff.news, the idea section).  Here
+ * the fast memory is `slots` expert slots and the policy is, in full:
+ *
+ *  - init: the shared expert (S = 1) takes slot 0, then the pinned experts
+ *    take slots 1, 2, ... in the order given; those slots are pinned and are
+ *    never evicted; each of them is a load.  Other slots start empty.
+ *  - plan (one per pass, `step` counting the plans of this layer): the
+ *    needed set is every expert some token selected plus the shared expert.
+ *    A needed expert already in a slot is a hit and that slot's stamp
+ *    becomes `step`.  Then the missing experts, in ascending id, each take
+ *    the unpinned slot not used by this pass (stamp < step) with the
+ *    smallest stamp, the lower slot on equal stamps (empty slots have stamp
+ *    -1, so they go first); the evicted expert leaves the tier; the slot is
+ *    a load.  With count_usage, usage[e] grows by the number of tokens that
+ *    selected e (the shared expert: every token).
+ *  - pin_top: the n routed experts with the largest usage, the lower id on
+ *    equal counts, in that order.
+ *
+ * Returns 0, or -1 if an index is invalid or the needed set does not fit in
+ * the unpinned slots together with the pinned hits.
+ */
+int orc_tier_init(int32_t E, int32_t S, int32_t slots, const int32_t* pin, int32_t n_pin,
+                  int32_t* slot_of, int32_t* expert_in, int32_t* stamp, int32_t* pinned,
+                  int32_t* usage, int32_t* loads, int32_t* n_loads) {
+  if (S + n_pin > slots) return -1;
+  for (int32_t e = 0; e < E + S; ++e) { slot_of[e] = -1; usage[e] = 0; }
+  for (int32_t s = 0; s < slots; ++s) { expert_in[s] = -1; stamp[s] = -1; pinned[s] = 0; }
+  int32_t n = 0;
+  for (int32_t i = -S; i < n_pin; ++i) {
+    const int32_t e = i < 0 ? E : pin[i];
+    if (e < 0 || e >= E + S || slot_of[e] >= 0) return -1;
+    slot_of[e] = n;
+    expert_in[n] = e;
+    pinned[n] = 1;
+    loads[n] = n;
+    ++n;
+  }
+  *n_loads = n;
+  return 0;
+}
+
+int orc_tier_plan(int32_t E, int32_t S, int32_t slots, const int32_t* idx, int64_t T, int32_t k,
+                  int32_t step, int count_usage, int32_t* slot_of, int32_t* expert_in,
+                  int32_t* stamp, const int32_t* pinned, int32_t* usage, int32_t* loads,
+                  int32_t* n_loads, int32_t* hits) {
+  int32_t* count = (int32_t*)calloc((size_t)(E + S), sizeof(int32_t));
+  int rc = 0;
+  for (int64_t i = 0; i < T * k; ++i) {
+    if (idx[i] < 0 || idx[i] >= E) { rc = -1; break; }
+    count[idx[i]] += 1;
+  }
+  if (S) count[E] = (int32_t)T;
+  int32_t nh = 0, nl = 0;
+  for (int32_t e = 0; e < E + S && rc == 0; ++e) {     /* hits */
+    if (count[e] == 0 || slot_of[e] < 0) continue;
+    stamp[slot_of[e]] = step;
+    ++nh;
+  }
+  for (int32_t e = 0; e < E + S && rc == 0; ++e) {     /* misses, ascending id */
+    if (count[e] == 0 || slot_of[e] >= 0) continue;
+    int32_t v = -1;
+    for (int32_t s = 0; s < slots; ++s) {
+      if (pinned[s] || stamp[s] >= step) continue;
+      if (v < 0 || stamp[s] < stamp[v]) v = s;
+    }
+    if (v < 0) { rc = -1; break; }
+    if (expert_in[v] >= 0) slot_of[expert_in[v]] = -1;
+    expert_in[v] = e;
+    slot_of[e] = v;
+    stamp[v] = step;
+    loads[nl++] = v;
+  }
+  if (rc == 0 && count_usage)
+    for (int32_t e = 0; e < E + S; ++e) usage[e] += count[e];
+  *n_loads = nl;
+  *hits = nh;
+  free(count);
+  return rc;
+}
+
+void orc_tier_pin_top(int32_t E, const int32_t* usage, int32_t n, int32_t* out) {
+  char* taken = (char*)calloc((size_t)E, 1);
+  for (int32_t i = 0; i < n && i < E; ++i) {
+    int32_t best = -1;
+    for (int32_t e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || usage[e] > usage[best]) best = e;
+    }
+    taken[best] = 1;
+    out[i] = best;
+  }
+  free(taken);
+}

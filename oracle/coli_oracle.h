@@ -103,6 +103,21 @@ void orc_router_logits(const float* x, const float* wr, int64_t T, int64_t D, in
 int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
                  int32_t* counts, int32_t* lists, int32_t* n_active, int32_t* active);
 
+/* Expert tier of one layer (per-layer LRU + pinned hot store + usage
+ * counts; the full policy is stated in coli_oracle.c).  State arrays:
+ * slot_of[E+S] (slot or -1), expert_in[slots] (expert or -1), stamp[slots]
+ * (plan step of last use, -1 never), pinned[slots] (0/1), usage[E+S].
+ * loads[] receives the slots to fill, in order.  Return 0 or -1. */
+int orc_tier_init(int32_t E, int32_t S, int32_t slots, const int32_t* pin, int32_t n_pin,
+                  int32_t* slot_of, int32_t* expert_in, int32_t* stamp, int32_t* pinned,
+                  int32_t* usage, int32_t* loads, int32_t* n_loads);
+int orc_tier_plan(int32_t E, int32_t S, int32_t slots, const int32_t* idx, int64_t T, int32_t k,
+                  int32_t step, int count_usage, int32_t* slot_of, int32_t* expert_in,
+                  int32_t* stamp, const int32_t* pinned, int32_t* usage, int32_t* loads,
+                  int32_t* n_loads, int32_t* hits);
+/* The n most used routed experts (ties to the lower id), in that order. */
+void orc_tier_pin_top(int32_t E, const int32_t* usage, int32_t n, int32_t* out);
+
 #ifdef __cplusplus
 }
 #endif

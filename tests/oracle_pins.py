@@ -513,6 +513,92 @@ def pin_int8_container(orc):
     assert np.array_equal(y4, y8), "container identity: layer output"
 
 
+def _lru_reference(refs, capacity):
+    """Textbook LRU over single references: a recency list, most recent last.
+    Returns the hit flags and the resident set after each reference."""
+    recency, hits, sets = [], [], []
+    for r in refs:
+        if r in recency:
+            recency.remove(r)
+            hits.append(True)
+        else:
+            if len(recency) == capacity:
+                recency.pop(0)
+            hits.append(False)
+        recency.append(r)
+        sets.append(set(recency))
+    return hits, sets
+
+
+def pin_tier(orc):
+    """Expert tier: a hand-worked LRU sequence (slots and loads written out),
+    an independent recency-list LRU on one-expert passes, the LRU inclusion
+    property, invariants with several experts per pass, pinned and shared
+    experts, usage counts, and the pin ranking against Python's sorted."""
+    from oracle import Tier
+    # hand-worked: capacity 3, references 0 1 2 0 3 0 4 2 3 0 (one token, k = 1, no shared)
+    t = Tier(orc, 8, 0, 3)
+    refs = [0, 1, 2, 0, 3, 0, 4, 2, 3, 0]
+    want_loads = [[0], [1], [2], [], [1], [], [2], [1], [0], [2]]
+    got = [t.plan(np.array([[r]], np.int32)) for r in refs]
+    assert [list(l) for l, _ in got] == want_loads, [list(l) for l, _ in got]
+    assert [h for _, h in got] == [0, 0, 0, 1, 0, 1, 0, 0, 0, 0]
+    assert t.expert_in.tolist() == [3, 2, 0] and t.slot_of[[0, 2, 3]].tolist() == [2, 1, 0]
+    assert np.all(t.slot_of[[1, 4, 5, 6, 7]] == -1)
+    # one expert per pass: identical to the recency-list LRU; hits grow with capacity
+    rng = np.random.default_rng(41)
+    p = 1.0 / np.arange(1, 33) ** 1.1
+    refs = rng.choice(32, size=400, p=p / p.sum())
+    prev = None
+    for cap in (2, 5, 9, 16):
+        t = Tier(orc, 32, 0, cap)
+        hits = [t.plan(np.array([[r]], np.int32))[1] == 1 for r in refs]
+        ref_hits, _ = _lru_reference(list(refs), cap)
+        assert hits == ref_hits, f"LRU hits differ at capacity {cap}"
+        resident = set(int(e) for e in t.expert_in if e >= 0)
+        assert resident == _lru_reference(list(refs), cap)[1][-1]
+        if prev is not None:
+            assert all(h or not ph for h, ph in zip(hits, prev)), "LRU inclusion"
+        prev = hits
+    # several experts per pass, a shared expert and pinned experts
+    E, S, k, T, slots = 16, 1, 2, 3, 12
+    pin = [5, 2]
+    t = Tier(orc, E, S, slots, pin)
+    assert t.init_loads.tolist() == [0, 1, 2] and t.expert_in[:3].tolist() == [E, 5, 2]
+    usage = np.zeros(E + S, np.int64)
+    for step in range(60):
+        idx = np.stack([rng.choice(E, k, replace=False, p=None) for _ in range(T)]).astype(np.int32)
+        before = t.expert_in.copy()
+        loads, hits = t.plan(idx)
+        need = set(idx.reshape(-1).tolist()) | {E}
+        assert hits + len(loads) == len(need)
+        assert hits == len(need & set(int(e) for e in before if e >= 0))
+        assert all(t.slot_of[e] >= 0 and t.expert_in[t.slot_of[e]] == e for e in need)
+        assert t.expert_in[:3].tolist() == [E, 5, 2], "pinned slots evicted"
+        assert len(set(loads.tolist())) == len(loads) and all(t.pinned[s] == 0 for s in loads)
+        assert all(t.stamp[t.slot_of[e]] == step for e in need)
+        np.add.at(usage, idx.reshape(-1), 1)
+        usage[E] += T
+    assert np.array_equal(t.usage, usage), "usage counts"
+    # a prefetch plan moves experts in without counting usage
+    u0 = t.usage.copy()
+    t.plan(np.array([[0, 1]], np.int32), count_usage=False)
+    assert np.array_equal(t.usage, u0)
+    # too many experts for the unpinned slots
+    t = Tier(orc, 16, 1, 4, [3])
+    try:
+        t.plan(np.array([[0, 1], [2, 4]], np.int32))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("tier accepted more experts than slots")
+    # pin ranking
+    u = rng.integers(0, 5, size=40).astype(np.int32)
+    t = Tier(orc, 40, 0, 4)
+    t.usage[:] = u
+    assert t.pin_top(12).tolist() == sorted(range(40), key=lambda e: (-int(u[e]), e))[:12]
+
+
 ALL_PINS = [pin_nibble_codec, pin_rint_ties, pin_quant_closed_forms, pin_partials_bruteforce,
             pin_dot_fp64, pin_exp, pin_route, pin_expert_fp64, pin_moe_invariants, pin_rmsnorm,
-            pin_dispatch, pin_router_logits, pin_int8_quant, pin_int8_container]
+            pin_dispatch, pin_router_logits, pin_int8_quant, pin_int8_container, pin_tier]

@@ -64,6 +64,16 @@ MUTANTS = {
     "int8 partials read unsigned codes":
         ("const int8_t* w8 = (const int8_t*)wrow + 32 * b;", "const uint8_t* w8 = wrow + 32 * b;"),
     "int8 rows at the nibble stride": ("Wq + r * (k * bits / 8)", "Wq + r * (k / 2)"),
+    "tier evicts the most recently used": ("if (v < 0 || stamp[s] < stamp[v]) v = s;",
+                                           "if (v < 0 || stamp[s] > stamp[v]) v = s;"),
+    "tier evicts pinned slots": ("if (pinned[s] || stamp[s] >= step) continue;",
+                                 "if (stamp[s] >= step) continue;"),
+    "tier reuses a slot of this pass": ("if (pinned[s] || stamp[s] >= step) continue;",
+                                        "if (pinned[s]) continue;"),
+    "tier hits leave the stamp": ("    stamp[slot_of[e]] = step;\n    ++nh;", "    ++nh;"),
+    "tier usage skips the shared expert": ("  if (S) count[E] = (int32_t)T;", ""),
+    "pin ranking ties to the higher id": ("if (best < 0 || usage[e] > usage[best]) best = e;",
+                                          "if (best < 0 || usage[e] >= usage[best]) best = e;"),
     "combine drops the shared expert": ("for (int64_t r = 0; r < D; ++r) { y[r] = o[r]; my[r] = m[r]; }",
                                         "for (int64_t r = 0; r < D; ++r) { y[r] = 0.0f; my[r] = m[r]; }"),
     "combine ignores routing weights": ("y[r] = fmaf(wj, o[r], y[r]);", "y[r] = y[r] + o[r];"),
