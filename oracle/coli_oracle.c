@@ -436,8 +436,8 @@ int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
  *  - pin_top: the n routed experts with the largest usage, the lower id on
  *    equal counts, in that order.
  *
- * Returns 0, or -1 if an index is invalid or the needed set does not fit in
- * the unpinned slots together with the pinned hits.
+ * Returns 0, or -1 (and changes nothing) if an index is invalid or the
+ * missing experts do not fit in the unpinned slots the pass's hits leave.
  */
 int orc_tier_init(int32_t E, int32_t S, int32_t slots, const int32_t* pin, int32_t n_pin,
                   int32_t* slot_of, int32_t* expert_in, int32_t* stamp, int32_t* pinned,
@@ -470,6 +470,16 @@ int orc_tier_plan(int32_t E, int32_t S, int32_t slots, const int32_t* idx, int64
     count[idx[i]] += 1;
   }
   if (S) count[E] = (int32_t)T;
+  if (rc == 0) {   /* the pass must fit: its misses in the unpinned slots its hits leave */
+    int32_t miss = 0, hit_unpinned = 0, unpinned = 0;
+    for (int32_t e = 0; e < E + S; ++e) {
+      if (count[e] == 0) continue;
+      if (slot_of[e] < 0) ++miss;
+      else if (!pinned[slot_of[e]]) ++hit_unpinned;
+    }
+    for (int32_t s = 0; s < slots; ++s) unpinned += pinned[s] ? 0 : 1;
+    if (miss > unpinned - hit_unpinned) rc = -1;
+  }
   int32_t nh = 0, nl = 0;
   for (int32_t e = 0; e < E + S && rc == 0; ++e) {     /* hits */
     if (count[e] == 0 || slot_of[e] < 0) continue;

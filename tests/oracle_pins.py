@@ -586,12 +586,17 @@ def pin_tier(orc):
     assert np.array_equal(t.usage, u0)
     # too many experts for the unpinned slots
     t = Tier(orc, 16, 1, 4, [3])
+    t.plan(np.array([[0, 1]], np.int32))
+    state = [a.copy() for a in (t.slot_of, t.expert_in, t.stamp, t.usage)]
     try:
-        t.plan(np.array([[0, 1], [2, 4]], np.int32))
+        t.plan(np.array([[0, 1], [2, 4]], np.int32))   # 0, 1 hit; 2, 4 need 2 more slots
     except ValueError:
         pass
     else:
         raise AssertionError("tier accepted more experts than slots")
+    assert all(np.array_equal(a, b) for a, b in zip(state, (t.slot_of, t.expert_in, t.stamp,
+                                                             t.usage))), "rejected plan changed the tier"
+    t.plan(np.array([[0, 3], [1, 3]], np.int32))          # fits: 3 is pinned
     # pin ranking
     u = rng.integers(0, 5, size=40).astype(np.int32)
     t = Tier(orc, 40, 0, 4)
