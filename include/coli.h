@@ -57,7 +57,9 @@ typedef enum {
   COLI_E_WORKSPACE = -3, /* workspace smaller than coli_moe_workspace_bytes()  */
   COLI_E_DEVICE = -4,    /* the current device is not gfx950                   */
   COLI_E_HIP = -5,       /* a HIP runtime call failed                          */
-  COLI_E_INDEX = -6      /* an expert index was outside [0, E) or repeated     */
+  COLI_E_INDEX = -6,     /* an expert index was outside [0, E) or repeated     */
+  COLI_E_TIER = -7       /* expert tier: a selected expert is not resident, or
+                            a pass needs more experts than the tier's slots  */
 } coli_status;
 
 /* Limits of this build. */
@@ -101,6 +103,12 @@ typedef enum {
  *
  * The shared expert (when S = 1) is index E.  E <= 256, S in {0, 1},
  * D % 64 == 0, F % 32 == 0, D and F <= COLI_MAX_DIM, weight_bits 4 or 8.
+ *
+ * Expert tiers (see coli_tier_* below): with slot_of != NULL the four arrays
+ * hold n_slots experts, and expert e lives at position slot_of[e] (a device
+ * array [E+S]; -1 = not resident).  A forward that selects a non-resident
+ * expert skips it and reports COLI_E_TIER through coli_moe_status().  With
+ * slot_of == NULL (n_slots ignored) expert e lives at position e.
  */
 typedef struct {
   int32_t n_routed;    /* E */
@@ -112,6 +120,8 @@ typedef struct {
   float* gu_s;
   uint8_t* dn_q;
   float* dn_s;
+  int32_t n_slots;        /* experts the arrays hold when slot_of != NULL */
+  const int32_t* slot_of; /* device [E+S] position of each expert, or NULL */
 } coli_expert_table;
 
 /* Sizes in bytes of the four table arrays for (E, S, D, F, weight_bits).
@@ -288,9 +298,84 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
                       int accumulate, void* workspace, size_t ws_bytes,
                       const coli_moe_trace* trace, const coli_moe_events* events, void* stream);
 
-/* Synchronises `stream`, then reports the device-side index check of the
- * last forward or layer call that used `workspace`: COLI_OK or COLI_E_INDEX. */
+/* Synchronises `stream`, then reports the device-side checks of the last
+ * forward or layer call that used `workspace`: COLI_OK, COLI_E_INDEX or
+ * COLI_E_TIER. */
 int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert tier: an HBM cache of one layer's experts over a store in host
+ * memory.  The pages keep the routed experts out of fast memory and cache
+ * them per layer with an LRU, a pinned hot store, and pins learned from a
+ * usage log (discuss.pytorch.kr colibri summary, "colibri의 핵심 아이디어";
+ * jeff.news, idea section; pulmap.app, "쓸수록 빨라지는 캐시": usage-learned
+ * pinning and next-layer readahead).  Here the fast memory is n_slots
+ * expert slots in HBM, the store is the layer's E+S experts in pinned host
+ * memory, and everything runs on the device: no host round trip per pass.
+ *
+ * Policy (deterministic):
+ *  - coli_tier_init: the shared expert takes slot 0, then the pinned experts
+ *    slots 1, 2, ... in the order given; those slots are never evicted; each
+ *    is a load.  The plan step counter starts at 0.
+ *  - coli_tier_plan (once per pass, before the forward): the needed set is
+ *    every selected expert plus the shared one.  Resident needed experts are
+ *    hits (their slot's stamp becomes the current step); then the missing
+ *    ones, in ascending id, each take the unpinned slot not used by this
+ *    pass with the smallest stamp (the lower slot on equal stamps; empty
+ *    slots have stamp -1); the evicted expert leaves the tier.  With
+ *    count_usage, usage[e] grows by the tokens that selected e (the shared
+ *    expert: all T).  A prefetch is a plan with count_usage = 0 on the
+ *    predicted selection.  If the needed set does not fit, the plan changes
+ *    nothing and sets the error flag (coli_tier_status: COLI_E_TIER).
+ *  - coli_tier_fetch copies every slot of the load list from the store.
+ *
+ * State (device arrays, caller-owned, int32):
+ */
+typedef struct {
+  int32_t* slot_of;   /* [E+S] slot of expert e, or -1                     */
+  int32_t* expert_in; /* [slots] expert in slot s, or -1                   */
+  int32_t* stamp;     /* [slots] plan step of the slot's last use, -1 never */
+  int32_t* pinned;    /* [slots] 1 = pinned                                */
+  int32_t* usage;     /* [E+S] selections counted                          */
+  int32_t* loads;     /* [1 + slots]: count, then the slots to fill         */
+  int32_t* counters;  /* [4]: plan steps, hits, loads, error flag          */
+} coli_tier_state;
+
+/* Sizes in bytes of the four arrays of a table holding `slots` experts.
+ * Returns the total, or 0 for an unsupported shape. */
+size_t coli_tier_table_bytes(int32_t slots, int64_t d_model, int64_t d_ff, int32_t weight_bits,
+                             size_t* gu_q, size_t* gu_s, size_t* dn_q, size_t* dn_s);
+
+/* Resets the state of `tier` (a table with slot_of == state->slot_of and
+ * n_slots slots) and fills the shared and pinned slots from `store` (as
+ * coli_tier_fetch).  pin: host array of n_pin distinct routed experts.
+ * Requires S + n_pin <= n_slots. */
+int coli_tier_init(const coli_expert_table* tier, const coli_tier_state* state,
+                   const int32_t* pin, int32_t n_pin, const coli_expert_table* store,
+                   void* stream);
+
+/* One pass's plan from the routing idx [T][k] (device, int32). */
+int coli_tier_plan(const coli_expert_table* tier, const coli_tier_state* state,
+                   const int32_t* idx, int64_t T, int32_t k, int32_t count_usage,
+                   void* stream);
+
+/* Fills the slots of the load list from `store`: a table (slot_of NULL) of
+ * the same E, S, D, F and weight_bits whose arrays are pinned host memory
+ * (hipHostMalloc) or device memory.  The copy is a kernel that reads the
+ * store through its device mapping, so it is stream-ordered and needs no
+ * host synchronisation; run it on a second stream to overlap the next
+ * layer's fetch with this layer's forward. */
+int coli_tier_fetch(const coli_expert_table* tier, const coli_tier_state* state,
+                    const coli_expert_table* store, void* stream);
+
+/* Synchronises `stream`, then reports the tier's error flag: COLI_OK or
+ * COLI_E_TIER (a pass needed more experts than the slots, or an index was
+ * invalid). */
+int coli_tier_status(const coli_tier_state* state, void* stream);
+
+/* Host-only: the n routed experts with the largest usage (ties to the lower
+ * id), in that order, for pinning on the next run.  usage: host [E]. */
+int coli_tier_rank(const int32_t* usage, int32_t E, int32_t n, int32_t* out);
 
 /* ------------------------------------------------------------------------ */
 const char* coli_status_string(int status);

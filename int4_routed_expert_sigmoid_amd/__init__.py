@@ -23,6 +23,7 @@ COLI_E_WORKSPACE = -3
 COLI_E_DEVICE = -4
 COLI_E_HIP = -5
 COLI_E_INDEX = -6
+COLI_E_TIER = -7
 COLI_MAX_EXPERTS = 256
 COLI_MAX_TOPK = 64
 
@@ -34,6 +35,8 @@ EXPORTED = [
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
     "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex",
     "coli_moe_status", "coli_status_string", "coli_last_hip_error",
+    "coli_tier_table_bytes", "coli_tier_init", "coli_tier_plan", "coli_tier_fetch",
+    "coli_tier_status", "coli_tier_rank",
 ]
 
 
@@ -52,7 +55,13 @@ class coli_expert_table(ctypes.Structure):
     _fields_ = [("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("weight_bits", ctypes.c_int32), ("gu_q", ctypes.c_void_p), ("gu_s", ctypes.c_void_p),
-                ("dn_q", ctypes.c_void_p), ("dn_s", ctypes.c_void_p)]
+                ("dn_q", ctypes.c_void_p), ("dn_s", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32), ("slot_of", ctypes.c_void_p)]
+
+
+class coli_tier_state(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("slot_of", "expert_in", "stamp", "pinned", "usage", "loads", "counters")]
 
 
 class coli_moe_events(ctypes.Structure):
@@ -104,6 +113,12 @@ def lib():
                                    _P, sz, _P, _P, _P], ctypes.c_int),
             "coli_moe_status": ([_P, sz, _P], ctypes.c_int),
             "coli_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "coli_tier_table_bytes": ([_I32, _I64, _I64, _I32, _P, _P, _P, _P], sz),
+            "coli_tier_init": ([_P, _P, _P, _I32, _P, _P], ctypes.c_int),
+            "coli_tier_plan": ([_P, _P, _P, _I64, _I32, _I32, _P], ctypes.c_int),
+            "coli_tier_fetch": ([_P, _P, _P, _P], ctypes.c_int),
+            "coli_tier_status": ([_P, _P], ctypes.c_int),
+            "coli_tier_rank": ([_P, _I32, _I32, _P], ctypes.c_int),
             "coli_last_hip_error": ([], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
@@ -146,27 +161,107 @@ class ExpertTable:
     weight_bits 4: int4 nibble codes; 8: int8 codes (the int8 head)."""
 
     def __init__(self, n_routed: int, n_shared: int, d_model: int, d_ff: int, device="cuda",
-                 weight_bits: int = 4):
+                 weight_bits: int = 4, _arrays=None):
         import torch
-        sizes = [ctypes.c_size_t() for _ in range(4)]
-        total = lib().coli_table_bytes(n_routed, n_shared, d_model, d_ff, weight_bits,
-                                       *[ctypes.byref(s) for s in sizes])
-        if total == 0:
-            raise ColiError("coli_table_bytes", COLI_E_SHAPE)
         self.E, self.S, self.D, self.F = n_routed, n_shared, d_model, d_ff
         self.weight_bits = weight_bits
+        if _arrays is None:
+            sizes = [ctypes.c_size_t() for _ in range(4)]
+            total = lib().coli_table_bytes(n_routed, n_shared, d_model, d_ff, weight_bits,
+                                           *[ctypes.byref(s) for s in sizes])
+            if total == 0:
+                raise ColiError("coli_table_bytes", COLI_E_SHAPE)
+            _arrays = (torch.empty(sizes[0].value, dtype=torch.uint8, device=device),
+                       torch.empty(sizes[1].value // 4, dtype=torch.float32, device=device),
+                       torch.empty(sizes[2].value, dtype=torch.uint8, device=device),
+                       torch.empty(sizes[3].value // 4, dtype=torch.float32, device=device))
+        self.gu_q, self.gu_s, self.dn_q, self.dn_s = _arrays
+        self.bytes = sum(a.numel() * a.element_size() for a in _arrays)
+        self.c = coli_expert_table(n_routed, n_shared, d_model, d_ff, weight_bits,
+                                   self.gu_q.data_ptr(), self.gu_s.data_ptr(),
+                                   self.dn_q.data_ptr(), self.dn_s.data_ptr(), 0, None)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def to_host_store(self):
+        """A copy of the table in pinned host memory: the store of an ExpertTier."""
+        import torch
+        arrays = []
+        for a in (self.gu_q, self.gu_s, self.dn_q, self.dn_s):
+            h = torch.empty(a.shape, dtype=a.dtype, pin_memory=True)   # hipHostMalloc'd
+            h.copy_(a)
+            arrays.append(h)
+        arrays = tuple(arrays)
+        return ExpertTable(self.E, self.S, self.D, self.F, weight_bits=self.weight_bits,
+                           _arrays=arrays)
+
+
+class ExpertTier:
+    """An HBM tier of `slots` experts of one layer (table storage + device
+    state), filled from a store by coli_tier_plan / coli_tier_fetch."""
+
+    def __init__(self, n_routed: int, n_shared: int, d_model: int, d_ff: int, slots: int,
+                 weight_bits: int = 4, device="cuda"):
+        import torch
+        sizes = [ctypes.c_size_t() for _ in range(4)]
+        total = lib().coli_tier_table_bytes(slots, d_model, d_ff, weight_bits,
+                                            *[ctypes.byref(s) for s in sizes])
+        if total == 0:
+            raise ColiError("coli_tier_table_bytes", COLI_E_SHAPE)
+        self.E, self.S, self.D, self.F, self.slots = n_routed, n_shared, d_model, d_ff, slots
+        self.weight_bits = weight_bits
+        i32 = dict(dtype=torch.int32, device=device)
+        A = n_routed + n_shared
+        self.st = {"slot_of": torch.full((A,), -1, **i32),
+                   "expert_in": torch.full((slots,), -1, **i32),
+                   "stamp": torch.full((slots,), -1, **i32),
+                   "pinned": torch.zeros(slots, **i32), "usage": torch.zeros(A, **i32),
+                   "loads": torch.zeros(1 + slots, **i32), "counters": torch.zeros(4, **i32)}
+        self.state = coli_tier_state(*[self.st[n].data_ptr() for n, _ in coli_tier_state._fields_])
         self.gu_q = torch.empty(sizes[0].value, dtype=torch.uint8, device=device)
         self.gu_s = torch.empty(sizes[1].value // 4, dtype=torch.float32, device=device)
         self.dn_q = torch.empty(sizes[2].value, dtype=torch.uint8, device=device)
         self.dn_s = torch.empty(sizes[3].value // 4, dtype=torch.float32, device=device)
         self.bytes = total
         self.c = coli_expert_table(n_routed, n_shared, d_model, d_ff, weight_bits,
-                                   self.gu_q.data_ptr(),
-                                   self.gu_s.data_ptr(), self.dn_q.data_ptr(),
-                                   self.dn_s.data_ptr())
+                                   self.gu_q.data_ptr(), self.gu_s.data_ptr(),
+                                   self.dn_q.data_ptr(), self.dn_s.data_ptr(), slots,
+                                   self.st["slot_of"].data_ptr())
 
     def ref(self):
+        """The tier as a table: pass it to coli_moe_forward / coli_moe_layer."""
         return ctypes.byref(self.c)
+
+    def init(self, store: "ExpertTable", pin=(), stream=None):
+        """Reset; the shared expert and the pinned ones are filled from store."""
+        arr = (ctypes.c_int32 * max(1, len(pin)))(*[int(e) for e in pin])
+        _check("coli_tier_init", lib().coli_tier_init(self.ref(), ctypes.byref(self.state), arr,
+                                                       len(pin), store.ref(), _stream(stream)))
+
+    def plan(self, idx, count_usage=True, stream=None):
+        import torch
+        _dtype(idx, torch.int32, "idx")
+        T, k = idx.shape
+        _check("coli_tier_plan", lib().coli_tier_plan(self.ref(), ctypes.byref(self.state),
+                                                       _ptr(idx), T, k, int(bool(count_usage)),
+                                                       _stream(stream)))
+
+    def fetch(self, store: "ExpertTable", stream=None):
+        _check("coli_tier_fetch", lib().coli_tier_fetch(self.ref(), ctypes.byref(self.state),
+                                                         store.ref(), _stream(stream)))
+
+    def status(self, stream=None) -> int:
+        return int(lib().coli_tier_status(ctypes.byref(self.state), _stream(stream)))
+
+
+def coli_tier_rank(usage, n: int):
+    """The n routed experts with the largest usage (host numpy int32 [E])."""
+    import numpy as np
+    u = np.ascontiguousarray(usage, dtype=np.int32)
+    out = np.empty(n, dtype=np.int32)
+    _check("coli_tier_rank", lib().coli_tier_rank(u.ctypes.data, u.size, n, out.ctypes.data))
+    return out
 
 
 def coli_table_set_expert(table: ExpertTable, expert: int, gate_q, gate_s, up_q, up_s, down_q,

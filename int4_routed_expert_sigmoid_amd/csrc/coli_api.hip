@@ -56,6 +56,9 @@ int table_check(const coli_expert_table* t) {
     return COLI_E_SHAPE;
   if (t->d_model > COLI_MAX_DIM || t->d_ff > COLI_MAX_DIM) return COLI_E_SHAPE;
   if (t->weight_bits != 4 && t->weight_bits != 8) return COLI_E_SHAPE;
+  if (t->slot_of && (t->n_slots < 1 || t->n_slots > t->n_routed + t->n_shared))
+    return COLI_E_SHAPE;
+  if (t->slot_of && !al4(t->slot_of)) return COLI_E_INVAL;
   if (!t->gu_q || !t->gu_s || !t->dn_q || !t->dn_s) return COLI_E_INVAL;
   if (!al16(t->gu_q) || !al16(t->dn_q) || !al4(t->gu_s) || !al4(t->dn_s)) return COLI_E_INVAL;
   return COLI_OK;
@@ -112,6 +115,7 @@ const char* coli_status_string(int status) {
     case COLI_E_DEVICE: return "current device is not gfx950 (or no device)";
     case COLI_E_HIP: return "HIP runtime error";
     case COLI_E_INDEX: return "expert index out of range or repeated within a token";
+    case COLI_E_TIER: return "expert tier: expert not resident, or a pass needs more slots";
     default: return "unknown status";
   }
 }
@@ -421,7 +425,152 @@ int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream) {
   if (e != hipSuccess) return hip_fail(e);
   e = hipStreamSynchronize(as_stream(stream));
   if (e != hipSuccess) return hip_fail(e);
-  return err == 0 ? COLI_OK : COLI_E_INDEX;
+  return err == 0 ? COLI_OK : err == COLI_E_TIER ? COLI_E_TIER : COLI_E_INDEX;
+}
+
+// ---------------------------------------------------------------------------
+// Expert tier.
+
+size_t coli_tier_table_bytes(int32_t slots, int64_t D, int64_t F, int32_t bits, size_t* gu_q,
+                             size_t* gu_s, size_t* dn_q, size_t* dn_s) {
+  if (slots < 1 || slots > COLI_MAX_EXPERTS + 1) return 0;
+  if (D <= 0 || D % 64 || F <= 0 || F % 32 || D > COLI_MAX_DIM || F > COLI_MAX_DIM) return 0;
+  if (bits != 4 && bits != 8) return 0;
+  const size_t n = (size_t)slots;
+  const size_t a = n * (size_t)(D * F * bits / 4), b = n * (size_t)(2 * F) * sizeof(float),
+               c = n * (size_t)(D * F * bits / 8), d = n * (size_t)D * sizeof(float);
+  if (gu_q) *gu_q = a;
+  if (gu_s) *gu_s = b;
+  if (dn_q) *dn_q = c;
+  if (dn_s) *dn_s = d;
+  return a + b + c + d;
+}
+
+static int tier_check(const coli_expert_table* t, const coli_tier_state* st) {
+  int rc = table_check(t);
+  if (rc) return rc;
+  if (!st || !t->slot_of || t->slot_of != st->slot_of) return COLI_E_INVAL;
+  const int32_t* p[] = {st->slot_of, st->expert_in, st->stamp, st->pinned, st->usage, st->loads,
+                        st->counters};
+  for (const int32_t* q : p)
+    if (!q || !al4(q)) return COLI_E_INVAL;
+  return COLI_OK;
+}
+
+static int store_view(const coli_expert_table* tier, const coli_expert_table* store,
+                      const void* src[4]);
+
+int coli_tier_init(const coli_expert_table* tier, const coli_tier_state* st, const int32_t* pin,
+                   int32_t n_pin, const coli_expert_table* store, void* stream) {
+  int rc = tier_check(tier, st);
+  if (rc) return rc;
+  const int E = tier->n_routed, S = tier->n_shared;
+  if (n_pin < 0 || (n_pin > 0 && !pin) || S + n_pin > tier->n_slots) return COLI_E_INVAL;
+  for (int i = 0; i < n_pin; ++i) {
+    if (pin[i] < 0 || pin[i] >= E) return COLI_E_INVAL;
+    for (int j = 0; j < i; ++j)
+      if (pin[j] == pin[i]) return COLI_E_INVAL;
+  }
+  if ((rc = check_device())) return rc;
+  const void* src[4];
+  if ((rc = store_view(tier, store, src))) return rc;
+  hipError_t e = coli::launch_tier_init(*tier, *st, pin, n_pin, as_stream(stream));
+  if (e == hipSuccess) e = coli::launch_tier_fetch(*tier, *st, src, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_tier_plan(const coli_expert_table* tier, const coli_tier_state* st, const int32_t* idx,
+                   int64_t T, int32_t k, int32_t count_usage, void* stream) {
+  int rc = tier_check(tier, st);
+  if (rc) return rc;
+  if (T < 0 || T > 0x7FFFFFFF || k < 1 || k > COLI_MAX_TOPK || k > tier->n_routed)
+    return COLI_E_SHAPE;
+  if (T * (int64_t)k > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if ((T > 0 && !idx) || !al4(idx) || (count_usage != 0 && count_usage != 1)) return COLI_E_INVAL;
+  if ((rc = check_device())) return rc;
+  hipError_t e = coli::launch_tier_plan(*tier, *st, idx, T, k, count_usage, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+// The device-visible address of a store array: device memory as it is,
+// pinned host memory through its device mapping; anything else is refused.
+static int device_view(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error of the failed query
+    return COLI_E_INVAL;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = p;
+    return COLI_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+    *out = attr.devicePointer;
+    return COLI_OK;
+  }
+  return COLI_E_INVAL;
+}
+
+// Checks a store against its tier and resolves its device-visible addresses
+// (call after check_device: the address query needs the device).
+static int store_view(const coli_expert_table* tier, const coli_expert_table* store,
+                      const void* src[4]) {
+  if (!store || store->slot_of) return COLI_E_INVAL;
+  if (store->n_routed != tier->n_routed || store->n_shared != tier->n_shared ||
+      store->d_model != tier->d_model || store->d_ff != tier->d_ff ||
+      store->weight_bits != tier->weight_bits)
+    return COLI_E_SHAPE;
+  if (!store->gu_q || !store->gu_s || !store->dn_q || !store->dn_s) return COLI_E_INVAL;
+  if (!al16(store->gu_q) || !al16(store->gu_s) || !al16(store->dn_q) || !al16(store->dn_s) ||
+      !al16(tier->gu_s) || !al16(tier->dn_s))
+    return COLI_E_INVAL;
+  const void* host[4] = {store->gu_q, store->gu_s, store->dn_q, store->dn_s};
+  for (int m = 0; m < 4; ++m) {
+    int rc = device_view(host[m], &src[m]);
+    if (rc) return rc;
+  }
+  return COLI_OK;
+}
+
+int coli_tier_fetch(const coli_expert_table* tier, const coli_tier_state* st,
+                    const coli_expert_table* store, void* stream) {
+  int rc = tier_check(tier, st);
+  if (rc) return rc;
+  if (!store) return COLI_E_INVAL;
+  if (store->n_routed != tier->n_routed || store->d_model != tier->d_model) return COLI_E_SHAPE;
+  if ((rc = check_device())) return rc;
+  const void* src[4];
+  if ((rc = store_view(tier, store, src))) return rc;
+  hipError_t e = coli::launch_tier_fetch(*tier, *st, src, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_tier_status(const coli_tier_state* st, void* stream) {
+  if (!st || !st->counters) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  int32_t c[4] = {};
+  hipError_t e = hipMemcpyAsync(c, st->counters, sizeof(c), hipMemcpyDeviceToHost,
+                                as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return c[3] == 0 ? COLI_OK : COLI_E_TIER;
+}
+
+int coli_tier_rank(const int32_t* usage, int32_t E, int32_t n, int32_t* out) {
+  if (E < 1 || E > COLI_MAX_EXPERTS || n < 0 || n > E) return COLI_E_SHAPE;
+  if (!usage || (n > 0 && !out)) return COLI_E_INVAL;
+  // selection by repeated maximum: n, E <= 256
+  bool taken[COLI_MAX_EXPERTS] = {};
+  for (int i = 0; i < n; ++i) {
+    int best = -1;
+    for (int e = 0; e < E; ++e)
+      if (!taken[e] && (best < 0 || usage[e] > usage[best])) best = e;
+    taken[best] = true;
+    out[i] = best;
+  }
+  return COLI_OK;
 }
 
 }  // extern "C"

@@ -60,6 +60,9 @@ struct GuArgs {
   int8_t* hq;
   float* hd;
   int32_t* hsum8;
+  const int32_t* slot_of;  // expert tier: storage position of each expert, or null
+  int n_store;             // positions the table holds
+  int32_t* err;
   int64_t T, D, F;
   int k, S;
   int32_t* tr_pg;
@@ -80,10 +83,27 @@ struct DnArgs {
   const int32_t* n_active;
   const int32_t* active;
   float* o;
+  const int32_t* slot_of;
+  int n_store;
+  int32_t* err;
   int64_t T, D, F;
   int k, S, E;
   int32_t* tr_pd;
 };
+
+// Storage position of expert e: e itself, or its tier slot.  A tier slot
+// outside [0, n_store) (the expert is not resident) flags COLI_E_TIER and
+// returns -1: the workgroup then skips the expert without reading it.
+__device__ __forceinline__ int storage_of(const int32_t* slot_of, int n_store, int e,
+                                          int32_t* err) {
+  if (!slot_of) return e;
+  const int p = *as_const(slot_of + e);
+  if (p < 0 || p >= n_store) {
+    if (threadIdx.x == 0) *err = COLI_E_TIER;
+    return -1;
+  }
+  return p;
+}
 
 // The 32 weight codes of one block as the 8 byte-vectors that line up with
 // the 8 int8 words of the activation block (offset-binary nibbles for int4,
@@ -388,14 +408,16 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
   const bool live = (int64_t)blockIdx.x * W + wave < G;
   const int grp = live ? (int)blockIdx.x * W + wave : (int)G - 1;
   const int KS = a.k + a.S;
+  const int es = storage_of(a.slot_of, a.n_store, e, a.err);
+  if (es < 0) return;                    // uniform across the workgroup
   const int NU = U * NB;                 // 1 KB chunks in the row group
-  const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)e * G + grp) * (size_t)NU * kWave);
+  const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)es * G + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
   clear_tail_records<MAXT>(NB, PF / U, threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
-  const float rs = a.gu_s[((size_t)e * G + grp) * kWave + lane];
+  const float rs = a.gu_s[((size_t)es * G + grp) * kWave + lane];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
   for (int c0 = 0; c0 < cnt; c0 += MAXT) {
     const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
@@ -493,15 +515,17 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   const int grp = live ? (int)blockIdx.x * W + wave : (int)G - 1;
   const int NB = (int)(a.F / 32);
   const int NU = U * NB;
+  const int es = storage_of(a.slot_of, a.n_store, e, a.err);
+  if (es < 0) return;                    // uniform across the workgroup
   const char* wbase =
-      reinterpret_cast<const char*>(a.dn_q + ((size_t)e * (a.D / 64) + grp) * (size_t)NU * kWave);
+      reinterpret_cast<const char*>(a.dn_q + ((size_t)es * (a.D / 64) + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
   clear_tail_records<MAXT>(NB, PF / U, threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
-  const float rs = a.dn_s[(size_t)e * a.D + row];
+  const float rs = a.dn_s[(size_t)es * a.D + row];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
   for (int c0 = 0; c0 < cnt; c0 += MAXT) {
     const int nt = cnt - c0 < MAXT ? cnt - c0 : MAXT;
@@ -620,8 +644,9 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   const coli_moe_events& ev = f.events ? *f.events : no_events;
   hipError_t rc = record(ev.begin, s);
   if (rc != hipSuccess) return rc;
-  // the grouped matrix-core kernels read int4 tables only
-  const bool grouped = t.weight_bits == 4 && T >= kMfmaMinTokens && mfma_path_fits(T, D, F, f.k, S);
+  // the grouped matrix-core kernels read resident int4 tables only
+  const bool grouped = t.weight_bits == 4 && !t.slot_of && T >= kMfmaMinTokens &&
+                       mfma_path_fits(T, D, F, f.k, S);
   if (!f.dispatched) {
     // the GEMV path also needs the code sums of x; the grouped path does not
     rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active, ws.active, ws.err,
@@ -650,6 +675,9 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   g.hq = ws.hq;
   g.hd = ws.hd;
   g.hsum8 = ws.hsum8;
+  g.slot_of = t.slot_of;
+  g.n_store = t.slot_of ? t.n_slots : E + S;
+  g.err = ws.err;
   g.T = T;
   g.D = D;
   g.F = F;
@@ -666,6 +694,9 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   d.n_active = ws.n_active;
   d.active = ws.active;
   d.o = ws.o;
+  d.slot_of = t.slot_of;
+  d.n_store = t.slot_of ? t.n_slots : E + S;
+  d.err = ws.err;
   d.T = T;
   d.D = D;
   d.F = F;

@@ -122,6 +122,14 @@ hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const
                                    const uint8_t* down_q, const float* down_s, hipStream_t s);
 hipError_t launch_rmsnorm_q8(const float* h, int64_t T, int64_t D, float eps, int8_t* q, float* d,
                              float* r_out, hipStream_t s);
+// Expert tier (coli_tier.hip).  pin: host array of n_pin experts.
+hipError_t launch_tier_init(const coli_expert_table& t, const coli_tier_state& st,
+                            const int32_t* pin, int n_pin, hipStream_t s);
+hipError_t launch_tier_plan(const coli_expert_table& t, const coli_tier_state& st,
+                            const int32_t* idx, int64_t T, int k, int count_usage, hipStream_t s);
+// src: device-visible addresses of the store's gu_q, gu_s, dn_q, dn_s.
+hipError_t launch_tier_fetch(const coli_expert_table& t, const coli_tier_state& st,
+                             const void* const src[4], hipStream_t s);
 // logits[t][e] = sum_d wr[e][d] x[t][d], fp64 sum rounded once (D % 64 == 0).
 hipError_t launch_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int E,
                                 float* out, hipStream_t s);

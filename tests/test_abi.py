@@ -62,8 +62,8 @@ def test_table_bytes():
         assert L.coli_table_bytes(16, 1, 256, 128, bits, None, None, None, None) == 0
 
 
-def _table(E=16, S=1, D=256, F=128, ptr=FAKE, bits=4):
-    return coli.coli_expert_table(E, S, D, F, bits, ptr, ptr, ptr, ptr)
+def _table(E=16, S=1, D=256, F=128, ptr=FAKE, bits=4, slots=0, slot_of=None):
+    return coli.coli_expert_table(E, S, D, F, bits, ptr, ptr, ptr, ptr, slots, slot_of)
 
 
 def test_validation_quant():
@@ -165,3 +165,39 @@ def test_validation_layer():
     assert f(*args(t, x=FAKE + 4)) == coli.COLI_E_INVAL     # x must be 16-byte aligned
     assert f(*args(t, acc=5)) == coli.COLI_E_INVAL
     assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK
+
+
+def test_tier_host_checks():
+    """Tier entry points: sizes, rank (host logic), and argument checks."""
+    import numpy as np
+    L = coli.lib()
+    sizes = [ctypes.c_size_t() for _ in range(4)]
+    tot = L.coli_tier_table_bytes(32, 6144, 2048, 4, *[ctypes.byref(s) for s in sizes])
+    assert tot == 32 * 18915328
+    assert L.coli_tier_table_bytes(0, 6144, 2048, 4, None, None, None, None) == 0
+    assert L.coli_tier_table_bytes(258, 6144, 2048, 4, None, None, None, None) == 0
+    assert L.coli_tier_table_bytes(8, 6144, 2048, 2, None, None, None, None) == 0
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 6, size=256).astype(np.int32)
+    assert coli.coli_tier_rank(u, 40).tolist() == sorted(range(256), key=lambda e: (-int(u[e]), e))[:40]
+    assert L.coli_tier_rank(None, 16, 2, None) == coli.COLI_E_INVAL
+    assert L.coli_tier_rank(FAKE, 16, 17, FAKE) == coli.COLI_E_SHAPE
+    st = coli.coli_tier_state(*([FAKE] * 7))
+    t = _table(slots=8, slot_of=FAKE)
+    f = L.coli_tier_plan
+    assert f(ctypes.byref(t), ctypes.byref(st), FAKE, 1, 0, 1, None) == coli.COLI_E_SHAPE
+    assert f(ctypes.byref(t), ctypes.byref(st), FAKE, 1, 2, 2, None) == coli.COLI_E_INVAL
+    assert f(ctypes.byref(_table(slots=8, slot_of=FAKE + 64)), ctypes.byref(st), FAKE, 1, 2, 1,
+             None) == coli.COLI_E_INVAL                        # table map != state map
+    assert f(ctypes.byref(_table(slots=18, slot_of=FAKE)), ctypes.byref(st), FAKE, 1, 2, 1,
+             None) == coli.COLI_E_SHAPE                        # more slots than experts
+    store = _table()
+    pin = (ctypes.c_int32 * 3)(1, 2, 1)
+    assert L.coli_tier_init(ctypes.byref(t), ctypes.byref(st), pin, 3, ctypes.byref(store),
+                            None) == coli.COLI_E_INVAL                   # repeated pin
+    pin = (ctypes.c_int32 * 8)(*range(8))
+    assert L.coli_tier_init(ctypes.byref(t), ctypes.byref(st), pin, 8, ctypes.byref(store),
+                            None) == coli.COLI_E_INVAL                   # 1 + 8 > 8 slots
+    assert L.coli_tier_fetch(ctypes.byref(t), ctypes.byref(st), ctypes.byref(_table(E=15)),
+                             None) == coli.COLI_E_SHAPE
+    assert L.coli_tier_status(None, None) == coli.COLI_E_INVAL
