@@ -266,6 +266,116 @@ def batch_leg(table, bits, wids, coli, synth, torch, hev, replays=4, pool=64):
     return res
 
 
+def tier_leg(coli, synth, torch, layers=4, slots=64, warm=32, timed=32):
+    """Decode through `layers` page-shape layers whose experts live only in
+    pinned host memory (4.86 GB per layer), each with an HBM tier of `slots`
+    experts: Zipf(1.1) routing, the pre-norm residual stack of the deep-decode
+    workload.  Per layer and token: RMSNorm+Q8, routing, tier plan, fetch of
+    the misses over the host link, forward through the tier.  Three runs of
+    `warm` + `timed` tokens: LRU from empty tiers; tiers re-initialised with
+    each layer's most used experts of the first run pinned (half the slots);
+    the same plus next-layer prefetch on a copy stream (prediction = the next
+    layer's actual routing: an upper bound of what readahead can hide)."""
+    from dataclasses import replace
+    w = replace(synth.WORKLOADS[4], layers=layers)
+    stores, tiers = [], []
+    for l in range(layers):
+        t = build_table(w, coli, synth, torch, layer=l)
+        stores.append(t.to_host_store())
+        del t
+        torch.cuda.empty_cache()
+        tiers.append(coli.ExpertTier(w.E, w.S, w.D, w.F, slots))
+    N = warm + timed
+    lg = [torch.from_numpy(synth.logits(w, N, 0, l)).cuda() for l in range(layers)]
+    zero = torch.zeros(w.E, dtype=torch.float32, device="cuda")
+    h0 = torch.from_numpy(synth.hidden0(w, N)).cuda()
+    xq = torch.empty((1, w.D), dtype=torch.int8, device="cuda")
+    xd = torch.empty((1, w.D // 32), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((1, w.k), dtype=torch.float32, device="cuda")
+    pidx = torch.empty((1, w.k), dtype=torch.int32, device="cuda")
+    pwt = torch.empty((1, w.k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(coli.coli_moe_workspace_bytes(tiers[0], 1, w.k), dtype=torch.uint8,
+                     device="cuda")
+    main = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    expert_bytes_all = sum(expert_bytes(w))
+
+    def run(prefetch):
+        h = h0.clone()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        for i in range(N):
+            if i == warm:
+                torch.cuda.synchronize()
+                c0 = [t.st["counters"].cpu().numpy().copy() for t in tiers]
+                t0.record()
+            hi = h[i:i + 1]
+            for l in range(layers):
+                if prefetch and l + 1 < layers:
+                    started = torch.cuda.Event()
+                    started.record(main)
+                    copy.wait_event(started)     # layer l+1 of the last token is done
+                    with torch.cuda.stream(copy):
+                        coli.coli_route_topk(lg[l + 1][i:i + 1], zero, w.k, pidx, pwt)
+                        tiers[l + 1].plan(pidx, count_usage=False)
+                        tiers[l + 1].fetch(stores[l + 1])
+                    ready = torch.cuda.Event()
+                    ready.record(copy)
+                coli.coli_rmsnorm_q8(hi, 1e-6, xq, xd)
+                coli.coli_route_topk(lg[l][i:i + 1], zero, w.k, idx, wt)
+                if prefetch and l > 0:
+                    main.wait_event(ready_prev)
+                tiers[l].plan(idx)
+                tiers[l].fetch(stores[l])
+                coli.coli_moe_forward(tiers[l], xq, xd, idx, wt, hi, ws, accumulate=True)
+                if prefetch and l + 1 < layers:
+                    ready_prev = ready
+        t1.record()
+        torch.cuda.synchronize()
+        if coli.coli_moe_status(ws) != coli.COLI_OK or any(t.status() for t in tiers):
+            raise RuntimeError("tier leg: device-side check failed")
+        c1 = [t.st["counters"].cpu().numpy() for t in tiers]
+        hits = sum(int(b[1] - a[1]) for a, b in zip(c0, c1))
+        loads = sum(int(b[2] - a[2]) for a, b in zip(c0, c1))
+        ms = t0.elapsed_time(t1) / timed
+        return {"ms_per_token": round(ms, 3), "tok_s": round(1000.0 / ms, 1),
+                "hit_rate": round(hits / max(1, hits + loads), 4),
+                "loads_per_token_layer": round(loads / (timed * layers), 3),
+                "host_read_gbps": round(loads * expert_bytes_all / (timed * ms * 1e-3) / 1e9, 1)}
+
+    res = {"workload": f"Zipf(1.1) decode, {layers} layers d6144 f2048 e256+1 top8, experts in "
+                       f"pinned host memory, {slots} HBM slots per layer",
+           "tier_bytes_per_layer": tiers[0].bytes, "store_bytes_per_layer": stores[0].bytes}
+    for t, st in zip(tiers, stores):
+        t.init(st)
+    res["lru"] = run(False)
+    pins = [coli.coli_tier_rank(t.st["usage"].cpu().numpy()[: w.E], slots // 2) for t in tiers]
+    for t, st, p in zip(tiers, stores, pins):
+        t.init(st, p)
+    res["learned_pins"] = run(False)
+    for t, st, p in zip(tiers, stores, pins):
+        t.init(st, p)
+    res["learned_pins_prefetch"] = run(True)
+    # host-link read rate of the fetch kernel: re-initialising a tier with
+    # slots - 1 pins fetches `slots` experts in one launch
+    many = list(range(slots - 1))
+    for _ in range(2):
+        tiers[0].init(stores[0], many)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    tiers[0].init(stores[0], many)
+    e1.record()
+    torch.cuda.synchronize()
+    fms = e0.elapsed_time(e1)
+    res["fetch_gbps"] = round(slots * expert_bytes_all / (fms * 1e-3) / 1e9, 1)
+    res["fetch_ms_per_expert"] = round(fms / slots, 4)
+    del tiers, stores
+    torch.cuda.empty_cache()
+    return res
+
+
 def router_leg(coli, synth, torch, steps=50):
     """The router projection (F32 weights [256][6144], fp64 sum) for 1 and 2048 tokens."""
     w = synth.WORKLOADS[1]
@@ -304,6 +414,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="timed 2048-token passes of the prefill leg (0: skip it)")
     ap.add_argument("--no-head", action="store_true", help="skip the int8 head leg")
+    ap.add_argument("--no-tier", action="store_true", help="skip the expert-tier leg")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 8 device-to-device copies of this many bytes (the known-size "
                          "kernel that scales the HBM byte counters under rocprofv3 --pmc)")
@@ -461,6 +572,8 @@ def main():
     out["router_logits"] = router_leg(coli, synth, torch)
     if not args.no_head:
         out["int8_head"] = head_leg(coli, synth, torch, hev)
+    if not args.no_tier:
+        out["tier"] = tier_leg(coli, synth, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out), flush=True)
