@@ -376,6 +376,42 @@ def tier_leg(coli, synth, torch, layers=4, slots=64, warm=32, timed=32):
     return res
 
 
+def paths_leg(table, coli, synth, torch, reps=8):
+    """The per-shape path choice, measured: the forward of T tokens (page
+    shape, router bias N(0, 0.1)) on the GEMV and on the grouped path; the
+    automatic choice switches to the grouped path at COLI_GROUPED_MIN_TOKENS."""
+    w = synth.WORKLOADS[3]
+    b = torch.from_numpy(synth.router_bias(w)).cuda()
+    rows = []
+    for T in (4, 8, 10, 12, 14, 16, 24, 32, 64, 128, 512):
+        x = torch.from_numpy(synth.activations(w, T, 4000)).cuda()
+        lg = torch.from_numpy(synth.logits(w, T, 4000)).cuda()
+        xq = torch.empty((T, w.D), dtype=torch.int8, device="cuda")
+        xd = torch.empty((T, w.D // 32), dtype=torch.float32, device="cuda")
+        idx = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+        wt = torch.empty((T, w.k), dtype=torch.float32, device="cuda")
+        coli.coli_quant_act_q8(x, xq, xd)
+        coli.coli_route_topk(lg, b, w.k, idx, wt)
+        y = torch.empty((T, w.D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(coli.coli_moe_workspace_bytes(table, T, w.k), dtype=torch.uint8,
+                         device="cuda")
+        row = {"tokens": T, "auto": "grouped" if coli.coli_moe_path(table, T, w.k) ==
+               coli.COLI_PATH_GROUPED else "gemv"}
+        for name, p in (("gemv", coli.COLI_PATH_GEMV), ("grouped", coli.COLI_PATH_GROUPED)):
+            for _ in range(2):
+                coli.coli_moe_forward_path(table, xq, xd, idx, wt, y, ws, p)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                coli.coli_moe_forward_path(table, xq, xd, idx, wt, y, ws, p)
+            e1.record()
+            torch.cuda.synchronize()
+            row[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+        rows.append(row)
+    return rows
+
+
 def router_leg(coli, synth, torch, steps=50):
     """The router projection (F32 weights [256][6144], fp64 sum) for 1 and 2048 tokens."""
     w = synth.WORKLOADS[1]
@@ -415,6 +451,7 @@ def main():
                     help="timed 2048-token passes of the prefill leg (0: skip it)")
     ap.add_argument("--no-head", action="store_true", help="skip the int8 head leg")
     ap.add_argument("--no-tier", action="store_true", help="skip the expert-tier leg")
+    ap.add_argument("--no-paths", action="store_true", help="skip the path-choice leg")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 8 device-to-device copies of this many bytes (the known-size "
                          "kernel that scales the HBM byte counters under rocprofv3 --pmc)")
@@ -567,6 +604,8 @@ def main():
         out["prefill"] = [prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3),
                           prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3,
                                       bias_free=True)]
+    if not args.no_paths:
+        out["paths"] = paths_leg(table, coli, synth, torch)
     verify = synth.WORKLOADS[2]
     out["verify"] = {"workload": verify.name, **batch_leg(table, 4, (2,), coli, synth, torch, hev)}
     out["router_logits"] = router_leg(coli, synth, torch)

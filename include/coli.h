@@ -229,6 +229,36 @@ int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const flo
                      int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
                      int accumulate, void* workspace, size_t ws_bytes, void* stream);
 
+/* Per-shape path choice (jeff.news, kernel section: the pages' int4 kernel
+ * wins in batch and loses to f32 for a single row, so the engine picks the
+ * kernel by shape).  Two exact paths compute every forward bit-identically:
+ *   COLI_PATH_GEMV     wavefront-per-row-group GEMV, 1-8 tokens per weight
+ *                      pass; any table.
+ *   COLI_PATH_GROUPED  grouped matrix-core GEMM over chunks of <= 64 tokens
+ *                      per expert; resident int4 tables only.
+ *   COLI_PATH_AUTO     GROUPED from the measured crossover in tokens per
+ *                      pass (COLI_GROUPED_MIN_TOKENS: at d_model 6144,
+ *                      d_ff 2048, 256 + 1 experts, top-8 the GEMV wins at 12
+ *                      tokens, the grouped path at 14), GEMV below it and
+ *                      wherever GROUPED does not apply.
+ * (An f32-weight path would move 8x the bytes of an HBM-bound GEMV, so it
+ * is never the faster one here.) */
+#define COLI_PATH_AUTO 0
+#define COLI_PATH_GEMV 1
+#define COLI_PATH_GROUPED 2
+#define COLI_GROUPED_MIN_TOKENS 14
+
+/* coli_moe_forward on the given path.  COLI_PATH_GROUPED on a table it does
+ * not apply to returns COLI_E_SHAPE. */
+int coli_moe_forward_path(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                          int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                          int accumulate, void* workspace, size_t ws_bytes, int32_t path,
+                          void* stream);
+
+/* Host-only: the path COLI_PATH_AUTO takes for (table, T, k): COLI_PATH_GEMV
+ * or COLI_PATH_GROUPED (or a negative status for invalid arguments). */
+int coli_moe_path(const coli_expert_table* table, int64_t T, int32_t k);
+
 /* Intermediate dumps for testing; every pointer may be NULL (not written).
  * Pair p = t*(k+S) + slot indexes per-(token, slot) arrays; pairs with an
  * invalid index are left unwritten. */

@@ -24,6 +24,7 @@ COLI_E_DEVICE = -4
 COLI_E_HIP = -5
 COLI_E_INDEX = -6
 COLI_E_TIER = -7
+COLI_PATH_AUTO, COLI_PATH_GEMV, COLI_PATH_GROUPED = 0, 1, 2
 COLI_MAX_EXPERTS = 256
 COLI_MAX_TOPK = 64
 
@@ -33,6 +34,7 @@ EXPORTED = [
     "coli_rmsnorm_q8", "coli_route_topk", "coli_router_logits", "coli_dispatch",
     "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
+    "coli_moe_forward_path", "coli_moe_path",
     "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex",
     "coli_moe_status", "coli_status_string", "coli_last_hip_error",
     "coli_tier_table_bytes", "coli_tier_init", "coli_tier_plan", "coli_tier_fetch",
@@ -106,6 +108,9 @@ def lib():
                                          sz, _P, _P], ctypes.c_int),
             "coli_moe_forward_profiled": ([_P, _P, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P,
                                            sz, _P, _P], ctypes.c_int),
+            "coli_moe_forward_path": ([_P, _P, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P, sz,
+                                       _I32, _P], ctypes.c_int),
+            "coli_moe_path": ([_P, _I64, _I32], ctypes.c_int),
             "coli_moe_layer_workspace_bytes": ([_P, _I64, _I32], sz),
             "coli_moe_layer": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P, ctypes.c_int, _P,
                                 sz, _P], ctypes.c_int),
@@ -346,6 +351,24 @@ def coli_moe_forward(table: ExpertTable, xq, xd, idx, w, y, workspace, accumulat
            lib().coli_moe_forward(table.ref(), _ptr(xq), _ptr(xd), T, _ptr(idx), _ptr(w), k,
                                   _ptr(y), int(bool(accumulate)), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def coli_moe_forward_path(table: ExpertTable, xq, xd, idx, w, y, workspace, path: int,
+                          accumulate=False, stream=None):
+    T, k = idx.shape
+    _check("coli_moe_forward_path",
+           lib().coli_moe_forward_path(table.ref(), _ptr(xq), _ptr(xd), T, _ptr(idx), _ptr(w), k,
+                                       _ptr(y), int(bool(accumulate)), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), path,
+                                       _stream(stream)))
+
+
+def coli_moe_path(table: ExpertTable, T: int, k: int) -> int:
+    """The path COLI_PATH_AUTO takes for T tokens per pass (host only)."""
+    r = int(lib().coli_moe_path(table.ref(), T, k))
+    if r < 0:
+        raise ColiError("coli_moe_path", r)
+    return r
 
 
 def coli_moe_forward_traced(table: ExpertTable, xq, xd, idx, w, y, workspace, trace: dict,

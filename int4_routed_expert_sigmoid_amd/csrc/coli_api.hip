@@ -257,11 +257,24 @@ size_t coli_moe_workspace_bytes(const coli_expert_table* table, int64_t T, int32
       .bytes;
 }
 
+// The path a forward takes: AUTO is grouped from COLI_GROUPED_MIN_TOKENS
+// tokens per pass where the grouped path applies (the crossover measured at
+// the page shape), else the GEMV.  Returns 0 (GEMV), 1 (grouped) or < 0.
+static int choose_grouped(const coli_expert_table* t, int64_t T, int k, int path) {
+  const bool applies = coli::grouped_applies(*t, T, k);
+  switch (path) {
+    case COLI_PATH_AUTO: return applies && T >= COLI_GROUPED_MIN_TOKENS ? 1 : 0;
+    case COLI_PATH_GEMV: return 0;
+    case COLI_PATH_GROUPED: return applies ? 1 : COLI_E_SHAPE;
+    default: return COLI_E_INVAL;
+  }
+}
+
 static int forward_impl(const coli_expert_table* table, const int8_t* xq, const float* xd,
                         int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
                         int accumulate, void* workspace, size_t ws_bytes,
                         const coli_moe_trace* trace, const coli_moe_events* events,
-                        void* stream) {
+                        void* stream, int path = COLI_PATH_AUTO) {
   int rc = table_check(table);
   if (rc) return rc;
   if (k < 1 || k > table->n_routed || k > COLI_MAX_TOPK) return COLI_E_SHAPE;
@@ -274,8 +287,11 @@ static int forward_impl(const coli_expert_table* table, const int8_t* xq, const 
   const coli::MoeWorkspace ws = coli::moe_workspace_layout(
       workspace, table->n_routed, table->n_shared, table->d_model, table->d_ff, T, k);
   if (ws_bytes < ws.bytes) return COLI_E_WORKSPACE;
+  const int grouped = choose_grouped(table, T, k, path);
+  if (grouped < 0) return grouped;
   if ((rc = check_device())) return rc;
   coli::ForwardArgs a;
+  a.grouped = grouped == 1;
   a.table = table;
   a.xq = xq;
   a.xd = xd;
@@ -298,6 +314,22 @@ int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const flo
                      void* workspace, size_t ws_bytes, void* stream) {
   return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, nullptr,
                       nullptr, stream);
+}
+
+int coli_moe_forward_path(const coli_expert_table* table, const int8_t* xq, const float* xd,
+                          int64_t T, const int32_t* idx, const float* w, int32_t k, float* y,
+                          int accumulate, void* workspace, size_t ws_bytes, int32_t path,
+                          void* stream) {
+  if (path < COLI_PATH_AUTO || path > COLI_PATH_GROUPED) return COLI_E_INVAL;
+  return forward_impl(table, xq, xd, T, idx, w, k, y, accumulate, workspace, ws_bytes, nullptr,
+                      nullptr, stream, path);
+}
+
+int coli_moe_path(const coli_expert_table* table, int64_t T, int32_t k) {
+  int rc = table_check(table);
+  if (rc) return rc;
+  if (k < 1 || k > table->n_routed || k > COLI_MAX_TOPK || T < 0) return COLI_E_SHAPE;
+  return choose_grouped(table, T, k, COLI_PATH_AUTO) == 1 ? COLI_PATH_GROUPED : COLI_PATH_GEMV;
 }
 
 int coli_moe_forward_profiled(const coli_expert_table* table, const int8_t* xq, const float* xd,
@@ -391,6 +423,7 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
   }
   if (e != hipSuccess) return hip_fail(e);
   coli::ForwardArgs a;
+  a.grouped = choose_grouped(table, T, k, COLI_PATH_AUTO) == 1;
   a.table = table;
   a.xq = l.xq;
   a.xd = l.xd;

@@ -644,9 +644,7 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   const coli_moe_events& ev = f.events ? *f.events : no_events;
   hipError_t rc = record(ev.begin, s);
   if (rc != hipSuccess) return rc;
-  // the grouped matrix-core kernels read resident int4 tables only
-  const bool grouped = t.weight_bits == 4 && !t.slot_of && T >= kMfmaMinTokens &&
-                       mfma_path_fits(T, D, F, f.k, S);
+  const bool grouped = f.grouped;
   if (!f.dispatched) {
     // the GEMV path also needs the code sums of x; the grouped path does not
     rc = launch_dispatch(f.idx, T, f.k, E, S, ws.counts, ws.lists, ws.n_active, ws.active, ws.err,

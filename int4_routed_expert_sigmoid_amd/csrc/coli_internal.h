@@ -165,12 +165,14 @@ struct ForwardArgs {
   const coli_moe_trace* trace;   // may be null
   const coli_moe_events* events; // may be null
   bool dispatched;               // the workspace already holds dispatch + xsum8
+  bool grouped;                  // run the grouped matrix-core path (see choose_grouped)
 };
 hipError_t launch_moe_forward(const ForwardArgs& a, hipStream_t s);
 
-// Grouped (matrix-core) expert FFN, used from kMfmaMinTokens tokens per pass.
-constexpr int64_t kMfmaMinTokens = 128;
+// Grouped (matrix-core) expert FFN, used from COLI_GROUPED_MIN_TOKENS tokens per pass.
 bool mfma_path_fits(int64_t T, int64_t D, int64_t F, int k, int S);
+// Whether the grouped path applies to (table, T, k): resident int4 tables only.
+bool grouped_applies(const coli_expert_table& t, int64_t T, int k);
 int64_t mfma_max_chunks(int64_t T, int k, int E, int S);
 int mfma_quads_gate_up(int64_t F);
 int mfma_quads_down(int64_t D);

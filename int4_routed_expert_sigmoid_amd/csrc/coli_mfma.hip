@@ -745,6 +745,11 @@ bool mfma_path_fits(int64_t T, int64_t D, int64_t F, int k, int S) {
   return T * D * 2 < 0x7FFFFFFFll && P * F * 2 < 0x7FFFFFFFll && D % 64 == 0 && F % 32 == 0;
 }
 
+bool grouped_applies(const coli_expert_table& t, int64_t T, int k) {
+  return t.weight_bits == 4 && !t.slot_of && T >= 1 &&
+         mfma_path_fits(T, t.d_model, t.d_ff, k, t.n_shared);
+}
+
 int64_t mfma_max_chunks(int64_t T, int k, int E, int S) {
   return T * (int64_t)(k + S) / kChunk + (E + S);
 }

@@ -201,3 +201,25 @@ def test_tier_host_checks():
     assert L.coli_tier_fetch(ctypes.byref(t), ctypes.byref(st), ctypes.byref(_table(E=15)),
                              None) == coli.COLI_E_SHAPE
     assert L.coli_tier_status(None, None) == coli.COLI_E_INVAL
+
+
+def test_path_choice_host():
+    """The automatic path choice (host logic) and the path argument's checks."""
+    L = coli.lib()
+    t = _table(256, 1, 6144, 2048)
+    path = lambda tab, T, k=8: L.coli_moe_path(ctypes.byref(tab), T, k)
+    assert path(t, 1) == coli.COLI_PATH_GEMV
+    assert path(t, 13) == coli.COLI_PATH_GEMV
+    assert path(t, 14) == coli.COLI_PATH_GROUPED
+    assert path(t, 2048) == coli.COLI_PATH_GROUPED
+    assert path(_table(256, 1, 6144, 2048, bits=8), 2048) == coli.COLI_PATH_GEMV   # int8
+    assert path(_table(256, 1, 6144, 2048, slots=64, slot_of=FAKE), 2048) == coli.COLI_PATH_GEMV
+    assert path(t, 4, 0) == coli.COLI_E_SHAPE
+    ws = L.coli_moe_workspace_bytes(ctypes.byref(t), 4, 8)
+    f = L.coli_moe_forward_path
+    args = lambda tab, p: (ctypes.byref(tab), FAKE, FAKE, 4, FAKE, FAKE, 8, FAKE, 0, FAKE, ws, p,
+                           None)
+    assert f(*args(t, 3)) == coli.COLI_E_INVAL
+    assert f(*args(t, -1)) == coli.COLI_E_INVAL
+    t8 = _table(256, 1, 6144, 2048, bits=8)
+    assert f(*args(t8, coli.COLI_PATH_GROUPED)) == coli.COLI_E_SHAPE

@@ -1,6 +1,6 @@
 """Parity of the grouped (matrix-core) expert path against the oracle (GPU).
 
-From 128 tokens per pass the forward runs the grouped kernels: per active
+From COLI_GROUPED_MIN_TOKENS (14) tokens per pass the forward runs the grouped kernels: per active
 expert, chunks of up to 64 tokens against 64-row weight groups.  These tests
 check every int32 block partial, g, u, h, Q8(h) and per-pair output
 bit-for-bit, over routings that exercise full, partial and single-token
@@ -125,3 +125,48 @@ def test_grouped_full_shape_sampled(big, T):
                              idx[sample], wt[sample])
     assert_bitexact("y sample", g["y"][sample], ys)
     assert_within_tol("y sample", g["y"][sample], ys, A)
+
+
+def forward_on(table, w, path, xq, xd, idx, wt):
+    T = idx.shape[0]
+    ws = torch.empty(coli.coli_moe_workspace_bytes(table, T, w.k), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, w.D), dtype=torch.float32, device=dev)
+    coli.coli_moe_forward_path(table, xq, xd, idx, wt, y, ws, path)
+    assert coli.coli_moe_status(ws) == coli.COLI_OK
+    return y.cpu().numpy()
+
+
+def routed_batch(w, T, token0):
+    x, lg, b = synth.activations(w, T, token0), synth.logits(w, T, token0), synth.router_bias(w)
+    xq = torch.empty((T, w.D), dtype=torch.int8, device=dev)
+    xd = torch.empty((T, w.D // 32), dtype=torch.float32, device=dev)
+    coli.coli_quant_act_q8(to_dev(x), xq, xd)
+    idx = torch.empty((T, w.k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, w.k), dtype=torch.float32, device=dev)
+    coli.coli_route_topk(to_dev(lg), to_dev(b), w.k, idx, wt)
+    return xq, xd, idx, wt
+
+
+@pytest.mark.parametrize("T", [1, 4, 37, 64, 128, 300])
+def test_forced_paths_bit_identical(tiny, T):
+    """Both paths at every batch size, including the grouped path below its
+    automatic threshold and the GEMV above it: identical outputs, equal to
+    the oracle."""
+    w, table, ox = tiny
+    xq, xd, idx, wt = routed_batch(w, T, 1200)
+    y1 = forward_on(table, w, coli.COLI_PATH_GEMV, xq, xd, idx, wt)
+    y2 = forward_on(table, w, coli.COLI_PATH_GROUPED, xq, xd, idx, wt)
+    assert_bitexact("GEMV vs grouped", y1, y2)
+    xq_h, xd_h, idx_h, wt_h = (a.cpu().numpy() for a in (xq, xd, idx, wt))
+    yr, _ = oracle.moe_layer(ox.table_for(idx_h), w.E, w.S, xq_h, xd_h, idx_h, wt_h)
+    assert_bitexact("y vs oracle", y1, yr)
+
+
+@pytest.mark.parametrize("T", [16, 96])
+def test_forced_paths_full_shape(big, T):
+    table, _ = big
+    w = synth.WORKLOADS[3]
+    xq, xd, idx, wt = routed_batch(w, T, 1300)
+    y1 = forward_on(table, w, coli.COLI_PATH_GEMV, xq, xd, idx, wt)
+    y2 = forward_on(table, w, coli.COLI_PATH_GROUPED, xq, xd, idx, wt)
+    assert_bitexact("GEMV vs grouped, page shape", y1, y2)
