@@ -33,6 +33,10 @@ _SIG = {
     "orc_q4_quant_row": ([_P, _I64, _P, _P], None),
     "orc_q4_quant": ([_P, _I64, _I64, _P, _P], None),
     "orc_q8w_quant_row": ([_P, _I64, _P, _P], None),
+    "orc_q2_quant_row": ([_P, _I64, _P, _P], None),
+    "orc_q2_quant": ([_P, _I64, _I64, _P, _P], None),
+    "orc_pack_q2": ([_P, _I64, _P], None),
+    "orc_unpack_q2": ([_P, _I64, _P], None),
     "orc_q8w_quant": ([_P, _I64, _I64, _P, _P], None),
     "orc_pack_q4": ([_P, _I64, _P], None),
     "orc_unpack_q4": ([_P, _I64, _P], None),
@@ -63,10 +67,10 @@ def _ptr(a):
 
 
 def _container(q, bits):
-    """A weight container as the C side reads it: uint8 nibble pairs (bits 4)
-    or int8 codes (bits 8)."""
-    if bits == 4:
-        assert q.dtype == np.uint8, "the nibble container is uint8"
+    """A weight container as the C side reads it: uint8 nibble pairs (bits 4),
+    uint8 2-bit quadruples (bits 2) or int8 codes (bits 8)."""
+    if bits in (2, 4):
+        assert q.dtype == np.uint8, "the packed containers are uint8"
         return _c(q, np.uint8)
     assert bits == 8 and q.dtype == np.int8, "the int8 container is int8"
     return _c(q, np.int8)
@@ -90,7 +94,7 @@ class Expert:
     def quantize(cls, w_gate, w_up, w_down, orc=None, bits=4):
         """Quantise fp32 matrices with the oracle's per-row rule for `bits`."""
         orc = orc or get()
-        quant = orc.q4_quant if bits == 4 else orc.q8w_quant
+        quant = {4: orc.q4_quant, 8: orc.q8w_quant, 2: orc.q2_quant}[bits]
         gq, gs = quant(w_gate)
         uq, us = quant(w_up)
         dq, ds = quant(w_down)
@@ -194,6 +198,34 @@ class Oracle:
         s = np.empty(rows, dtype=np.float32)
         self.L.orc_q8w_quant(_ptr(w), rows, k, _ptr(q), _ptr(s))
         return q, s
+
+    def q2_quant_row(self, w):
+        w = _c(w, np.float32)
+        q = np.empty(w.shape, dtype=np.int8)
+        s = np.empty(1, dtype=np.float32)
+        self.L.orc_q2_quant_row(_ptr(w), w.size, _ptr(q), _ptr(s))
+        return q, float(s[0])
+
+    def q2_quant(self, w):
+        """w [rows][k] fp32 -> (packed uint8 [rows][k/4], s fp32 [rows])."""
+        w = _c(w, np.float32)
+        rows, k = w.shape
+        packed = np.empty((rows, k // 4), dtype=np.uint8)
+        s = np.empty(rows, dtype=np.float32)
+        self.L.orc_q2_quant(_ptr(w), rows, k, _ptr(packed), _ptr(s))
+        return packed, s
+
+    def pack_q2(self, q):
+        q = _c(q, np.int8)
+        out = np.empty(q.shape[:-1] + (q.shape[-1] // 4,), dtype=np.uint8)
+        self.L.orc_pack_q2(_ptr(q), q.size, _ptr(out))
+        return out
+
+    def unpack_q2(self, packed):
+        packed = _c(packed, np.uint8)
+        q = np.empty(packed.shape[:-1] + (packed.shape[-1] * 4,), dtype=np.int8)
+        self.L.orc_unpack_q2(_ptr(packed), q.size, _ptr(q))
+        return q
 
     def pack_q4(self, q):
         q = _c(q, np.int8)

@@ -137,6 +137,62 @@ void orc_q4_quant_row(const float* w, int64_t k, int8_t* q, float* s) {
   }
 }
 
+/* ------------------------------------------------------------------------
+ * Per-row symmetric int2, the narrowest packing the pages name next to int8
+ * and int4 (discuss.pytorch.kr, "colibri의 주요 기능", integer-dot bullet:
+ * the int8/int4/int2 packings match the int8 container bit for bit).
+ * Reading: the int4 rule with one level a side, s = max|w| / 1,
+ * q = lrintf(w / s) clamped to [-1, 1]; packed four 2-bit two's-complement
+ * fields per byte, the lowest bits holding the first column.  The container
+ * decodes all four field values (-2 included), like the nibble one.
+ */
+void orc_q2_quant_row(const float* w, int64_t k, int8_t* q, float* s) {
+  float amax = 0.0f;
+  for (int64_t j = 0; j < k; ++j) {
+    const float a = fabsf(w[j]);
+    if (a > amax) amax = a;
+  }
+  const float s2 = amax / 1.0f;
+  *s = s2;
+  for (int64_t j = 0; j < k; ++j) {
+    long v = 0;
+    if (s2 != 0.0f) v = lrintf(w[j] / s2);
+    if (v > 1) v = 1;
+    if (v < -1) v = -1;
+    q[j] = (int8_t)v;
+  }
+}
+
+void orc_pack_q2(const int8_t* q, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n / 4; ++i) {
+    uint8_t byte = 0;
+    for (int j = 0; j < 4; ++j) byte |= (uint8_t)(((uint8_t)q[4 * i + j] & 3u) << (2 * j));
+    out[i] = byte;
+  }
+}
+
+/* Two's-complement 2-bit field f -> f - 4 if f >= 2. */
+void orc_unpack_q2(const uint8_t* in, int64_t n, int8_t* q) {
+  for (int64_t i = 0; i < n / 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int f = (in[i] >> (2 * j)) & 3;
+      q[4 * i + j] = (int8_t)(f >= 2 ? f - 4 : f);
+    }
+}
+
+void orc_q2_quant(const float* w, int64_t rows, int64_t k, uint8_t* packed, float* s) {
+#pragma omp parallel
+  {
+    int8_t* q = (int8_t*)malloc((size_t)k);
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+      orc_q2_quant_row(w + r * k, k, q, s + r);
+      orc_pack_q2(q, k, packed + r * (k / 4));
+    }
+    free(q);
+  }
+}
+
 /* Signed nibbles packed two per U8 byte, low nibble = even column. */
 void orc_pack_q4(const int8_t* q, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n / 2; ++i)
@@ -236,7 +292,8 @@ void orc_route(const float* logits, const float* bias, int64_t T, int32_t E, int
  * Integer dot of one weight row with a Q8 vector, per block of 32:
  * P_b = sum_j q_w * q_x, exact in int32 (|P_b| <= 32*127*127).  bits = 4:
  * the row is the nibble container (k/2 bytes); bits = 8: the int8 container
- * (k bytes, one code per column).
+ * (k bytes, one code per column); bits = 2: four 2-bit fields per byte
+ * (k/4 bytes).
  */
 void orc_row_partials(const uint8_t* wrow, int bits, const int8_t* xq, int64_t k, int32_t* P) {
   for (int64_t b = 0; b < k / 32; ++b) {
@@ -244,6 +301,14 @@ void orc_row_partials(const uint8_t* wrow, int bits, const int8_t* xq, int64_t k
     if (bits == 8) {
       const int8_t* w8 = (const int8_t*)wrow + 32 * b;
       for (int j = 0; j < 32; ++j) acc += (int32_t)w8[j] * (int32_t)xq[32 * b + j];
+      P[b] = acc;
+      continue;
+    }
+    if (bits == 2) {
+      for (int j = 0; j < 32; ++j) {
+        const int f = (wrow[(32 * b + j) / 4] >> (2 * (j % 4))) & 3;
+        acc += (f >= 2 ? f - 4 : f) * (int32_t)xq[32 * b + j];
+      }
       P[b] = acc;
       continue;
     }

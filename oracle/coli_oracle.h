@@ -44,6 +44,14 @@ void orc_q4_quant(const float* w, int64_t rows, int64_t k, uint8_t* packed, floa
 void orc_q8w_quant_row(const float* w, int64_t k, int8_t* q, float* s);
 void orc_q8w_quant(const float* w, int64_t rows, int64_t k, int8_t* q, float* s);
 
+/* per-row symmetric int2: s = max|w| / 1, q = lrintf(w / s) in [-1, 1];
+ * 2-bit container: byte i = sum_j (q[4i+j] & 3) << 2j; decode maps field
+ * f >= 2 to f - 4. */
+void orc_q2_quant_row(const float* w, int64_t k, int8_t* q, float* s);
+void orc_q2_quant(const float* w, int64_t rows, int64_t k, uint8_t* packed, float* s);
+void orc_pack_q2(const int8_t* q, int64_t n, uint8_t* out);
+void orc_unpack_q2(const uint8_t* in, int64_t n, int8_t* q);
+
 /* nibble container: byte i = (q[2i] & 15) | (q[2i+1] & 15) << 4. */
 void orc_pack_q4(const int8_t* q, int64_t n, uint8_t* out);
 void orc_unpack_q4(const uint8_t* in, int64_t n, int8_t* q);
@@ -53,9 +61,10 @@ void orc_unpack_q4(const uint8_t* in, int64_t n, int8_t* q);
 void orc_route(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
                float routed_scale, int32_t* idx, float* w);
 
-/* Weight matrices come in one of two containers, named by `bits`: 4 = the
+/* Weight matrices come in one of three containers, named by `bits`: 4 = the
  * nibble container (k/2 bytes per row), 8 = the int8 container (k bytes per
- * row, one int8 code per column).  Scales are one f32 per row in both. */
+ * row, one int8 code per column), 2 = the 2-bit container (k/4 bytes per
+ * row).  Scales are one f32 per row in all three. */
 
 /* int32 block partials of one weight row with a Q8 vector: P[k/32]. */
 void orc_row_partials(const uint8_t* wrow, int bits, const int8_t* xq, int64_t k, int32_t* P);

@@ -59,9 +59,25 @@ def load_golden(name):
     return rows
 
 
+def unpack2_ref(packed):
+    """[..., k/4] bytes -> [..., k] int64: 2-bit fields, lowest bits first,
+    sign-extended by shifting the field to the top of an int32 and back."""
+    b = packed.astype(np.int64)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 4,), dtype=np.int64)
+    for j in range(4):
+        f = ((b >> (2 * j)) & 3).astype(np.int32)
+        out[..., j::4] = (np.left_shift(f, 30) >> 30).astype(np.int64)
+    return out
+
+
 def codes_of(Wq, bits=4):
-    """The integer codes of a weight container: nibbles (bits 4) or int8 (bits 8)."""
-    return unpack_ref(Wq) if bits == 4 else Wq.view(np.int8).astype(np.int64)
+    """The integer codes of a weight container: nibbles (bits 4), 2-bit
+    fields (bits 2) or int8 (bits 8)."""
+    if bits == 4:
+        return unpack_ref(Wq)
+    if bits == 2:
+        return unpack2_ref(Wq)
+    return Wq.view(np.int8).astype(np.int64)
 
 
 def dot_ref64(Wq, Ws, xq, xd, bits=4):
@@ -301,7 +317,7 @@ def _silu64(g):
 
 
 def pin_expert_fp64(orc):
-    for bits, seed in ((4, 6), (8, 16)):
+    for bits, seed in ((4, 6), (8, 16), (2, 26)):
         _expert_fp64(orc, bits, np.random.default_rng(seed))
 
 
@@ -604,6 +620,65 @@ def pin_tier(orc):
     assert t.pin_top(12).tolist() == sorted(range(40), key=lambda e: (-int(u[e]), e))[:12]
 
 
+def pin_int2(orc):
+    """The 2-bit container: all 256 bytes decode like sign extension and
+    re-encode to themselves, a hand-packed byte, textbook ties of the int2
+    quantiser at s = 2^-2, brute-force partials over the full field range,
+    the fp64 dequantised matvec, and the same codes in the 2-bit, nibble and
+    int8 containers giving identical results (the pages' invariant)."""
+    from oracle import Expert
+    allb = np.arange(256, dtype=np.uint8)
+    un = orc.unpack_q2(allb)
+    assert np.array_equal(un.astype(np.int64), unpack2_ref(allb)), "unpack of all 256 bytes"
+    assert np.array_equal(orc.pack_q2(un), allb), "re-pack of all 256 bytes"
+    # codes 1, -1, 0, -2 -> fields 01, 11, 00, 10 from the lowest bits up
+    assert int(orc.pack_q2(np.array([1, -1, 0, -2], np.int8))[0]) == 0b10_00_11_01
+    mult = [0.5, -0.5, 0.75, -0.25, 1.0, -1.0, 0.0, 0.25]
+    q, sc = orc.q2_quant_row(np.array(mult, np.float32) * np.float32(0.25))
+    assert sc == 0.25 and [int(v) for v in q] == [0, 0, 1, 0, 1, -1, 0, 0], (sc, list(q))
+    q, sc = orc.q2_quant_row(np.full(32, -3.5, np.float32))
+    assert sc == 3.5 and np.all(q == -1)
+    q, sc = orc.q2_quant_row(np.zeros(32, np.float32))
+    assert sc == 0.0 and np.all(q == 0)
+    rng = np.random.default_rng(27)
+    w = (rng.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    packed, sc = orc.q2_quant(w)
+    qi = unpack2_ref(packed)
+    assert np.all(np.abs(qi) <= 1) and np.all(np.abs(qi).max(1) == 1), "int2 range / max"
+    ratio = (w / sc[:, None]).astype(np.float32).astype(np.float64)
+    assert np.all(np.abs(ratio - qi) <= 0.5), "int2 not nearest"
+    assert np.all(qi[np.abs(ratio - qi) == 0.5] % 2 == 0), "int2 tie not to even"
+    assert np.all(sc == np.abs(w).max(1)), "int2 scale"
+    for rows, k in ((7, 32), (33, 256), (64, 2048)):
+        q = rng.integers(-2, 2, size=(rows, k)).astype(np.int8)
+        xq = rng.integers(-127, 128, size=k).astype(np.int8)
+        xd = rng.uniform(0.01, 0.1, k // 32).astype(np.float32)
+        Ws = rng.uniform(0.5, 2.0, rows).astype(np.float32)
+        _, P, _ = orc.matvec(orc.pack_q2(q), Ws, xq, xd, want_partials=True, bits=2)
+        ref = np.einsum("rbj,bj->rb", q.astype(np.int64).reshape(rows, -1, 32),
+                        xq.astype(np.int64).reshape(-1, 32))
+        assert np.array_equal(P.astype(np.int64), ref), f"int2 partials {rows}x{k}"
+    w = (rng.standard_normal((64, 6144)) * 0.02).astype(np.float32)
+    Wq, Ws = orc.q2_quant(w)
+    xq, xd = orc.q8_quant(rng.standard_normal(6144).astype(np.float32))
+    y, _, _ = orc.matvec(Wq, Ws, xq, xd, bits=2)
+    ref, absterm, _ = dot_ref64(Wq, Ws, xq, xd, bits=2)
+    within_tol(y, ref, absterm, "int2 matvec")
+    D, F, E, k, T = 256, 128, 6, 2, 5
+    experts = {2: {}, 4: {}, 8: {}}
+    for e in range(E + 1):
+        mats = [rng.integers(-2, 2, size=shape).astype(np.int8) for shape in ((F, D), (F, D), (D, F))]
+        sc = [rng.uniform(1e-3, 1e-2, m.shape[0]).astype(np.float32) for m in mats]
+        experts[2][e] = Expert(*[a for m, s_ in zip(mats, sc) for a in (orc.pack_q2(m), s_)], bits=2)
+        experts[4][e] = Expert(*[a for m, s_ in zip(mats, sc) for a in (orc.pack_q4(m), s_)], bits=4)
+        experts[8][e] = Expert(*[a for m, s_ in zip(mats, sc) for a in (m, s_)], bits=8)
+    xq, xd = orc.q8_quant(rng.standard_normal((T, D)).astype(np.float32))
+    idx, wt = orc.route(rng.standard_normal((T, E)).astype(np.float32), np.zeros(E, np.float32), k)
+    y = {b: orc.moe_layer(experts[b], E, 1, xq, xd, idx, wt)[0] for b in (2, 4, 8)}
+    assert np.array_equal(y[2], y[8]) and np.array_equal(y[4], y[8]), "container identity"
+
+
 ALL_PINS = [pin_nibble_codec, pin_rint_ties, pin_quant_closed_forms, pin_partials_bruteforce,
             pin_dot_fp64, pin_exp, pin_route, pin_expert_fp64, pin_moe_invariants, pin_rmsnorm,
-            pin_dispatch, pin_router_logits, pin_int8_quant, pin_int8_container, pin_tier]
+            pin_dispatch, pin_router_logits, pin_int8_quant, pin_int8_container, pin_tier,
+            pin_int2]

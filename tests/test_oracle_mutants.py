@@ -64,6 +64,15 @@ MUTANTS = {
     "int8 partials read unsigned codes":
         ("const int8_t* w8 = (const int8_t*)wrow + 32 * b;", "const uint8_t* w8 = wrow + 32 * b;"),
     "int8 rows at the nibble stride": ("Wq + r * (k * bits / 8)", "Wq + r * (k / 2)"),
+    "int2 ties away from zero": ("if (s2 != 0.0f) v = lrintf(w[j] / s2);",
+                                 "if (s2 != 0.0f) v = lroundf(w[j] / s2);"),
+    "int2 scale over 2": ("const float s2 = amax / 1.0f;", "const float s2 = amax / 2.0f;"),
+    "int2 decode sign threshold": ("q[4 * i + j] = (int8_t)(f >= 2 ? f - 4 : f);",
+                                   "q[4 * i + j] = (int8_t)(f > 2 ? f - 4 : f);"),
+    "int2 dot reads fields unsigned": ("acc += (f >= 2 ? f - 4 : f) * (int32_t)xq[32 * b + j];",
+                                       "acc += f * (int32_t)xq[32 * b + j];"),
+    "int2 field order reversed": ("byte |= (uint8_t)(((uint8_t)q[4 * i + j] & 3u) << (2 * j));",
+                                  "byte |= (uint8_t)(((uint8_t)q[4 * i + j] & 3u) << (2 * (3 - j)));"),
     "tier evicts the most recently used": ("if (v < 0 || stamp[s] < stamp[v]) v = s;",
                                            "if (v < 0 || stamp[s] > stamp[v]) v = s;"),
     "tier evicts pinned slots": ("if (pinned[s] || stamp[s] >= step) continue;",
