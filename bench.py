@@ -46,8 +46,9 @@ def build_table(w, coli, synth, torch, layer=0, bits=4):
     table = coli.ExpertTable(w.E, w.S, w.D, w.F, weight_bits=bits)
     F, D = w.F, w.D
     scratch = torch.empty(F * D, dtype=torch.float32, device="cuda")
-    per, qdt = (2, torch.uint8) if bits == 4 else (1, torch.int8)
-    quant = coli.coli_quant_weight_q4 if bits == 4 else coli.coli_quant_weight_q8
+    quant, qdt, per = {4: (coli.coli_quant_weight_q4, torch.uint8, 2),
+                       8: (coli.coli_quant_weight_q8, torch.int8, 1),
+                       2: (coli.coli_quant_weight_q2, torch.uint8, 4)}[bits]
     q = [torch.empty((F, D // per), dtype=qdt, device="cuda") for _ in range(2)]
     q.append(torch.empty((D, F // per), dtype=qdt, device="cuda"))
     s = [torch.empty(F, dtype=torch.float32, device="cuda") for _ in range(2)]
@@ -196,6 +197,17 @@ def head_leg(coli, synth, torch, hev):
     table = build_table(synth.WORKLOADS[2], coli, synth, torch, layer=HEAD_LAYER, bits=8)
     res = {"workload": "int8 head d6144 f2048 e256+1 top8", "table_bytes": table.bytes}
     res.update(batch_leg(table, 8, (1, 2), coli, synth, torch, hev))
+    del table
+    torch.cuda.empty_cache()
+    return res
+
+
+def int2_leg(coli, synth, torch, hev):
+    """An int2 layer (2-bit weights, 2.43 GB table) at decode (1 token per
+    pass) and in the verify pass (4 tokens)."""
+    table = build_table(synth.WORKLOADS[2], coli, synth, torch, layer=2, bits=2)
+    res = {"workload": "int2 layer d6144 f2048 e256+1 top8", "table_bytes": table.bytes}
+    res.update(batch_leg(table, 2, (1, 2), coli, synth, torch, hev))
     del table
     torch.cuda.empty_cache()
     return res
@@ -449,7 +461,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch steps directly, no HIP graph")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="timed 2048-token passes of the prefill leg (0: skip it)")
-    ap.add_argument("--no-head", action="store_true", help="skip the int8 head leg")
+    ap.add_argument("--no-head", action="store_true", help="skip the int8 head and int2 legs")
     ap.add_argument("--no-tier", action="store_true", help="skip the expert-tier leg")
     ap.add_argument("--no-paths", action="store_true", help="skip the path-choice leg")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -611,6 +623,8 @@ def main():
     out["router_logits"] = router_leg(coli, synth, torch)
     if not args.no_head:
         out["int8_head"] = head_leg(coli, synth, torch, hev)
+    if not args.no_head:
+        out["int2"] = int2_leg(coli, synth, torch, hev)
     if not args.no_tier:
         out["tier"] = tier_leg(coli, synth, torch)
     if not args.no_cpu_baseline:

@@ -101,8 +101,19 @@ typedef enum {
  * byte j of a chunk is column 16c+j as a two's-complement int8.  gu_s and
  * dn_s are as above.  int8 tables run the GEMV kernels at every batch size.
  *
+ * int2 tables (weight_bits = 2; same page, integer-dot bullet: int8, int4 and
+ * int2 packings): codes in [-2, 1] (the quantiser produces [-1, 1]), a
+ * 16-byte chunk holds 64 columns (two blocks), so d_ff % 64 == 0:
+ *   gu_q  [E+S][F/32][D/64][64][16], dn_q  [E+S][D/64][F/64][64][16];
+ * 32-bit word m of a chunk holds columns 16m..16m+15: byte j has, from the
+ * lowest bits up, 2-bit fields for columns 16m+j, 16m+4+j, 16m+8+j and
+ * 16m+12+j, each stored as q + 2.  The canonical int2 container is
+ * [rows][k/4] bytes, byte i holding columns 4i..4i+3 from the lowest bits
+ * up in two's complement.  int2 tables run the GEMV kernels.
+ *
  * The shared expert (when S = 1) is index E.  E <= 256, S in {0, 1},
- * D % 64 == 0, F % 32 == 0, D and F <= COLI_MAX_DIM, weight_bits 4 or 8.
+ * D % 64 == 0, F % 32 == 0 (int2: F % 64 == 0), D and F <= COLI_MAX_DIM,
+ * weight_bits 2, 4 or 8.
  *
  * Expert tiers (see coli_tier_* below): with slot_of != NULL the four arrays
  * hold n_slots experts, and expert e lives at position slot_of[e] (a device
@@ -115,7 +126,7 @@ typedef struct {
   int32_t n_shared;    /* S */
   int32_t d_model;     /* D */
   int32_t d_ff;        /* F */
-  int32_t weight_bits; /* 4: nibble-packed int4 codes; 8: int8 codes */
+  int32_t weight_bits; /* 4: nibble-packed int4; 8: int8; 2: 2-bit fields */
   uint8_t* gu_q;
   float* gu_s;
   uint8_t* dn_q;
@@ -162,6 +173,14 @@ int coli_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, fl
  * -127, 127), an all-zero row gives s = 0 and q = 0.  w [rows][k] f32 ->
  * q [rows][k] int8 and s [rows] f32.  k % 32 == 0. */
 int coli_quant_weight_q8(const float* w, int64_t rows, int64_t k, int8_t* q, float* s,
+                         void* stream);
+
+/* Per-row symmetric int2 into the 2-bit container (discuss.pytorch.kr colibri
+ * summary, "colibri의 주요 기능", integer-dot bullet): s = max|w| / 1.0f,
+ * q = clamp(rint_half_even(w / s), -1, 1), an all-zero row gives s = 0 and
+ * q = 0.  w [rows][k] f32 -> q [rows][k/4] bytes (byte i: columns 4i..4i+3,
+ * lowest bits first, two's complement) and s [rows] f32.  k % 32 == 0. */
+int coli_quant_weight_q2(const float* w, int64_t rows, int64_t k, uint8_t* q, float* s,
                          void* stream);
 
 /* Fused RMSNorm (unit gain) + Q8_0 of the normalised vector, for a pre-norm

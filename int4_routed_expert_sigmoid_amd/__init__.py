@@ -30,7 +30,7 @@ COLI_MAX_TOPK = 64
 
 EXPORTED = [
     "coli_table_bytes", "coli_table_set_expert", "coli_quant_act_q8", "coli_quant_weight_q4",
-    "coli_quant_weight_q8",
+    "coli_quant_weight_q8", "coli_quant_weight_q2",
     "coli_rmsnorm_q8", "coli_route_topk", "coli_router_logits", "coli_dispatch",
     "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
@@ -96,6 +96,7 @@ def lib():
             "coli_quant_act_q8": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
             "coli_quant_weight_q4": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
             "coli_quant_weight_q8": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+            "coli_quant_weight_q2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
             "coli_rmsnorm_q8": ([_P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
             "coli_route_topk": ([_P, _P, _I64, _I32, _I32, ctypes.c_float, _P, _P, _P],
                                 ctypes.c_int),
@@ -163,7 +164,7 @@ def _dtype(t, dt, name):
 # --------------------------------------------------------------------------- table
 class ExpertTable:
     """A device-resident expert table (torch-allocated) and its C descriptor.
-    weight_bits 4: int4 nibble codes; 8: int8 codes (the int8 head)."""
+    weight_bits 4: int4 nibble codes; 8: int8 codes (the int8 head); 2: 2-bit codes."""
 
     def __init__(self, n_routed: int, n_shared: int, d_model: int, d_ff: int, device="cuda",
                  weight_bits: int = 4, _arrays=None):
@@ -300,6 +301,14 @@ def coli_quant_weight_q8(w, q, s, stream=None):
     rows, k = w.shape
     _check("coli_quant_weight_q8",
            lib().coli_quant_weight_q8(_ptr(w), rows, k, _ptr(q), _ptr(s), _stream(stream)))
+
+
+def coli_quant_weight_q2(w, q, s, stream=None):
+    import torch
+    _dtype(w, torch.float32, "w"); _dtype(q, torch.uint8, "q"); _dtype(s, torch.float32, "s")
+    rows, k = w.shape
+    _check("coli_quant_weight_q2",
+           lib().coli_quant_weight_q2(_ptr(w), rows, k, _ptr(q), _ptr(s), _stream(stream)))
 
 
 def coli_rmsnorm_q8(h, eps, q, d, r_out=None, stream=None):

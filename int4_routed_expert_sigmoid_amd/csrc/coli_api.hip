@@ -55,7 +55,8 @@ int table_check(const coli_expert_table* t) {
   if (t->d_model <= 0 || t->d_model % 64 != 0 || t->d_ff <= 0 || t->d_ff % 32 != 0)
     return COLI_E_SHAPE;
   if (t->d_model > COLI_MAX_DIM || t->d_ff > COLI_MAX_DIM) return COLI_E_SHAPE;
-  if (t->weight_bits != 4 && t->weight_bits != 8) return COLI_E_SHAPE;
+  if (t->weight_bits != 2 && t->weight_bits != 4 && t->weight_bits != 8) return COLI_E_SHAPE;
+  if (t->weight_bits == 2 && t->d_ff % 64) return COLI_E_SHAPE;   // int2 chunks: 64 columns
   if (t->slot_of && (t->n_slots < 1 || t->n_slots > t->n_routed + t->n_shared))
     return COLI_E_SHAPE;
   if (t->slot_of && !al4(t->slot_of)) return COLI_E_INVAL;
@@ -125,7 +126,8 @@ int coli_last_hip_error(void) { return g_last_hip_error; }
 size_t coli_table_bytes(int32_t E, int32_t S, int64_t D, int64_t F, int32_t bits, size_t* gu_q,
                         size_t* gu_s, size_t* dn_q, size_t* dn_s) {
   if (E < 1 || E > COLI_MAX_EXPERTS || S < 0 || S > 1 || D <= 0 || D % 64 || F <= 0 || F % 32 ||
-      D > COLI_MAX_DIM || F > COLI_MAX_DIM || (bits != 4 && bits != 8))
+      D > COLI_MAX_DIM || F > COLI_MAX_DIM || (bits != 2 && bits != 4 && bits != 8) ||
+      (bits == 2 && F % 64))
     return 0;
   const size_t n = (size_t)(E + S);
   const size_t a = n * (size_t)(D * F * bits / 4), b = n * (size_t)(2 * F) * sizeof(float),
@@ -175,6 +177,19 @@ int coli_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8_t* q, fl
   int rc = check_device();
   if (rc) return rc;
   hipError_t e = coli::launch_quant_weight_q4(w, rows, k, q, s, as_stream(stream));
+  return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_quant_weight_q2(const float* w, int64_t rows, int64_t k, uint8_t* q, float* s,
+                         void* stream) {
+  if (rows < 0 || k <= 0 || k % 32) return COLI_E_SHAPE;
+  if (rows > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (rows == 0) return COLI_OK;
+  if (!w || !q || !s) return COLI_E_INVAL;
+  if (!al16(w) || !al4(q) || !al4(s)) return COLI_E_INVAL;
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = coli::launch_quant_weight_q2(w, rows, k, q, s, as_stream(stream));
   return e == hipSuccess ? COLI_OK : hip_fail(e);
 }
 
@@ -468,7 +483,7 @@ size_t coli_tier_table_bytes(int32_t slots, int64_t D, int64_t F, int32_t bits, 
                              size_t* gu_s, size_t* dn_q, size_t* dn_s) {
   if (slots < 1 || slots > COLI_MAX_EXPERTS + 1) return 0;
   if (D <= 0 || D % 64 || F <= 0 || F % 32 || D > COLI_MAX_DIM || F > COLI_MAX_DIM) return 0;
-  if (bits != 4 && bits != 8) return 0;
+  if ((bits != 2 && bits != 4 && bits != 8) || (bits == 2 && F % 64)) return 0;
   const size_t n = (size_t)slots;
   const size_t a = n * (size_t)(D * F * bits / 4), b = n * (size_t)(2 * F) * sizeof(float),
                c = n * (size_t)(D * F * bits / 8), d = n * (size_t)D * sizeof(float);

@@ -26,9 +26,11 @@
 //
 // int8 tables (the int8 speculative head: discuss.pytorch.kr colibri summary,
 // "colibri의 주요 기능", MTP bullet; jeff.news, MTP section) run the same
-// kernels with two 1 KB wavefront loads per 32-column block (U = 2 chunks):
-// the codes are already signed bytes, so they go to v_dot4_i32_i8 as loaded
-// and the block dot starts from 0.
+// kernels with two 1 KB wavefront loads per 32-column block: the codes are
+// already signed bytes, so they go to v_dot4_i32_i8 as loaded and the block
+// dot starts from 0.  int2 tables (same page, integer-dot bullet: int8/int4/
+// int2 packings) hold two blocks per 1 KB wavefront load; their 2-bit fields
+// are stored q + 2 and the block dot starts from -2 sum x.
 //
 // The SwiGLU, the row scale and the Q8_0 re-quantisation of h are fused into
 // the gate/up epilogue; the routing-weighted combine runs as its own kernel in
@@ -104,6 +106,14 @@ __device__ __forceinline__ int storage_of(const int32_t* slot_of, int n_store, i
   }
   return p;
 }
+
+// 16-byte chunks per 32-column block (int4: 1, int8: 2); int2 packs two
+// blocks in a chunk and has its own loop.
+constexpr int chunks_per_block(int bits) { return bits == 8 ? 2 : 1; }
+// Blocks in flight in a ring of pf chunks.
+constexpr int blocks_per_ring(int pf, int bits) { return bits == 8 ? pf / 2 : bits == 4 ? pf : 2 * pf; }
+// Chunks of a row group of nb blocks.
+constexpr int row_chunks(int nb, int bits) { return bits == 8 ? 2 * nb : bits == 4 ? nb : nb / 2; }
 
 // The 32 weight codes of one block as the 8 byte-vectors that line up with
 // the 8 int8 words of the activation block (offset-binary nibbles for int4,
@@ -228,19 +238,22 @@ __device__ __forceinline__ void clear_tail_records(int NB, int pb, int tid, int 
   for (int i = tid; i < n; i += nth) tail[i] = make_uint4(0, 0, 0, 0);
 }
 
+// The block's sum term is staged as -8 sum x (int4: nibbles are q + 8) or
+// -2 sum x (int2: fields are q + 2; sum_shift 2, exact since -8 sum x is a
+// multiple of 8); int8 blocks do not use it.
 template <int MAXT>
 __device__ __forceinline__ void stage_token(unsigned char* lds, int j,
                                             const int8_t* __restrict__ xrow,
                                             const float* __restrict__ drow,
                                             const int32_t* __restrict__ srow, int NB, int tid,
-                                            int nth) {
+                                            int nth, int sum_shift) {
   constexpr int R = PassLds<MAXT>::R;
   const uint4* xg = reinterpret_cast<const uint4*>(xrow);
   for (int i = tid; i < 2 * NB; i += nth)
     *reinterpret_cast<uint4*>(lds + (size_t)(i >> 1) * R + 32 * j + 16 * (i & 1)) = xg[i];
   for (int b = tid; b < NB; b += nth)
     *reinterpret_cast<float2*>(lds + (size_t)b * R + PassLds<MAXT>::DM + 8 * j) =
-        make_float2(drow[b], __int_as_float(srow[b]));
+        make_float2(drow[b], __int_as_float(srow[b] >> sum_shift));
 }
 
 struct XBlock {
@@ -367,6 +380,79 @@ __device__ __forceinline__ void stream_rows(Ring<PF>& ring, float* acc,
   }
 }
 
+// int2: one 16-byte chunk holds two blocks (64 columns).  Word m of the
+// chunk covers columns 16m..16m+15; its byte j holds, from the lowest bits
+// up, 2-bit fields for columns 16m + 4i + j (i = 0..3), offset binary
+// (q + 2), so (w >> 2i) & 0x03030303 is the byte vector of activation word
+// 4m + i.  The first split of each word writes fresh registers (early
+// clobber), which ends the ring slot's live range before its refill.
+__device__ __forceinline__ void split_pairs(uint32_t w, uint32_t& f0, uint32_t& t) {
+  asm volatile("v_and_b32 %0, 0x3030303, %2\n\tv_lshrrev_b32 %1, 2, %2"
+               : "=&v"(f0), "=&v"(t)
+               : "v"(w));
+}
+
+__device__ __forceinline__ void unpack_int2(u32x4 w, Unpacked* u) {
+  const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint32_t t;
+    Unpacked& ub = u[m >> 1];
+    const int base = 4 * (m & 1);
+    split_pairs(word[m], ub.v[base], t);
+    ub.v[base + 1] = t & 0x03030303u;
+    ub.v[base + 2] = (t >> 2) & 0x03030303u;
+    ub.v[base + 3] = (t >> 4) & 0x03030303u;
+  }
+}
+
+// stream_rows for int2 tables: ring slot i holds blocks 2i and 2i + 1 of the
+// ring pass, so PF chunks are 2 PF blocks in flight.  The block dot starts
+// from the staged -2 sum x (codes are stored as q + 2).
+template <int NT, int MAXT, int PF, bool TRACE>
+__device__ __forceinline__ void stream_rows2(Ring<PF>& ring, float* acc,
+                                             int32_t* const* trace_row) {
+  constexpr int PB = 2 * PF;
+  constexpr int R = PassLds<MAXT>::R;
+  const unsigned char* lds = gemv_lds();
+  const int NU = ring.NU;
+  const int NB = 2 * NU;
+  XBlock cur[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) cur[j] = read_xblock<MAXT>(lds, j);
+  for (int b0 = 0; b0 < NB; b0 += PB) {
+    const unsigned char* rec = lds + (size_t)b0 * R;
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      Unpacked u[2];
+      unpack_int2(ring.buf[i], u);
+      __builtin_amdgcn_sched_barrier(0);
+      const int c = b0 / 2 + i + PF;
+      ring.buf[i] = __builtin_amdgcn_raw_buffer_load_b128(ring.rsrc, ring.loff,
+                                                          (c < NU ? c : NU - 1) * 1024,
+                                                          kNonTemporal);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = b0 + 2 * i + h;
+        XBlock nxt[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) nxt[j] = read_xblock<MAXT>(rec + (2 * i + h + 1) * R, j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int p = block_dot<1>(u[h], cur[j]);
+          if (TRACE) {
+            if (trace_row[j] && b < NB) trace_row[j][b] = p;
+          }
+          acc[j] = __builtin_fmaf((float)p, cur[j].dm.x, acc[j]);
+          cur[j] = nxt[j];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
 // Token slots a pass of nt tokens computes: the next power of two (at most
 // MAXT); slots from nt on repeat the last token and their results are unused.
 template <int MAXT>
@@ -374,15 +460,26 @@ __device__ __forceinline__ int pass_slots(int nt) {
   return (MAXT >= 8 && nt > 4) ? 8 : (MAXT >= 4 && nt > 2) ? 4 : (MAXT >= 2 && nt == 2) ? 2 : 1;
 }
 
-// Runs stream_rows for the nt (1..MAXT) tokens of one pass.
-template <int MAXT, int PF, int U, bool TRACE>
+// Runs the loop of the table's container for NT token slots.
+template <int NT, int MAXT, int PF, int BITS, bool TRACE>
+__device__ __forceinline__ void stream_slots(Ring<PF>& ring, float* acc,
+                                             int32_t* const* trace_row) {
+  if constexpr (BITS == 2) {
+    stream_rows2<NT, MAXT, PF, TRACE>(ring, acc, trace_row);
+  } else {
+    stream_rows<NT, MAXT, PF, chunks_per_block(BITS), TRACE>(ring, acc, trace_row);
+  }
+}
+
+// Runs the loop for the nt (1..MAXT) tokens of one pass.
+template <int MAXT, int PF, int BITS, bool TRACE>
 __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
                                             int32_t* const* trace_row) {
   switch (pass_slots<MAXT>(nt)) {
-    case 8: stream_rows<(MAXT >= 8 ? 8 : 1), MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
-    case 4: stream_rows<(MAXT >= 4 ? 4 : 1), MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
-    case 2: stream_rows<(MAXT >= 2 ? 2 : 1), MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
-    default: stream_rows<1, MAXT, PF, U, TRACE>(ring, acc, trace_row); break;
+    case 8: stream_slots<(MAXT >= 8 ? 8 : 1), MAXT, PF, BITS, TRACE>(ring, acc, trace_row); break;
+    case 4: stream_slots<(MAXT >= 4 ? 4 : 1), MAXT, PF, BITS, TRACE>(ring, acc, trace_row); break;
+    case 2: stream_slots<(MAXT >= 2 ? 2 : 1), MAXT, PF, BITS, TRACE>(ring, acc, trace_row); break;
+    default: stream_slots<1, MAXT, PF, BITS, TRACE>(ring, acc, trace_row); break;
   }
 }
 
@@ -394,7 +491,7 @@ __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
 // and stores nothing.
 constexpr int gemv_waves(int maxt) { return maxt >= 4 ? 4 : 1; }
 
-template <int MAXT, int PF, int U, bool TRACE>
+template <int MAXT, int PF, int BITS, bool TRACE>
 __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a) {
   constexpr int W = gemv_waves(MAXT);
   const int slot = blockIdx.y;
@@ -410,12 +507,12 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
   const int KS = a.k + a.S;
   const int es = storage_of(a.slot_of, a.n_store, e, a.err);
   if (es < 0) return;                    // uniform across the workgroup
-  const int NU = U * NB;                 // 1 KB chunks in the row group
+  const int NU = row_chunks(NB, BITS);   // 1 KB chunks in the row group
   const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)es * G + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
-  clear_tail_records<MAXT>(NB, PF / U, threadIdx.x, kWave * W);
+  clear_tail_records<MAXT>(NB, blocks_per_ring(PF, BITS), threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const float rs = a.gu_s[((size_t)es * G + grp) * kWave + lane];
   const cptr<int32_t> list = as_const(a.lists + (size_t)e * a.T);
@@ -443,14 +540,14 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
       if (j < ns) {
         const int64_t t = __builtin_amdgcn_readfirstlane(pair[j] / KS);
         stage_token<MAXT>(gemv_lds(), j, a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB,
-                          threadIdx.x, kWave * W);
+                          threadIdx.x, kWave * W, BITS == 2 ? 2 : 0);
       }
     }
     __syncthreads();
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, U, TRACE>(nt, ring, acc, trow);
+    stream_pass<MAXT, PF, BITS, TRACE>(nt, ring, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
       if (j < nt) {
@@ -501,7 +598,7 @@ __device__ __forceinline__ float combine_row(const float* __restrict__ o,
   return acc;
 }
 
-template <int MAXT, int PF, int U, bool TRACE>
+template <int MAXT, int PF, int BITS, bool TRACE>
 __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   constexpr int W = gemv_waves(MAXT);
   const int slot = blockIdx.y;
@@ -514,7 +611,7 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   const bool live = (int64_t)blockIdx.x * W + wave < G;
   const int grp = live ? (int)blockIdx.x * W + wave : (int)G - 1;
   const int NB = (int)(a.F / 32);
-  const int NU = U * NB;
+  const int NU = row_chunks(NB, BITS);
   const int es = storage_of(a.slot_of, a.n_store, e, a.err);
   if (es < 0) return;                    // uniform across the workgroup
   const char* wbase =
@@ -522,7 +619,7 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   const uint32_t loff = 16u * (uint32_t)lane;
   Ring<PF> ring;
   ring.start(wbase, loff, NU);          // the weight stream starts before anything else
-  clear_tail_records<MAXT>(NB, PF / U, threadIdx.x, kWave * W);
+  clear_tail_records<MAXT>(NB, blocks_per_ring(PF, BITS), threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
   const float rs = a.dn_s[(size_t)es * a.D + row];
@@ -546,14 +643,14 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
       if (j < ns) {
         const size_t p = (size_t)__builtin_amdgcn_readfirstlane(pair[j]);
         stage_token<MAXT>(gemv_lds(), j, a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB,
-                          threadIdx.x, kWave * W);
+                          threadIdx.x, kWave * W, BITS == 2 ? 2 : 0);
       }
     }
     __syncthreads();
     float acc[MAXT];
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) acc[j] = 0.0f;
-    stream_pass<MAXT, PF, U, TRACE>(nt, ring, acc, trow);
+    stream_pass<MAXT, PF, BITS, TRACE>(nt, ring, acc, trow);
 #pragma unroll
     for (int j = 0; j < MAXT; ++j)
       if (live && j < nt) a.o[(size_t)pair[j] * a.D + row] = acc[j] * rs;
@@ -582,54 +679,57 @@ hipError_t record(void* ev, hipStream_t s) {
 
 // Weight loads (1 KB per wavefront) in flight per wavefront, by tokens per
 // pass and 16-byte chunks per block.
-constexpr int pf_gate_up(int maxt, int u) { return maxt > 0 && u > 0 ? 16 : 0; }
-constexpr int pf_down(int maxt, int u) { return maxt > 0 && u > 0 ? 8 : 0; }
+constexpr int pf_gate_up(int maxt, int bits) { return maxt > 0 && bits > 0 ? 16 : 0; }
+constexpr int pf_down(int maxt, int bits) { return maxt > 0 && bits > 0 ? 8 : 0; }
 constexpr size_t kLdsLimit = 65536;
 
-template <int MAXT, int U, bool TRACE>
+template <int MAXT, int BITS, bool TRACE>
 hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
-  const size_t lds_gu = pass_lds_bytes(MAXT, g.D / 32, pf_gate_up(MAXT, U) / U);
-  const size_t lds_dn = pass_lds_bytes(MAXT, d.F / 32, pf_down(MAXT, U) / U);
+  constexpr int PG = pf_gate_up(MAXT, BITS), PD = pf_down(MAXT, BITS);
+  const size_t lds_gu = pass_lds_bytes(MAXT, g.D / 32, blocks_per_ring(PG, BITS));
+  const size_t lds_dn = pass_lds_bytes(MAXT, d.F / 32, blocks_per_ring(PD, BITS));
   constexpr int W = gemv_waves(MAXT);
-  hipLaunchKernelGGL((gate_up_kernel<MAXT, pf_gate_up(MAXT, U), U, TRACE>),
+  hipLaunchKernelGGL((gate_up_kernel<MAXT, PG, BITS, TRACE>),
                      dim3((unsigned)((g.F / 32 + W - 1) / W), maxA), dim3(kWave * W), lds_gu, s, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev_down, s)) != hipSuccess) return rc;
-  hipLaunchKernelGGL((down_kernel<MAXT, pf_down(MAXT, U), U, TRACE>),
+  hipLaunchKernelGGL((down_kernel<MAXT, PD, BITS, TRACE>),
                      dim3((unsigned)((d.D / 64 + W - 1) / W), maxA), dim3(kWave * W), lds_dn, s, d);
   return hipGetLastError();
 }
 
 // Tokens per pass: the batch (a power of two up to 8), capped so that the
 // pass's LDS token records fit in 64 KB in both kernels.
-int pass_tokens(int64_t T, int64_t D, int64_t F, int U) {
+int pass_tokens(int64_t T, int64_t D, int64_t F, int bits) {
   int m = T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8;
   auto fits = [&](int mt) {
-    return pass_lds_bytes(mt, D / 32, pf_gate_up(mt, U) / U) <= kLdsLimit &&
-           pass_lds_bytes(mt, F / 32, pf_down(mt, U) / U) <= kLdsLimit;
+    return pass_lds_bytes(mt, D / 32, blocks_per_ring(pf_gate_up(mt, bits), bits)) <= kLdsLimit &&
+           pass_lds_bytes(mt, F / 32, blocks_per_ring(pf_down(mt, bits), bits)) <= kLdsLimit;
   };
   while (m > 1 && !fits(m)) m /= 2;
   return m;
 }
 
-template <int U, bool TRACE>
-hipError_t launch_gemv_u(const GuArgs& g, const DnArgs& d, int maxA, int64_t T, void* ev_down,
-                         hipStream_t s) {
-  switch (pass_tokens(T, g.D, g.F, U)) {
-    case 1: return launch_pair<1, U, TRACE>(g, d, maxA, ev_down, s);
-    case 2: return launch_pair<2, U, TRACE>(g, d, maxA, ev_down, s);
-    case 4: return launch_pair<4, U, TRACE>(g, d, maxA, ev_down, s);
-    default: return launch_pair<8, U, TRACE>(g, d, maxA, ev_down, s);
+template <int BITS, bool TRACE>
+hipError_t launch_gemv_bits(const GuArgs& g, const DnArgs& d, int maxA, int64_t T,
+                            void* ev_down, hipStream_t s) {
+  switch (pass_tokens(T, g.D, g.F, BITS)) {
+    case 1: return launch_pair<1, BITS, TRACE>(g, d, maxA, ev_down, s);
+    case 2: return launch_pair<2, BITS, TRACE>(g, d, maxA, ev_down, s);
+    case 4: return launch_pair<4, BITS, TRACE>(g, d, maxA, ev_down, s);
+    default: return launch_pair<8, BITS, TRACE>(g, d, maxA, ev_down, s);
   }
 }
 
-// U = 16-byte chunks per 32-column block: 1 for int4 tables, 2 for int8.
 template <bool TRACE>
 hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int bits, int maxA, int64_t T,
                        void* ev_down, hipStream_t s) {
-  return bits == 8 ? launch_gemv_u<2, TRACE>(g, d, maxA, T, ev_down, s)
-                   : launch_gemv_u<1, TRACE>(g, d, maxA, T, ev_down, s);
+  switch (bits) {
+    case 8: return launch_gemv_bits<8, TRACE>(g, d, maxA, T, ev_down, s);
+    case 2: return launch_gemv_bits<2, TRACE>(g, d, maxA, T, ev_down, s);
+    default: return launch_gemv_bits<4, TRACE>(g, d, maxA, T, ev_down, s);
+  }
 }
 
 }  // namespace

@@ -117,6 +117,8 @@ hipError_t launch_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8
                                   hipStream_t s);
 hipError_t launch_quant_weight_q8(const float* w, int64_t rows, int64_t k, int8_t* q, float* sc,
                                   hipStream_t s);
+hipError_t launch_quant_weight_q2(const float* w, int64_t rows, int64_t k, uint8_t* q, float* sc,
+                                  hipStream_t s);
 hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const uint8_t* gate_q,
                                    const float* gate_s, const uint8_t* up_q, const float* up_s,
                                    const uint8_t* down_q, const float* down_s, hipStream_t s);

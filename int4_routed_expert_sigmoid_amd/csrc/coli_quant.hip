@@ -117,6 +117,70 @@ __global__ void __launch_bounds__(256) quant_weight_q8_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
+// Per-row int2 (the narrowest packing next to int8 and int4): s = max|w| / 1,
+// q = rint_half_even(w / s) in [-1, 1], four 2-bit two's-complement fields
+// per byte, the lowest bits holding the first column.  One 256-thread
+// workgroup per row, 16 columns per 32-bit word.
+__device__ __forceinline__ uint32_t q2_code(float v, float s) {
+  if (s == 0.0f) return 0;
+  float q = __builtin_rintf(v / s);
+  q = q > 1.0f ? 1.0f : q;
+  q = q < -1.0f ? -1.0f : q;
+  return (uint32_t)(int)q & 3u;
+}
+
+__global__ void __launch_bounds__(256) quant_weight_q2_kernel(const float* __restrict__ w,
+                                                              int64_t k, uint32_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const float4* wr = reinterpret_cast<const float4*>(w + row * k);
+  float amax = 0.0f;
+  for (int64_t c = threadIdx.x; c < k / 4; c += 256) {
+    const float4 v = wr[c];
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  amax = block_max_256(amax, red);
+  const float sc = amax / 1.0f;
+  if (threadIdx.x == 0) s[row] = sc;
+  uint32_t* qr = q + row * (k / 16);
+  for (int64_t c = threadIdx.x; c < k / 16; c += 256) {   // 16 columns -> one word
+    uint32_t word = 0;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const float4 v = wr[4 * c + f];
+      word |= (q2_code(v.x, sc) | (q2_code(v.y, sc) << 2) | (q2_code(v.z, sc) << 4) |
+               (q2_code(v.w, sc) << 6)) << (8 * f);
+    }
+    qr[c] = word;   // byte i: columns 4i..4i+3, lowest bits first
+  }
+}
+
+// Canonical int2 chunk (16 bytes, 64 columns; byte i holds columns
+// 4i..4i+3, lowest bits first, two's complement) -> table chunk (word m,
+// byte j, field i: column 16m + 4i + j; field = q + 2).  Field j of canonical
+// byte 4m + i moves to field i of byte j of word m; XOR 2 turns a 2-bit two's
+// complement value into q + 2.
+__device__ __forceinline__ uint4 retile_chunk2(uint4 src) {
+  const uint32_t sw[4] = {src.x, src.y, src.z, src.w};
+  uint32_t dw[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t byte = (sw[m] >> (8 * i)) & 0xFFu;   // canonical byte 4m + i
+        const uint32_t f = ((byte >> (2 * j)) & 3u) ^ 2u;
+        word |= f << (8 * j + 2 * i);
+      }
+    dw[m] = word;
+  }
+  return make_uint4(dw[0], dw[1], dw[2], dw[3]);
+}
+
+// ---------------------------------------------------------------------------
 // Canonical container chunk (16 bytes, 32 columns, column 2i in the low nibble
 // of byte i, two's complement) -> table chunk (word kk, byte j: column
 // 8kk+j low, 8kk+4+j high; nibble = q + 8).
@@ -152,13 +216,20 @@ struct SetExpertArgs {
   int64_t D, F;
 };
 
-// A canonical row is a run of 16-byte chunks (32 int4 columns, or 16 int8
-// columns, each); the table puts chunk c of every lane's row side by side.
-// int4 chunks are re-encoded (retile_chunk), int8 chunks copied unchanged.
+// A canonical row is a run of 16-byte chunks (32 int4, 16 int8 or 64 int2
+// columns each); the table puts chunk c of every lane's row side by side.
+// int4 and int2 chunks are re-encoded (retile_chunk, retile_chunk2), int8
+// chunks copied unchanged.
+template <int BITS>
+__device__ __forceinline__ uint4 retile(uint4 src) {
+  if constexpr (BITS == 4) return retile_chunk(src);
+  if constexpr (BITS == 2) return retile_chunk2(src);
+  return src;
+}
+
 template <int BITS>
 __global__ void __launch_bounds__(256) table_set_expert_kernel(SetExpertArgs a) {
-  constexpr int U = BITS / 4;                       // chunks per 32-column block
-  const int64_t ncd = U * a.D / 32, ncf = U * a.F / 32;   // chunks per row
+  const int64_t ncd = a.D * BITS / 128, ncf = a.F * BITS / 128;   // chunks per row
   const int64_t n_gu = (a.F / 32) * ncd * 64;   // chunks in the gate/up slot
   const int64_t n_dn = (a.D / 64) * ncf * 64;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -167,14 +238,14 @@ __global__ void __launch_bounds__(256) table_set_expert_kernel(SetExpertArgs a) 
       const int64_t lane = i % 64, c = (i / 64) % ncd, g = i / (64 * ncd);
       const int64_t row = 32 * g + (lane & 31);
       const uint4 src = ((lane < 32 ? a.gate_q : a.up_q) + row * ncd)[c];
-      a.gu_q[i] = BITS == 4 ? retile_chunk(src) : src;
+      a.gu_q[i] = retile<BITS>(src);
       if (c == 0) a.gu_s[g * 64 + lane] = lane < 32 ? a.gate_s[row] : a.up_s[row];
     } else {
       const int64_t j = i - n_gu;
       const int64_t lane = j % 64, c = (j / 64) % ncf, g = j / (64 * ncf);
       const int64_t row = 64 * g + lane;
       const uint4 src = a.down_q[row * ncf + c];
-      a.dn_q[j] = BITS == 4 ? retile_chunk(src) : src;
+      a.dn_q[j] = retile<BITS>(src);
       if (c == 0) a.dn_s[row] = a.down_s[row];
     }
   }
@@ -246,6 +317,14 @@ hipError_t launch_quant_weight_q4(const float* w, int64_t rows, int64_t k, uint8
   return hipGetLastError();
 }
 
+hipError_t launch_quant_weight_q2(const float* w, int64_t rows, int64_t k, uint8_t* q, float* sc,
+                                  hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_weight_q2_kernel, dim3((unsigned)rows), dim3(256), 0, s, w, k,
+                     reinterpret_cast<uint32_t*>(q), sc);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_weight_q8(const float* w, int64_t rows, int64_t k, int8_t* q, float* sc,
                                   hipStream_t s) {
   if (rows == 0) return hipSuccess;
@@ -272,10 +351,12 @@ hipError_t launch_table_set_expert(const coli_expert_table& t, int expert, const
   a.dn_s = t.dn_s + (size_t)expert * (size_t)D;
   a.D = D;
   a.F = F;
-  const int64_t chunks = ((F / 32) * (D / 32) * 64 + (D / 64) * (F / 32) * 64) * (bits / 4);
+  const int64_t chunks = ((F / 32) * (D * bits / 128) + (D / 64) * (F * bits / 128)) * 64;
   const dim3 grid((unsigned)grid_for(chunks, 256, 1 << 16));
   if (bits == 8)
     hipLaunchKernelGGL(table_set_expert_kernel<8>, grid, dim3(256), 0, s, a);
+  else if (bits == 2)
+    hipLaunchKernelGGL(table_set_expert_kernel<2>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(table_set_expert_kernel<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();

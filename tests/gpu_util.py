@@ -25,10 +25,9 @@ def build_table(w: synth.Workload, layer: int = 0, bits: int = 4):
     table = coli.ExpertTable(w.E, w.S, w.D, w.F, weight_bits=bits)
     F, D = w.F, w.D
     scratch = torch.empty(F * D, dtype=torch.float32, device="cuda")
-    if bits == 4:
-        quant, qdt, per = coli.coli_quant_weight_q4, torch.uint8, 2
-    else:
-        quant, qdt, per = coli.coli_quant_weight_q8, torch.int8, 1
+    quant, qdt, per = {4: (coli.coli_quant_weight_q4, torch.uint8, 2),
+                       8: (coli.coli_quant_weight_q8, torch.int8, 1),
+                       2: (coli.coli_quant_weight_q2, torch.uint8, 4)}[bits]
     gq = torch.empty((F, D // per), dtype=qdt, device="cuda")
     uq = torch.empty_like(gq)
     dq = torch.empty((D, F // per), dtype=qdt, device="cuda")
@@ -124,6 +123,31 @@ def decode_table_expert8(w: synth.Workload, gu_q, gu_s, dn_q, dn_s, e: int):
     dn = dn_q[e * D * F:(e + 1) * D * F].view(np.int8).reshape(D // 64, F // 16, 64, 16)
     dcodes = dn.transpose(0, 2, 1, 3).reshape(D, F).astype(np.int64)
     return gate, up, s[:, :32].reshape(F), s[:, 32:].reshape(F), dcodes, dn_s[e * D:(e + 1) * D]
+
+
+def decode_table_expert2(w: synth.Workload, gu_q, gu_s, dn_q, dn_s, e: int):
+    """Test-side decoder of the documented int2 table layout (chunk of 64
+    columns; word m, byte j, field i = column 16m + 4i + j, stored q + 2)."""
+    D, F = w.D, w.F
+
+    def chunk_codes(chunks):          # [..., 16] bytes -> [..., 64] codes
+        b = chunks.reshape(chunks.shape[:-1] + (4, 4)).astype(np.int64)   # word m, byte j
+        out = np.empty(chunks.shape[:-1] + (64,), dtype=np.int64)
+        for m in range(4):
+            for j in range(4):
+                for i in range(4):
+                    out[..., 16 * m + 4 * i + j] = ((b[..., m, j] >> (2 * i)) & 3) - 2
+        return out
+
+    per_gu = 2 * F * D // 4
+    gu = gu_q[e * per_gu:(e + 1) * per_gu].reshape(F // 32, D // 64, 64, 16)
+    codes = chunk_codes(gu).transpose(0, 2, 1, 3).reshape(F // 32, 64, D)
+    per_dn = D * F // 4
+    dn = dn_q[e * per_dn:(e + 1) * per_dn].reshape(D // 64, F // 64, 64, 16)
+    dcodes = chunk_codes(dn).transpose(0, 2, 1, 3).reshape(D, F)
+    s = gu_s[e * 2 * F:(e + 1) * 2 * F].reshape(F // 32, 64)
+    return (codes[:, :32, :].reshape(F, D), codes[:, 32:, :].reshape(F, D), s[:, :32].reshape(F),
+            s[:, 32:].reshape(F), dcodes, dn_s[e * D:(e + 1) * D])
 
 
 def assert_bitexact(name, got, ref):

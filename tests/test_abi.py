@@ -58,8 +58,13 @@ def test_table_bytes():
     assert L.coli_table_bytes(257, 1, 6144, 2048, 4, None, None, None, None) == 0
     assert L.coli_table_bytes(16, 2, 256, 128, 4, None, None, None, None) == 0
     assert L.coli_table_bytes(16, 0, 256, 128 + 16, 4, None, None, None, None) == 0
-    for bits in (0, 2, 16):
+    for bits in (0, 3, 16):
         assert L.coli_table_bytes(16, 1, 256, 128, bits, None, None, None, None) == 0
+    # int2 tables: four codes per byte, the same scales; d_ff % 64 == 0
+    tot = L.coli_table_bytes(256, 1, 6144, 2048, 2, *[ctypes.byref(s) for s in sizes])
+    assert [s.value for s in sizes] == [257 * 6144 * 1024, 257 * 2 * 2048 * 4,
+                                       257 * 6144 * 512, 257 * 6144 * 4]
+    assert L.coli_table_bytes(16, 1, 256, 96, 2, None, None, None, None) == 0
 
 
 def _table(E=16, S=1, D=256, F=128, ptr=FAKE, bits=4, slots=0, slot_of=None):
@@ -78,6 +83,8 @@ def test_validation_quant():
     assert L.coli_quant_weight_q8(FAKE, 4, 64, FAKE, None, None) == coli.COLI_E_INVAL
     assert L.coli_quant_weight_q8(FAKE + 4, 4, 64, FAKE, FAKE, None) == coli.COLI_E_INVAL
     assert L.coli_quant_weight_q8(None, 0, 64, None, None, None) == coli.COLI_OK
+    assert L.coli_quant_weight_q2(FAKE, 4, 48, FAKE, FAKE, None) == coli.COLI_E_SHAPE
+    assert L.coli_quant_weight_q2(FAKE, 4, 64, None, FAKE, None) == coli.COLI_E_INVAL
     assert L.coli_rmsnorm_q8(FAKE, 1, 40, 1e-6, FAKE, FAKE, None, None) == coli.COLI_E_SHAPE
     assert L.coli_rmsnorm_q8(FAKE, 1, 64, -1.0, FAKE, FAKE, None, None) == coli.COLI_E_INVAL
     assert L.coli_rmsnorm_q8(FAKE, 1, 64, float("nan"), FAKE, FAKE, None, None) == coli.COLI_E_INVAL
@@ -130,8 +137,9 @@ def test_validation_forward():
     assert f(*args(_table(F=48))) == coli.COLI_E_SHAPE
     assert f(*args(_table(E=300))) == coli.COLI_E_SHAPE
     assert f(*args(_table(ptr=None))) == coli.COLI_E_INVAL
-    assert f(*args(_table(bits=2))) == coli.COLI_E_SHAPE
+    assert f(*args(_table(bits=3))) == coli.COLI_E_SHAPE
     assert f(*args(_table(bits=0))) == coli.COLI_E_SHAPE
+    assert f(*args(_table(F=96, bits=2))) == coli.COLI_E_SHAPE      # int2 needs d_ff % 64
     assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK          # empty batch: nothing to do
     assert L.coli_moe_forward_traced(*args(t), None) == coli.COLI_E_INVAL
     assert L.coli_moe_status(None, 64, None) == coli.COLI_E_INVAL
@@ -176,7 +184,9 @@ def test_tier_host_checks():
     assert tot == 32 * 18915328
     assert L.coli_tier_table_bytes(0, 6144, 2048, 4, None, None, None, None) == 0
     assert L.coli_tier_table_bytes(258, 6144, 2048, 4, None, None, None, None) == 0
-    assert L.coli_tier_table_bytes(8, 6144, 2048, 2, None, None, None, None) == 0
+    assert L.coli_tier_table_bytes(8, 6144, 2048, 3, None, None, None, None) == 0
+    assert L.coli_tier_table_bytes(8, 6144, 2048, 2, None, None, None, None) == 8 * (
+        3 * 6144 * 512 + 4 * (2 * 2048 + 6144))
     rng = np.random.default_rng(5)
     u = rng.integers(0, 6, size=256).astype(np.int32)
     assert coli.coli_tier_rank(u, 40).tolist() == sorted(range(256), key=lambda e: (-int(u[e]), e))[:40]
