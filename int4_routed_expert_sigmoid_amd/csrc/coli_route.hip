@@ -89,125 +89,134 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
   }
 }
 
-// One workgroup per expert e in [0, E+S).  Its four wavefronts split the
-// routing entries into four contiguous ranges; each counts its matches
-// (ballot popcounts over batches of 8 x 64 entries whose loads are in flight
-// together), a workgroup prefix of the four counts gives each wavefront its
-// first list position, and a second pass writes the positions.  The list is
-// in entry order = token order, as with one sweep.
-constexpr int kListBatch = 8;
+// Batch-union dispatch in one pass.  Workgroup c owns tokens
+// [64c, 64c + 64) and their k entries each.  An entry of expert e goes to
+// list position (entries of e in all earlier tokens) + (earlier entries of e
+// among its own), the first from an LDS histogram of every preceding entry,
+// the second from a scan of its own entries: each list is in entry order,
+// i.e. ascending token order, with no communication between workgroups and
+// no scratch memory.  Out-of-range entries are left out.  The last
+// workgroup also writes the counts, the active list and the index check (an
+// entry out of range, or equal to an earlier entry of its token).
+constexpr int kDispatchTokens = 64;
+constexpr int kDispatchLoads = 16;   // global loads in flight per thread
 
-__global__ void __launch_bounds__(256) dispatch_lists_kernel(const int32_t* __restrict__ idx,
-                                                             int64_t T, int k, int E, int S,
-                                                             int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ lists) {
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  int32_t* le = lists + (int64_t)e * T;
-  if (e == E) {   // the shared expert serves every token, in slot k
-    for (int64_t t = threadIdx.x; t < T; t += blockDim.x) le[t] = (int32_t)(t * (k + S) + k);
-    if (threadIdx.x == 0) counts[e] = (int32_t)T;
-    return;
-  }
-  __shared__ int wcnt[4];
-  const int64_t n = T * k;
-  const int64_t span = (n + 4 * kWave - 1) / (4 * kWave) * kWave;   // entries per wavefront
-  const int64_t lo = wave * span, hi = lo + span < n ? lo + span : n;
-  int cnt = 0;
-  for (int64_t i0 = lo; i0 < hi; i0 += kWave * kListBatch) {
-    int v[kListBatch];
+// hist[e] += entries of expert e among idx[lo, hi), for valid e.
+__device__ __forceinline__ void histogram(const int32_t* __restrict__ idx, int64_t lo, int64_t hi,
+                                          int E, int* hist) {
+  for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += 256 * kDispatchLoads) {
+    int v[kDispatchLoads];
 #pragma unroll
-    for (int u = 0; u < kListBatch; ++u) {
-      const int64_t i = i0 + (int64_t)u * kWave + lane;
+    for (int u = 0; u < kDispatchLoads; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
       v[u] = i < hi ? idx[i] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kListBatch; ++u) cnt += __popcll(__ballot(v[u] == e));
+    for (int u = 0; u < kDispatchLoads; ++u)
+      if (v[u] >= 0 && v[u] < E) atomicAdd(&hist[v[u]], 1);
   }
-  if (lane == 0) wcnt[wave] = cnt;
-  __syncthreads();
-  int64_t base = 0, total = 0;
-  for (int w = 0; w < 4; ++w) {
-    base += w < wave ? wcnt[w] : 0;
-    total += wcnt[w];
-  }
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t i0 = lo; i0 < hi; i0 += kWave * kListBatch) {
-    int v[kListBatch];
-#pragma unroll
-    for (int u = 0; u < kListBatch; ++u) {
-      const int64_t i = i0 + (int64_t)u * kWave + lane;
-      v[u] = i < hi ? idx[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kListBatch; ++u) {
-      const int64_t i = i0 + (int64_t)u * kWave + lane;
-      const bool hit = v[u] == e;
-      const uint64_t m = __ballot(hit);
-      const int64_t pos = base + __popcll(m & lt);
-      if (hit && pos < T) le[pos] = (int32_t)((i / k) * (k + S) + i % k);
-      base += __popcll(m);
-    }
-  }
-  if (threadIdx.x == 0) counts[e] = (int32_t)(total < T ? total : T);
 }
 
-// Workgroup 0: compact the active-expert list and check the indices.
-// Every workgroup: -8 * (sum of each Q8 block of x), the offset that turns the
-// offset-binary nibble dot into the signed one.
-__global__ void __launch_bounds__(256) dispatch_finish_kernel(
-    const int32_t* __restrict__ idx, int64_t T, int k, int E, int S,
-    const int32_t* __restrict__ counts, int32_t* __restrict__ n_active,
-    int32_t* __restrict__ active, int32_t* __restrict__ err, const int8_t* __restrict__ xq,
-    int64_t D, int32_t* __restrict__ xsum8) {
-  if (blockIdx.x == 0) {
-    __shared__ int bad_any;
-    if (threadIdx.x == 0) bad_any = 0;
-    __syncthreads();
-    // the index check, over chunks of whole tokens staged in LDS: an entry is
-    // bad if out of range or equal to an earlier entry of its token
-    __shared__ int ent[4096];
-    int bad = 0;
-    const int64_t n = T * k, chunk = (4096 / k) * k;
-    for (int64_t c0 = 0; c0 < n; c0 += chunk) {
-      const int64_t m = n - c0 < chunk ? n - c0 : chunk;
-#pragma unroll 16
-      for (int64_t i = threadIdx.x; i < m; i += blockDim.x) ent[i] = idx[c0 + i];
-      __syncthreads();
-      for (int64_t i = threadIdx.x; i < m; i += blockDim.x) {
-        const int e = ent[i];
-        if (e < 0 || e >= E) { bad = 1; continue; }
-        for (int64_t j = (i / k) * k; j < i; ++j) bad |= ent[j] == e;
-      }
-      __syncthreads();
-    }
-    if (bad) atomicOr(&bad_any, 1);
-    if (threadIdx.x < kWave) {
-      const int lane = threadIdx.x;
-      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      int base = 0;
-      for (int e0 = 0; e0 < E + S; e0 += kWave) {
-        const int e = e0 + lane;
-        const bool on = e < E + S && counts[e] > 0;
-        const uint64_t m = __ballot(on);
-        if (on) active[base + __popcll(m & lt)] = e;
-        base += __popcll(m);
-      }
-      if (lane == 0) *n_active = base;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) *err = bad_any ? (int)COLI_E_INDEX : 0;
+__global__ void __launch_bounds__(256) dispatch_sort_kernel(const int32_t* __restrict__ idx,
+                                                            int64_t T, int k, int E, int S,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ lists,
+                                                            int32_t* __restrict__ n_active,
+                                                            int32_t* __restrict__ active,
+                                                            int32_t* __restrict__ err) {
+  __shared__ int hist[COLI_MAX_EXPERTS + 1];
+  __shared__ int ent[kDispatchTokens * COLI_MAX_TOPK];
+  __shared__ int bad_any;
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * kDispatchTokens;
+  const int nt = (int)(T - t0 < kDispatchTokens ? T - t0 : kDispatchTokens);
+  const int64_t g0 = t0 * k;   // first entry of this workgroup
+  const int m = nt * k;
+  for (int e = tid; e < E + S; e += 256) hist[e] = 0;
+  if (tid == 0) bad_any = 0;
+  for (int i = tid; i < m; i += 256) ent[i] = idx[g0 + i];
+  __syncthreads();
+  histogram(idx, 0, g0, E, hist);
+  __syncthreads();
+  for (int i = tid; i < m; i += 256) {
+    const int e = ent[i];
+    if (e < 0 || e >= E) continue;
+    int rank = 0;
+    for (int j = 0; j < i; ++j) rank += ent[j] == e;
+    const int64_t pos = hist[e] + rank;
+    const int64_t g = g0 + i;
+    if (pos < T) lists[(int64_t)e * T + pos] = (int32_t)((g / k) * (k + S) + g % k);
   }
-  if (xq) {
-    const int64_t nb = T * (D / 32);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-      const int* xp = reinterpret_cast<const int*>(xq + 32 * b);
-      int sum = 0;
+  if (S)   // the shared expert serves every token, in slot k
+    for (int i = tid; i < nt; i += 256)
+      lists[(int64_t)E * T + t0 + i] = (int32_t)((t0 + i) * (k + S) + k);
+  if (blockIdx.x != gridDim.x - 1) return;
+  // the last workgroup: its own entries complete the totals; then the index
+  // check over whole-token chunks of every entry staged through LDS
+  __syncthreads();
+  for (int i = tid; i < m; i += 256) {
+    const int e = ent[i];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  int bad = 0;
+  const int64_t n = T * k, chunk = (kDispatchTokens * COLI_MAX_TOPK / k) * k;
+  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
+    const int cm = (int)(n - c0 < chunk ? n - c0 : chunk);
+    __syncthreads();   // the previous chunk's readers are done
+    for (int i0 = tid; i0 < cm; i0 += 256 * kDispatchLoads) {
+      int v[kDispatchLoads];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum = sdot4(xp[j], 0x01010101, sum);
-      xsum8[b] = -8 * sum;
+      for (int u = 0; u < kDispatchLoads; ++u) {
+        const int i = i0 + u * 256;
+        v[u] = i < cm ? idx[c0 + i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kDispatchLoads; ++u)
+        if (i0 + u * 256 < cm) ent[i0 + u * 256] = v[u];
     }
+    __syncthreads();
+    for (int t = tid; t < cm / k; t += 256) {
+      const int* et = ent + t * k;
+      for (int j = 0; j < k; ++j) {
+        const int e = et[j];
+        if (e < 0 || e >= E) bad = 1;
+        for (int i = 0; i < j; ++i) bad |= et[i] == e;
+      }
+    }
+  }
+  if (bad) atomicOr(&bad_any, 1);
+  __syncthreads();
+  for (int e = tid; e < E + S; e += 256)
+    counts[e] = e == E ? (int32_t)T : (hist[e] < T ? hist[e] : (int32_t)T);
+  if (tid < kWave) {
+    const int lane = tid;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int base = 0;
+    for (int e0 = 0; e0 < E + S; e0 += kWave) {
+      const int e = e0 + lane;
+      const bool on = e < E + S && (e == E ? T > 0 : hist[e] > 0);
+      const uint64_t msk = __ballot(on);
+      if (on) active[base + __popcll(msk & lt)] = e;
+      base += __popcll(msk);
+    }
+    if (lane == 0) {
+      *n_active = base;
+      *err = bad_any ? (int)COLI_E_INDEX : 0;
+    }
+  }
+}
+
+// -8 sum of the codes of every Q8 block of x (the GEMV's offset-binary
+// nibble correction).
+__global__ void __launch_bounds__(256) xsum8_kernel(const int8_t* __restrict__ xq, int64_t nb,
+                                                    int32_t* __restrict__ xsum8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    const int* xp = reinterpret_cast<const int*>(xq + 32 * b);
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum = sdot4(xp[j], 0x01010101, sum);
+    xsum8[b] = -8 * sum;
   }
 }
 
@@ -345,18 +354,15 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, int32_t* counts,
                            int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
                            const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_lists_kernel, dim3((unsigned)(E + S)), dim3(256), 0, s, idx, T, k,
-                     E, S, counts, lists);
+  const int64_t groups = T > 0 ? (T + kDispatchTokens - 1) / kDispatchTokens : 1;
+  hipLaunchKernelGGL(dispatch_sort_kernel, dim3((unsigned)groups), dim3(256), 0, s, idx, T, k, E,
+                     S, counts, lists, n_active, active, err);
   hipError_t rc = hipGetLastError();
-  if (rc != hipSuccess) return rc;
-  int64_t blocks = 1;
-  if (xq) {
-    blocks = (T * (D / 32) + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    if (blocks < 1) blocks = 1;
-  }
-  hipLaunchKernelGGL(dispatch_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, s, idx, T, k,
-                     E, S, counts, n_active, active, err, xq, D, xsum8);
+  if (rc != hipSuccess || !xq || T == 0) return rc;
+  const int64_t nb = T * (D / 32);
+  int64_t blocks = (nb + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(xsum8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, xq, nb, xsum8);
   return hipGetLastError();
 }
 
