@@ -14,8 +14,9 @@
  *
  * Conventions for every entry point:
  *  - Bulk arrays (f32 inputs of the quantisers, packed weights, table arrays,
- *    workspace) must be 16-byte aligned, every other pointer 4-byte aligned
- *    (torch allocations are); misaligned pointers return COLI_E_INVAL.
+ *    layer outputs y, workspace) must be 16-byte aligned, every other pointer
+ *    4-byte aligned (torch allocations and their row slices are);
+ *    misaligned pointers return COLI_E_INVAL.
  *  - Tensor pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
  *    owned by the caller; the library never allocates, frees or keeps them.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).

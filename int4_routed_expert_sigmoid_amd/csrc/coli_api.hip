@@ -297,7 +297,7 @@ static int forward_impl(const coli_expert_table* table, const int8_t* xq, const 
   if (accumulate != 0 && accumulate != 1) return COLI_E_INVAL;
   if (T == 0) return COLI_OK;
   if (!xq || !xd || !idx || !w || !y || !workspace) return COLI_E_INVAL;
-  if (!al4(xq) || !al4(xd) || !al4(idx) || !al4(w) || !al4(y) || !al16(workspace))
+  if (!al4(xq) || !al4(xd) || !al4(idx) || !al4(w) || !al16(y) || !al16(workspace))
     return COLI_E_INVAL;
   const coli::MoeWorkspace ws = coli::moe_workspace_layout(
       workspace, table->n_routed, table->n_shared, table->d_model, table->d_ff, T, k);
@@ -412,7 +412,7 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
   if (!std::isfinite(routed_scale)) return COLI_E_INVAL;
   if (T == 0) return COLI_OK;
   if (!x || !logits || !y || !workspace) return COLI_E_INVAL;
-  if (!al16(x) || !al4(logits) || !al4(bias) || !al4(y) || !al16(workspace)) return COLI_E_INVAL;
+  if (!al16(x) || !al4(logits) || !al4(bias) || !al16(y) || !al16(workspace)) return COLI_E_INVAL;
   const LayerWorkspace l = layer_workspace_layout(workspace, table, T, k);
   if (ws_bytes < l.bytes) return COLI_E_WORKSPACE;
   if ((rc = check_device())) return rc;

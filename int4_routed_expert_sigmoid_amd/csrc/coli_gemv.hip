@@ -581,23 +581,6 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
   }
 }
 
-// One output row of the layer for token t: y = o_shared + sum_j w_j o_j,
-// accumulated as y = fmaf(w_j, o_j, y) in slot order (shared expert first).
-__device__ __forceinline__ float combine_row(const float* __restrict__ o,
-                                             const int32_t* __restrict__ idx,
-                                             const float* __restrict__ w, int64_t t, int64_t r,
-                                             int64_t D, int k, int E, int S) {
-  const int KS = k + S;
-  const float* ot = o + (size_t)t * KS * D;
-  float acc = S ? ot[(size_t)k * D + r] : 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if (e < 0 || e >= E) continue;
-    acc = __builtin_fmaf(w[t * k + j], ot[(size_t)j * D + r], acc);
-  }
-  return acc;
-}
-
 template <int MAXT, int PF, int BITS, bool TRACE>
 __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   constexpr int W = gemv_waves(MAXT);
@@ -657,18 +640,55 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   }
 }
 
-// y[t][r] = o_shared + sum_j w_j o_j, as y = fmaf(w_j, o_j, y) in slot order.
+__device__ __forceinline__ float4 fma4(float w, float4 a, float4 acc) {
+  return make_float4(__builtin_fmaf(w, a.x, acc.x), __builtin_fmaf(w, a.y, acc.y),
+                     __builtin_fmaf(w, a.z, acc.z), __builtin_fmaf(w, a.w, acc.w));
+}
+
+// y[t][r] = o_shared + sum_j w_j o_j, as y = fmaf(w_j, o_j, y) in slot order,
+// four rows per thread.  KU > 0: k == KU, unrolled, every slot's load issued
+// before the ordered fmaf chain; KU == 0: any k.
+template <int KU>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ w, int64_t D,
                                                       int k, int E, int S, float* __restrict__ y,
                                                       int accumulate) {
   const int64_t t = blockIdx.y;
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= D) return;
-  const float v = combine_row(o, idx, w, t, r, D, k, E, S);
-  float* yt = y + t * D + r;
-  *yt = accumulate ? *yt + v : v;
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // 4-row group
+  if (4 * q >= D) return;
+  const int KS = k + S;
+  const float4* ot = reinterpret_cast<const float4*>(o + (size_t)t * KS * D) + q;
+  const int64_t D4 = D / 4;
+  float4 acc = S ? ot[k * D4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if constexpr (KU > 0) {
+    float4 v[KU];
+    float wj[KU];
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const int e = idx[t * KU + j];
+      const bool ok = e >= 0 && e < E;
+      wj[j] = ok ? w[t * KU + j] : 0.0f;
+      v[j] = ok ? ot[j * D4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const int e = idx[t * KU + j];
+      if (e >= 0 && e < E) acc = fma4(wj[j], v[j], acc);
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e < 0 || e >= E) continue;
+      acc = fma4(w[t * k + j], ot[j * D4], acc);
+    }
+  }
+  float4* yt = reinterpret_cast<float4*>(y + t * D) + q;
+  if (accumulate) {
+    const float4 r = *yt;
+    acc = make_float4(r.x + acc.x, r.y + acc.y, r.z + acc.z, r.w + acc.w);
+  }
+  *yt = acc;
 }
 
 // Stage events (profiled forward only; not for stream capture, where a record
@@ -816,8 +836,13 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   }
   if (rc != hipSuccess) return rc;
   if ((rc = record(ev.combine, s)) != hipSuccess) return rc;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((D + 255) / 256), (unsigned)T), dim3(256), 0,
-                     s, ws.o, f.idx, f.w, D, f.k, E, S, f.y, f.accumulate);
+  const dim3 cgrid((unsigned)((D / 4 + 255) / 256), (unsigned)T);
+  if (f.k == 8)
+    hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, s, ws.o, f.idx, f.w, D, f.k, E, S,
+                       f.y, f.accumulate);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, cgrid, dim3(256), 0, s, ws.o, f.idx, f.w, D, f.k, E, S,
+                       f.y, f.accumulate);
   rc = hipGetLastError();
   if (rc == hipSuccess) rc = record(ev.end, s);
   if (rc != hipSuccess || !tr) return rc;

@@ -133,6 +133,7 @@ def test_validation_forward():
     assert f(*args(t, k=17)) == coli.COLI_E_SHAPE
     assert f(*args(t, acc=2)) == coli.COLI_E_INVAL
     assert f(*args(t, y=None)) == coli.COLI_E_INVAL
+    assert f(*args(t, y=FAKE + 4)) == coli.COLI_E_INVAL      # y must be 16-byte aligned
     assert f(*args(_table(D=96))) == coli.COLI_E_SHAPE
     assert f(*args(_table(F=48))) == coli.COLI_E_SHAPE
     assert f(*args(_table(E=300))) == coli.COLI_E_SHAPE
