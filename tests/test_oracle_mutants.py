@@ -77,8 +77,8 @@ MUTANTS = {
                                            "if (v < 0 || stamp[s] > stamp[v]) v = s;"),
     "tier evicts pinned slots": ("if (pinned[s] || stamp[s] >= step) continue;",
                                  "if (stamp[s] >= step) continue;"),
-    "tier reuses a slot of this pass": ("if (pinned[s] || stamp[s] >= step) continue;",
-                                        "if (pinned[s]) continue;"),
+    "tier fit check counts hit slots as free": ("if (miss > unpinned - hit_unpinned) rc = -1;",
+                                                "if (miss > unpinned) rc = -1;"),
     "tier hits leave the stamp": ("    stamp[slot_of[e]] = step;\n    ++nh;", "    ++nh;"),
     "tier usage skips the shared expert": ("  if (S) count[E] = (int32_t)T;", ""),
     "pin ranking ties to the higher id": ("if (best < 0 || usage[e] > usage[best]) best = e;",
