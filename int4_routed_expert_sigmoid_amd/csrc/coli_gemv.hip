@@ -241,19 +241,68 @@ __device__ __forceinline__ void clear_tail_records(int NB, int pb, int tid, int 
 // The block's sum term is staged as -8 sum x (int4: nibbles are q + 8) or
 // -2 sum x (int2: fields are q + 2; sum_shift 2, exact since -8 sum x is a
 // multiple of 8); int8 blocks do not use it.
-template <int MAXT>
+//
+// Every load of a round (up to kStageX 16-byte code loads and kStageD scale/sum
+// pairs per thread; one round covers d_model 8192 at 64 threads) is issued
+// before the first LDS store, so staging costs one memory round trip, not
+// one per load.  Memory waits retire in issue order, so the kernels issue
+// only the head of their weight ring before the staging loads and the rest
+// of it from after_loads(), which runs once the first round's loads are out:
+// the staging then waits for the ring head, not for the whole ring.
+constexpr int kStageX = 8;
+constexpr int kStageD = 4;
+
+template <int MAXT, typename F>
+__device__ __forceinline__ void stage_round(unsigned char* lds, int j, const u32x4* xg,
+                                            const float* __restrict__ drow,
+                                            const int32_t* __restrict__ srow, int NB, int tid,
+                                            int nth, int sum_shift, int r, F&& after_loads) {
+  constexpr int R = PassLds<MAXT>::R;
+  const int n = 2 * NB;
+  // Indices past the end are clamped to the last element, for the loads and
+  // the stores alike (a clamped lane rewrites that element with its own
+  // value): the round is branch-free, so its loads stay together.
+  int xi[kStageX], bi[kStageD];
+  u32x4 v[kStageX];
+  float d[kStageD];
+  int32_t s[kStageD];
+#pragma unroll
+  for (int u = 0; u < kStageX; ++u) {
+    const int i = (r * kStageX + u) * nth + tid;
+    xi[u] = i < n ? i : n - 1;
+    v[u] = xg[xi[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < kStageD; ++u) {
+    const int b = (r * kStageD + u) * nth + tid;
+    bi[u] = b < NB ? b : NB - 1;
+    d[u] = drow[bi[u]];
+    s[u] = srow[bi[u]];
+  }
+  after_loads();
+  // the loaded values are taken here, after every load of the round has been
+  // issued (otherwise the compiler sinks each load down to its store)
+#pragma unroll
+  for (int u = 0; u < kStageX; ++u) asm volatile("" : "+v"(v[u]));
+#pragma unroll
+  for (int u = 0; u < kStageX; ++u)
+    *reinterpret_cast<u32x4*>(lds + (size_t)(xi[u] >> 1) * R + 32 * j + 16 * (xi[u] & 1)) = v[u];
+#pragma unroll
+  for (int u = 0; u < kStageD; ++u)
+    *reinterpret_cast<float2*>(lds + (size_t)bi[u] * R + PassLds<MAXT>::DM + 8 * j) =
+        make_float2(d[u], __int_as_float(s[u] >> sum_shift));
+}
+
+template <int MAXT, typename F>
 __device__ __forceinline__ void stage_token(unsigned char* lds, int j,
                                             const int8_t* __restrict__ xrow,
                                             const float* __restrict__ drow,
                                             const int32_t* __restrict__ srow, int NB, int tid,
-                                            int nth, int sum_shift) {
-  constexpr int R = PassLds<MAXT>::R;
-  const uint4* xg = reinterpret_cast<const uint4*>(xrow);
-  for (int i = tid; i < 2 * NB; i += nth)
-    *reinterpret_cast<uint4*>(lds + (size_t)(i >> 1) * R + 32 * j + 16 * (i & 1)) = xg[i];
-  for (int b = tid; b < NB; b += nth)
-    *reinterpret_cast<float2*>(lds + (size_t)b * R + PassLds<MAXT>::DM + 8 * j) =
-        make_float2(drow[b], __int_as_float(srow[b] >> sum_shift));
+                                            int nth, int sum_shift, F&& after_loads) {
+  const u32x4* xg = reinterpret_cast<const u32x4*>(xrow);
+  stage_round<MAXT>(lds, j, xg, drow, srow, NB, tid, nth, sum_shift, 0, after_loads);
+  for (int r = 1; r * nth * kStageX < 2 * NB || r * nth * kStageD < NB; ++r)
+    stage_round<MAXT>(lds, j, xg, drow, srow, NB, tid, nth, sum_shift, r, [] {});
 }
 
 struct XBlock {
@@ -296,19 +345,32 @@ struct Ring {
   int NU;
   u32x4 buf[PF];
 
-  // Issues the first PF loads, in slot order so that slot 0 lands first.
+  // Issues slots [0, N0) (the ring head), in slot order so that slot 0 lands
+  // first; issue<N0>() issues the rest.
+  template <int N0>
   __device__ __forceinline__ void start(const char* wbase, uint32_t lane_off, int nu) {
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, nu * 1024, kBufferConfig);
     loff = lane_off;
     NU = nu;
+    issue_range<0, N0>();
+  }
+  template <int N0>
+  __device__ __forceinline__ void issue() {
+    issue_range<N0, PF>();
+  }
+  template <int A, int B>
+  __device__ __forceinline__ void issue_range() {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
+    for (int i = A; i < B; ++i) {
       buf[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, loff, (i < NU ? i : NU - 1) * 1024,
                                                      kNonTemporal);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
+
+// Ring slots issued before the token staging (the rest follow its loads).
+constexpr int ring_head(int pf, int maxt) { return maxt >= 8 || pf < 4 ? pf : 4; }
 
 // Refills the U slots of ring position i (block b) with the chunks of block
 // b + PB, clamped into the row group.
@@ -510,8 +572,9 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
   const int NU = row_chunks(NB, BITS);   // 1 KB chunks in the row group
   const char* wbase = reinterpret_cast<const char*>(a.gu_q + ((size_t)es * G + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
+  constexpr int H = ring_head(PF, MAXT);
   Ring<PF> ring;
-  ring.start(wbase, loff, NU);          // the weight stream starts before anything else
+  ring.template start<H>(wbase, loff, NU);       // the weight stream starts before anything else
   clear_tail_records<MAXT>(NB, blocks_per_ring(PF, BITS), threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const float rs = a.gu_s[((size_t)es * G + grp) * kWave + lane];
@@ -523,7 +586,7 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
     int32_t* trow[MAXT];
     if (c0 > 0) {
       __syncthreads();                // the previous pass has finished reading the LDS records
-      ring.start(wbase, loff, NU);    // each pass streams the row group again
+      ring.template start<H>(wbase, loff, NU); // each pass streams the row group again
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
@@ -537,10 +600,15 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
-      if (j < ns) {
+      if (j < ns) {   // (ns >= 1: token 0 always runs and issues the ring's rest)
         const int64_t t = __builtin_amdgcn_readfirstlane(pair[j] / KS);
-        stage_token<MAXT>(gemv_lds(), j, a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB,
-                          threadIdx.x, kWave * W, BITS == 2 ? 2 : 0);
+        if (j == 0)
+          stage_token<MAXT>(gemv_lds(), j, a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB,
+                            threadIdx.x, kWave * W, BITS == 2 ? 2 : 0,
+                            [&] { ring.template issue<H>(); });
+        else
+          stage_token<MAXT>(gemv_lds(), j, a.xq + t * a.D, a.xd + t * NB, a.xsum8 + t * NB, NB,
+                            threadIdx.x, kWave * W, BITS == 2 ? 2 : 0, [] {});
       }
     }
     __syncthreads();
@@ -600,8 +668,9 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
   const char* wbase =
       reinterpret_cast<const char*>(a.dn_q + ((size_t)es * (a.D / 64) + grp) * (size_t)NU * kWave);
   const uint32_t loff = 16u * (uint32_t)lane;
+  constexpr int H = ring_head(PF, MAXT);
   Ring<PF> ring;
-  ring.start(wbase, loff, NU);          // the weight stream starts before anything else
+  ring.template start<H>(wbase, loff, NU);       // the weight stream starts before anything else
   clear_tail_records<MAXT>(NB, blocks_per_ring(PF, BITS), threadIdx.x, kWave * W);
   const int cnt = as_const(a.counts)[e];
   const size_t row = 64 * (size_t)grp + lane;
@@ -614,7 +683,7 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
     int32_t* trow[MAXT];
     if (c0 > 0) {
       __syncthreads();
-      ring.start(wbase, loff, NU);
+      ring.template start<H>(wbase, loff, NU);
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
@@ -623,10 +692,15 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < MAXT; ++j) {
-      if (j < ns) {
+      if (j < ns) {   // (ns >= 1: token 0 always runs and issues the ring's rest)
         const size_t p = (size_t)__builtin_amdgcn_readfirstlane(pair[j]);
-        stage_token<MAXT>(gemv_lds(), j, a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB,
-                          threadIdx.x, kWave * W, BITS == 2 ? 2 : 0);
+        if (j == 0)
+          stage_token<MAXT>(gemv_lds(), j, a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB,
+                            threadIdx.x, kWave * W, BITS == 2 ? 2 : 0,
+                            [&] { ring.template issue<H>(); });
+        else
+          stage_token<MAXT>(gemv_lds(), j, a.hq + p * a.F, a.hd + p * NB, a.hsum8 + p * NB, NB,
+                            threadIdx.x, kWave * W, BITS == 2 ? 2 : 0, [] {});
       }
     }
     __syncthreads();
