@@ -721,7 +721,8 @@ __device__ __forceinline__ float4 fma4(float w, float4 a, float4 acc) {
 
 // y[t][r] = o_shared + sum_j w_j o_j, as y = fmaf(w_j, o_j, y) in slot order,
 // four rows per thread.  KU > 0: k == KU, unrolled, every slot's load issued
-// before the ordered fmaf chain; KU == 0: any k.
+// before the ordered fmaf chain; KU == 0: any k.  Slots with an index outside
+// [0, E) are skipped (their o rows were never written).
 template <int KU>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ idx,
@@ -739,11 +740,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     float4 v[KU];
     float wj[KU];
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const int e = idx[t * KU + j];
-      const bool ok = e >= 0 && e < E;
-      wj[j] = ok ? w[t * KU + j] : 0.0f;
-      v[j] = ok ? ot[j * D4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int j = 0; j < KU; ++j) {   // o rows of skipped slots are read but never used,
+      wj[j] = w[t * KU + j];         // so no load waits for the index check
+      v[j] = ot[j * D4];
     }
 #pragma unroll
     for (int j = 0; j < KU; ++j) {

@@ -15,9 +15,8 @@
 // deterministic without atomics.
 #include "coli_internal.h"
 
-// Wavefront max of a 64-bit value (ROCm device library, DPP-based).
-extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(
-    unsigned long long);
+// Wavefront max of a 32-bit value (ROCm device library, DPP-based).
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_max_u32(unsigned int);
 
 namespace coli {
 namespace {
@@ -36,34 +35,76 @@ __device__ __forceinline__ uint32_t ordered_bits(float c) {
 // of its selection score above the inverted expert index, so that a larger
 // key is a larger score or, on a tie, the lower index: the strict order of
 // the selection.  Each of the k rounds is one wavefront max (DPP) of the
-// lanes' best remaining keys; the winner is struck out.  The selected
-// experts' sigmoid scores are recomputed by their slot lanes and summed in
-// slot order through readlane.
+// lanes' best remaining keys, taken as two 32-bit maxima; the winner is
+// struck out.  The selected
+// experts' sigmoid scores are fetched by their slot lanes from the lanes that
+// computed them (no second read of the logits) and summed in slot order
+// through readlane.
 __device__ __forceinline__ void route_token(const float* __restrict__ lg,
                                             const float* __restrict__ bias, int E, int k,
                                             float routed_scale, int lane, int* out_idx,
                                             float* out_w) {
+  // all eight loads first (indices clamped into [0, E)), then the scores
+  float lv[4], bv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + kWave * i;
+    const int ec = e < E ? e : E - 1;
+    lv[i] = lg[ec];
+    bv[i] = bias ? bias[ec] : 0.0f;
+  }
   uint64_t key[4];
+  float sg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + kWave * i;
     key[i] = 0;   // below every real key
+    sg[i] = 0.0f;
     if (e < E) {
-      const float c = sigmoid_f32(lg[e]) + (bias ? bias[e] : 0.0f);
+      sg[i] = sigmoid_f32(lv[i]);
+      const float c = sg[i] + bv[i];
       key[i] = ((uint64_t)ordered_bits(c) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
     }
   }
+  // the lane's keys in descending order (a five-exchange sorting network);
+  // real keys are distinct, so after each round only the winning lane has
+  // its first key equal to the winner and shifts its keys up
+  uint64_t q[4] = {key[0], key[1], key[2], key[3]};
+  auto exch = [](uint64_t& x, uint64_t& y) {
+    const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
+    x = hi;
+    y = lo;
+  };
+  exch(q[0], q[1]);
+  exch(q[2], q[3]);
+  exch(q[0], q[2]);
+  exch(q[1], q[3]);
+  exch(q[1], q[2]);
   int my_idx = -1;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0] > key[1] ? key[0] : key[1];
-    const uint64_t b23 = key[2] > key[3] ? key[2] : key[3];
-    best = best > b23 ? best : b23;
-    const uint64_t win = __ockl_wfred_max_u64((unsigned long long)best);   // wavefront max
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = key[i] == win ? 0 : key[i];
+    // wavefront max of the 64-bit keys as two 32-bit maxima: the score bits,
+    // then the index part among the lanes holding that score (a real key's
+    // index part is never 0, so the other lanes' 0 cannot win)
+    const uint32_t hi = __ockl_wfred_max_u32((uint32_t)(q[0] >> 32));
+    const uint32_t lo = __ockl_wfred_max_u32((uint32_t)(q[0] >> 32) == hi ? (uint32_t)q[0] : 0u);
+    const uint64_t win = ((uint64_t)hi << 32) | lo;
+    const bool mine = q[0] == win;
+    q[0] = mine ? q[1] : q[0];
+    q[1] = mine ? q[2] : q[1];
+    q[2] = mine ? q[3] : q[2];
+    q[3] = mine ? 0 : q[3];
     if (lane == j) my_idx = (int)(0xFFFFFFFFu - (uint32_t)win);
   }
-  const float my_s = lane < k ? sigmoid_f32(lg[my_idx]) : 0.0f;
+  // the selected expert's sigmoid score, from the lane that computed it
+  // (expert e sits in lane e % 64, register e / 64)
+  const int src = my_idx & (kWave - 1), reg = my_idx >> 6;
+  float my_s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v = __shfl(sg[i], src);
+    my_s = reg == i ? v : my_s;
+  }
+  if (lane >= k) my_s = 0.0f;
   float sum = 0.0f;
   for (int j = 0; j < k; ++j)
     sum = sum + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
@@ -241,8 +282,9 @@ struct PrologueArgs {
 
 // The whole front of a small batch.  Workgroup 0 (4 wavefronts): routing (one
 // wavefront per token), then the dispatch lists (one thread per routing
-// entry, entries from LDS), the active-expert compaction and the index check.
-// Workgroups 1..: Q8_0 of every token with its block sums, in parallel.
+// entry, entries from LDS), the active-expert compaction and the index check;
+// a single token takes a barrier-free path (below).  Workgroups 1..: Q8_0 of
+// every token with its block sums, in parallel.
 __global__ void __launch_bounds__(256) prologue_small_kernel(PrologueArgs a) {
   __shared__ int ent[kPrologueMaxEntries];
   __shared__ bool valid[kPrologueMaxEntries];
@@ -265,6 +307,38 @@ __global__ void __launch_bounds__(256) prologue_small_kernel(PrologueArgs a) {
         a.xd[g >> 3] = dv;
         a.xsum8[g >> 3] = -8 * sum;
       }
+    }
+    return;
+  }
+  if (a.T == 1) {
+    // One token: every wavefront routes it (the same result in each) and
+    // writes its share of the dispatch from registers, with no barrier.  The
+    // k experts are distinct and in [0, E) (k <= E), so every entry is listed
+    // at position 0 of its expert's list and the index check passes.
+    int my_idx;
+    float my_w;
+    route_token(a.logits, a.bias, a.E, a.k, a.routed_scale, lane, &my_idx, &my_w);
+    const int k = a.k, E = a.E, S = a.S;
+    int rank = 0;   // position of this lane's expert among the selected, ascending
+    for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(my_idx, j) < my_idx;
+    if (wave == 0 && lane < k) {
+      a.idx[lane] = my_idx;
+      a.w[lane] = my_w;
+      a.lists[my_idx] = lane;      // pair 0 * (k + S) + slot
+      a.active[rank] = my_idx;     // the shared expert E sorts after every routed one
+    }
+    for (int e = tid; e < E + S; e += 256) {
+      int c = e == E ? 1 : 0;
+      for (int j = 0; j < k; ++j) c |= __builtin_amdgcn_readlane(my_idx, j) == e;
+      a.counts[e] = c;
+    }
+    if (tid == 0) {
+      if (S) {
+        a.lists[E] = k;            // the shared expert takes slot k
+        a.active[k] = E;
+      }
+      *a.n_active = k + S;
+      *a.err = 0;
     }
     return;
   }

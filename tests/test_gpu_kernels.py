@@ -128,6 +128,18 @@ def test_route_topk(wl, T):
     assert_bitexact("w", wt, rw)
 
 
+def lane_heavy_logits():
+    """256 experts whose top-8 sit in few wavefront lanes (expert e is held by
+    lane e % 64): a four-way tie inside lane 3, a tie across lanes 7 and 3,
+    one more winner in lane 7, and the 8th taken among 248 equal scores;
+    row 1 puts all eight winners into lanes 3 and 7 with distinct scores."""
+    lg = np.full((2, 256), -2.0, np.float32)
+    lg[0, [3, 67, 131, 195, 7, 71]] = 1.0
+    lg[0, 135] = 0.5
+    lg[1, [3, 67, 131, 195, 7, 71, 135, 199]] = np.float32([5, 1, 4, 2, 8, 3, 7, 6]) / 4
+    return lg
+
+
 def test_route_topk_edges():
     cases = [
         (np.float32([[1.0, 2.0, 1.0, 2.0, 2.0, 0.0]]), None, 4, 1.0),      # exact ties
@@ -135,6 +147,8 @@ def test_route_topk_edges():
         (np.float32([[2.0, 1.0, -3.0]]), np.float32([0.0, 0.5, 0.0]), 2, 2.5),  # bias flip
         (np.float32([[0.7]]), None, 1, 1.0),                                  # E = 1
         (-np.abs(synth.normal(77, 5 * 256, 3.0)).reshape(5, 256), None, 64, 1.0),  # k = 64
+        (lane_heavy_logits(), None, 8, 1.0),     # winners stacked in a few lanes, with ties
+        (lane_heavy_logits(), np.linspace(-0.01, 0.01, 256, dtype=np.float32), 8, 1.0),
     ]
     for lg, b, k, sc in cases:
         bb = np.zeros(lg.shape[1], np.float32) if b is None else b
