@@ -558,7 +558,10 @@ def main():
     # Dominant-kernel timing with HIP events on the forward's stream: one pass
     # of the pool through the profiled forward, enqueued behind a few graph
     # replays so that every event and kernel is already queued when the GPU
-    # reaches it (the events then bracket the kernel, not host launch gaps).
+    # reaches it.  The library attaches the gate_up / down events to the
+    # gate/up kernel's own dispatch (start and end of its execution) and the
+    # combine event to the end of the down kernel, so gate_up is the kernel's
+    # duration; front, down and combine each include one dispatch gap.
     hev = HipEvents()
     ev_names = ("begin", "gate_up", "down", "combine", "end")
     prof = [{k: hev.create() for k in ev_names} for _ in range(P)]

@@ -308,16 +308,23 @@ int coli_moe_forward_traced(const coli_expert_table* table, const int8_t* xq, co
                             int accumulate, void* workspace, size_t ws_bytes,
                             const coli_moe_trace* trace, void* stream);
 
-/* Stage timing: hipEvent_t handles (created by the caller, passed as void*)
- * that the forward records on `stream` between its internal kernels.  Any
- * may be NULL.  Used by the benchmark to time the dominant kernel.  Not for
- * use under stream capture (a captured record expresses a dependency only). */
+/* Stage timing: hipEvent_t handles (created by the caller with timing
+ * enabled, passed as void*) that the forward records on `stream`.  Any may
+ * be NULL.  Used by the benchmark to time the dominant kernel.  On the
+ * GEMV path (decode / verify) gate_up, down and combine are attached to the
+ * GEMV kernels' own dispatches (hipExtLaunchKernel start / stop events), so
+ * gate_up..down is the gate/up kernel's execution time; on the grouped path
+ * they are markers between the kernels.  Not for use under stream capture
+ * (a captured record expresses a dependency only). */
 typedef struct {
   void* begin;   /* before the dispatch kernels (coli_moe_layer*: before
                     the front end: quantisation, routing, dispatch)     */
-  void* gate_up; /* after dispatch, before the gate/up GEMV            */
-  void* down;    /* after the gate/up GEMV, before the down GEMV       */
-  void* combine; /* after the down GEMV, before the weighted combine   */
+  void* gate_up; /* GEMV: start of the gate/up kernel; grouped: before
+                    the gate/up kernel                                   */
+  void* down;    /* GEMV: end of the gate/up kernel; grouped: between
+                    the gate/up and down kernels                         */
+  void* combine; /* GEMV: end of the down kernel; grouped: before the
+                    weighted combine                                     */
   void* end;     /* after the weighted combine                         */
 } coli_moe_events;
 

@@ -40,6 +40,8 @@
 // measured slower on MI355X than the extra launch.)
 #include "coli_internal.h"
 
+#include <hip/hip_ext.h>
+
 namespace coli {
 namespace {
 
@@ -776,19 +778,34 @@ constexpr int pf_gate_up(int maxt, int bits) { return maxt > 0 && bits > 0 ? 16 
 constexpr int pf_down(int maxt, int bits) { return maxt > 0 && bits > 0 ? 8 : 0; }
 constexpr size_t kLdsLimit = 65536;
 
+// Stage events of the GEMV kernels, attached to the kernels' own dispatches
+// (hipExtLaunchKernelGGL): gu_start / gu_stop take the start and end of the
+// gate/up kernel's execution, dn_stop the end of the down kernel's.  So the
+// gate/up interval is the kernel itself, with no marker packet or dispatch
+// gap inside it.  Any may be null.
+struct GemvEvents {
+  void* gu_start;
+  void* gu_stop;
+  void* dn_stop;
+};
+
 template <int MAXT, int BITS, bool TRACE>
-hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, void* ev_down, hipStream_t s) {
+hipError_t launch_pair(const GuArgs& g, const DnArgs& d, int maxA, const GemvEvents& ev,
+                       hipStream_t s) {
   constexpr int PG = pf_gate_up(MAXT, BITS), PD = pf_down(MAXT, BITS);
   const size_t lds_gu = pass_lds_bytes(MAXT, g.D / 32, blocks_per_ring(PG, BITS));
   const size_t lds_dn = pass_lds_bytes(MAXT, d.F / 32, blocks_per_ring(PD, BITS));
   constexpr int W = gemv_waves(MAXT);
-  hipLaunchKernelGGL((gate_up_kernel<MAXT, PG, BITS, TRACE>),
-                     dim3((unsigned)((g.F / 32 + W - 1) / W), maxA), dim3(kWave * W), lds_gu, s, g);
+  hipExtLaunchKernelGGL((gate_up_kernel<MAXT, PG, BITS, TRACE>),
+                        dim3((unsigned)((g.F / 32 + W - 1) / W), maxA), dim3(kWave * W),
+                        (uint32_t)lds_gu, s, reinterpret_cast<hipEvent_t>(ev.gu_start),
+                        reinterpret_cast<hipEvent_t>(ev.gu_stop), 0, g);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
-  if ((rc = record(ev_down, s)) != hipSuccess) return rc;
-  hipLaunchKernelGGL((down_kernel<MAXT, PD, BITS, TRACE>),
-                     dim3((unsigned)((d.D / 64 + W - 1) / W), maxA), dim3(kWave * W), lds_dn, s, d);
+  hipExtLaunchKernelGGL((down_kernel<MAXT, PD, BITS, TRACE>),
+                        dim3((unsigned)((d.D / 64 + W - 1) / W), maxA), dim3(kWave * W),
+                        (uint32_t)lds_dn, s, nullptr, reinterpret_cast<hipEvent_t>(ev.dn_stop),
+                        0, d);
   return hipGetLastError();
 }
 
@@ -806,22 +823,22 @@ int pass_tokens(int64_t T, int64_t D, int64_t F, int bits) {
 
 template <int BITS, bool TRACE>
 hipError_t launch_gemv_bits(const GuArgs& g, const DnArgs& d, int maxA, int64_t T,
-                            void* ev_down, hipStream_t s) {
+                            const GemvEvents& ev, hipStream_t s) {
   switch (pass_tokens(T, g.D, g.F, BITS)) {
-    case 1: return launch_pair<1, BITS, TRACE>(g, d, maxA, ev_down, s);
-    case 2: return launch_pair<2, BITS, TRACE>(g, d, maxA, ev_down, s);
-    case 4: return launch_pair<4, BITS, TRACE>(g, d, maxA, ev_down, s);
-    default: return launch_pair<8, BITS, TRACE>(g, d, maxA, ev_down, s);
+    case 1: return launch_pair<1, BITS, TRACE>(g, d, maxA, ev, s);
+    case 2: return launch_pair<2, BITS, TRACE>(g, d, maxA, ev, s);
+    case 4: return launch_pair<4, BITS, TRACE>(g, d, maxA, ev, s);
+    default: return launch_pair<8, BITS, TRACE>(g, d, maxA, ev, s);
   }
 }
 
 template <bool TRACE>
 hipError_t launch_gemv(const GuArgs& g, const DnArgs& d, int bits, int maxA, int64_t T,
-                       void* ev_down, hipStream_t s) {
+                       const GemvEvents& ev, hipStream_t s) {
   switch (bits) {
-    case 8: return launch_gemv_bits<8, TRACE>(g, d, maxA, T, ev_down, s);
-    case 2: return launch_gemv_bits<2, TRACE>(g, d, maxA, T, ev_down, s);
-    default: return launch_gemv_bits<4, TRACE>(g, d, maxA, T, ev_down, s);
+    case 8: return launch_gemv_bits<8, TRACE>(g, d, maxA, T, ev, s);
+    case 2: return launch_gemv_bits<2, TRACE>(g, d, maxA, T, ev, s);
+    default: return launch_gemv_bits<4, TRACE>(g, d, maxA, T, ev, s);
   }
 }
 
@@ -894,7 +911,7 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   d.k = f.k;
   d.S = S;
   d.E = E;
-  if ((rc = record(ev.gate_up, s)) != hipSuccess) return rc;
+  const GemvEvents gev = {ev.gate_up, ev.down, ev.combine};
   if (tr) {
     g.tr_pg = tr->p_gate;
     g.tr_pu = tr->p_up;
@@ -902,13 +919,14 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
     g.tr_u = tr->u;
     g.tr_h = tr->h;
     d.tr_pd = tr->p_down;
-    rc = launch_gemv<true>(g, d, t.weight_bits, (int)maxA, T, ev.down, s);
+    rc = launch_gemv<true>(g, d, t.weight_bits, (int)maxA, T, gev, s);
   } else {
-    rc = launch_gemv<false>(g, d, t.weight_bits, (int)maxA, T, ev.down, s);
+    rc = launch_gemv<false>(g, d, t.weight_bits, (int)maxA, T, gev, s);
   }
   }
   if (rc != hipSuccess) return rc;
-  if ((rc = record(ev.combine, s)) != hipSuccess) return rc;
+  // the GEMV path attaches `combine` to the end of its down kernel
+  if (grouped && (rc = record(ev.combine, s)) != hipSuccess) return rc;
   const dim3 cgrid((unsigned)((D / 4 + 255) / 256), (unsigned)T);
   if (f.k == 8)
     hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(256), 0, s, ws.o, f.idx, f.w, D, f.k, E, S,

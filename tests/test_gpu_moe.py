@@ -172,6 +172,23 @@ def test_invalid_index_is_reported_not_faulting(tiny):
     assert coli.coli_moe_status(ws) == coli.COLI_OK
 
 
+def test_invalid_index_one_token(tiny):
+    """One token (the quarter-row path): an out-of-range expert leaves its
+    slot without a live expert; the flag is raised and the rest is finite."""
+    w, table, _ = tiny
+    xq = torch.ones((1, w.D), dtype=torch.int8, device=dev)
+    xd = torch.ones((1, w.D // 32), dtype=torch.float32, device=dev)
+    wt = torch.full((1, w.k), 0.5, dtype=torch.float32, device=dev)
+    y = torch.empty((1, w.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(coli.coli_moe_workspace_bytes(table, 1, w.k), dtype=torch.uint8, device=dev)
+    for bad in ([[0, 16]], [[5, 5]], [[-1, 3]]):
+        coli.coli_moe_forward(table, xq, xd, to_dev(np.int32(bad)), wt, y, ws)
+        assert coli.coli_moe_status(ws) == coli.COLI_E_INDEX, bad
+        assert torch.isfinite(y).all(), bad
+    coli.coli_moe_forward(table, xq, xd, to_dev(np.int32([[0, 1]])), wt, y, ws)
+    assert coli.coli_moe_status(ws) == coli.COLI_OK
+
+
 # ---------------------------------------------------------------- page-scale layer
 @pytest.fixture(scope="module")
 def big():
