@@ -355,6 +355,24 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
                       int accumulate, void* workspace, size_t ws_bytes,
                       const coli_moe_trace* trace, const coli_moe_events* events, void* stream);
 
+/* One pre-norm residual MoE block in place: h <- h + MoE(RMSNorm(h)), the
+ * layer form of a deep decode stack (router and norm stay F32: aitrends.kr,
+ * "알아두면 좋은 것"; shared expert and routed experts combined as in
+ * coli_moe_forward).  RMSNorm has unit gain and the arithmetic of
+ * coli_rmsnorm_q8; routing, forward and combine are those of coli_moe_layer
+ * with accumulate = 1, so the result is bit-identical to coli_rmsnorm_q8 +
+ * coli_route_topk + coli_moe_forward(accumulate = 1).  For small batches
+ * (T <= 64 and T*k <= 1024) the RMSNorm + Q8_0, routing and dispatch run in
+ * one kernel, so a decode block is 4 kernels.  h [T][D] f32 (device, 16-byte
+ * aligned), read and overwritten; logits [T][E] f32; bias [E] f32 or NULL;
+ * eps finite and >= 0.  The workspace is coli_moe_layer's
+ * (coli_moe_layer_workspace_bytes(table, T, k) bytes, clobbered, calls
+ * sharing it must not overlap).  Argument errors return before any launch;
+ * index errors are reported by coli_moe_status. */
+int coli_moe_block(const coli_expert_table* table, float* h, const float* logits,
+                   const float* bias, int64_t T, int32_t k, float routed_scale, float eps,
+                   void* workspace, size_t ws_bytes, void* stream);
+
 /* Synchronises `stream`, then reports the device-side checks of the last
  * forward or layer call that used `workspace`: COLI_OK, COLI_E_INDEX or
  * COLI_E_TIER. */

@@ -35,7 +35,7 @@ EXPORTED = [
     "coli_moe_workspace_bytes",
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
     "coli_moe_forward_path", "coli_moe_path",
-    "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex",
+    "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex", "coli_moe_block",
     "coli_moe_status", "coli_status_string", "coli_last_hip_error",
     "coli_tier_table_bytes", "coli_tier_init", "coli_tier_plan", "coli_tier_fetch",
     "coli_tier_status", "coli_tier_rank",
@@ -117,6 +117,8 @@ def lib():
                                 sz, _P], ctypes.c_int),
             "coli_moe_layer_ex": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P, ctypes.c_int,
                                    _P, sz, _P, _P, _P], ctypes.c_int),
+            "coli_moe_block": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, ctypes.c_float, _P,
+                                sz, _P], ctypes.c_int),
             "coli_moe_status": ([_P, sz, _P], ctypes.c_int),
             "coli_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "coli_tier_table_bytes": ([_I32, _I64, _I64, _I32, _P, _P, _P, _P], sz),
@@ -432,6 +434,18 @@ def coli_moe_layer(table: ExpertTable, x, logits, bias, k, y, workspace, routed_
                                    routed_scale, _ptr(y), int(bool(accumulate)), _ptr(workspace),
                                    ws, None if tr is None else ctypes.byref(tr),
                                    None if ev is None else ctypes.byref(ev), _stream(stream)))
+
+
+def coli_moe_block(table: ExpertTable, h, logits, bias, k, workspace, eps=1e-6,
+                   routed_scale=1.0, stream=None):
+    """In place: h [T][D] f32 <- h + MoE(RMSNorm(h)); logits [T][E] f32, bias [E] f32 or None."""
+    import torch
+    _dtype(h, torch.float32, "h"); _dtype(logits, torch.float32, "logits")
+    _dtype(bias, torch.float32, "bias")
+    _check("coli_moe_block",
+           lib().coli_moe_block(table.ref(), _ptr(h), _ptr(logits), _ptr(bias), h.shape[0], k,
+                                routed_scale, eps, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def coli_moe_status(workspace, stream=None) -> int:

@@ -399,10 +399,14 @@ size_t coli_moe_layer_workspace_bytes(const coli_expert_table* table, int64_t T,
   return layer_workspace_layout(nullptr, table, T, k).bytes;
 }
 
-int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const float* logits,
+// The layer from f32 activations (norm: from the residual stream h, whose
+// RMSNorm is quantised) and router logits: the fused front end for small
+// batches, else Q8_0 (or RMSNorm + Q8_0) and routing kernels, then the forward.
+static int layer_impl(const coli_expert_table* table, const float* x, const float* logits,
                       const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
                       int accumulate, void* workspace, size_t ws_bytes,
-                      const coli_moe_trace* trace, const coli_moe_events* events, void* stream) {
+                      const coli_moe_trace* trace, const coli_moe_events* events, bool norm,
+                      float eps, void* stream) {
   int rc = table_check(table);
   if (rc) return rc;
   const int E = table->n_routed, S = table->n_shared;
@@ -410,6 +414,7 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
   if (T < 0 || T * (int64_t)(k + S) > 0x7FFFFFFF) return COLI_E_SHAPE;
   if (accumulate != 0 && accumulate != 1) return COLI_E_INVAL;
   if (!std::isfinite(routed_scale)) return COLI_E_INVAL;
+  if (norm && !(std::isfinite(eps) && eps >= 0.0f)) return COLI_E_INVAL;
   if (T == 0) return COLI_OK;
   if (!x || !logits || !y || !workspace) return COLI_E_INVAL;
   if (!al16(x) || !al4(logits) || !al4(bias) || !al16(y) || !al16(workspace)) return COLI_E_INVAL;
@@ -431,9 +436,10 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
   if (small) {
     e = coli::launch_prologue_small(x, logits, bias, T, E, S, k, routed_scale, D, l.xq, l.xd,
                                     l.fwd.xsum8, l.idx, l.w, l.fwd.counts, l.fwd.lists,
-                                    l.fwd.n_active, l.fwd.active, l.fwd.err, s);
+                                    l.fwd.n_active, l.fwd.active, l.fwd.err, norm, eps, s);
   } else {
-    e = coli::launch_quant_act_q8(x, T, D, l.xq, l.xd, s);
+    e = norm ? coli::launch_rmsnorm_q8(x, T, D, eps, l.xq, l.xd, nullptr, s)
+             : coli::launch_quant_act_q8(x, T, D, l.xq, l.xd, s);
     if (e == hipSuccess) e = coli::launch_route_topk(logits, bias, T, E, k, routed_scale, l.idx, l.w, s);
   }
   if (e != hipSuccess) return hip_fail(e);
@@ -454,6 +460,21 @@ int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const floa
   a.dispatched = small;
   e = coli::launch_moe_forward(a, s);
   return e == hipSuccess ? COLI_OK : hip_fail(e);
+}
+
+int coli_moe_layer_ex(const coli_expert_table* table, const float* x, const float* logits,
+                      const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                      int accumulate, void* workspace, size_t ws_bytes,
+                      const coli_moe_trace* trace, const coli_moe_events* events, void* stream) {
+  return layer_impl(table, x, logits, bias, T, k, routed_scale, y, accumulate, workspace,
+                    ws_bytes, trace, events, false, 0.0f, stream);
+}
+
+int coli_moe_block(const coli_expert_table* table, float* h, const float* logits,
+                   const float* bias, int64_t T, int32_t k, float routed_scale, float eps,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  return layer_impl(table, h, logits, bias, T, k, routed_scale, h, 1, workspace, ws_bytes,
+                    nullptr, nullptr, true, eps, stream);
 }
 
 int coli_moe_layer(const coli_expert_table* table, const float* x, const float* logits,

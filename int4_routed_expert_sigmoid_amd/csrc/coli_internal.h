@@ -68,6 +68,52 @@ __device__ __forceinline__ int q8_quad(float4 v, float* d_out, int* sum_out) {
   return (q0 & 0xFF) | ((q1 & 0xFF) << 8) | ((q2 & 0xFF) << 16) | ((int)((unsigned)q3 << 24));
 }
 
+// RMSNorm with unit gain, then Q8_0, of one row of D values (D % 32 == 0),
+// by one 256-thread workgroup: the sum of squares in fp64 (each square is
+// exact; per-thread strided partials, a lane butterfly, then the four
+// wavefronts' sums as (w0 + w1) + (w2 + w3)), r = (float)(1 / sqrt(ss / D +
+// eps)) in fp64, x = h * r in fp32, then q8_quad.  Writes the packed codes,
+// the block scales, and when non-null the blocks' -8 * code sums and r.
+// red / rsh: workgroup LDS (4 doubles, 1 float).  Every thread must call it.
+__device__ __forceinline__ void rmsnorm_q8_row(const float* __restrict__ hrow, int64_t D, float eps,
+                                               int* __restrict__ q, float* __restrict__ d,
+                                               int32_t* __restrict__ xsum8,
+                                               float* __restrict__ r_out, double* red,
+                                               float* rsh) {
+  const float4* hr = reinterpret_cast<const float4*>(hrow);
+  double ss = 0.0;
+  for (int64_t c = threadIdx.x; c < D / 4; c += 256) {
+    const float4 v = hr[c];
+    ss += (double)v.x * (double)v.x;
+    ss += (double)v.y * (double)v.y;
+    ss += (double)v.z * (double)v.z;
+    ss += (double)v.w * (double)v.w;
+  }
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float r = (float)(1.0 / sqrt(tot / (double)D + (double)eps));
+    *rsh = r;
+    if (r_out) *r_out = r;
+  }
+  __syncthreads();
+  const float r = *rsh;
+  for (int64_t c = threadIdx.x; c < D / 4; c += 256) {   // D/4 is a multiple of 8
+    const float4 v = hr[c];
+    const float4 xh = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+    float dv;
+    int sum;
+    q[c] = q8_quad(xh, &dv, &sum);
+    if ((c & 7) == 0) {
+      d[c >> 3] = dv;
+      if (xsum8) xsum8[c >> 3] = -8 * sum;
+    }
+  }
+}
+
 // Read-only data that is uniform across a wavefront (the token's Q8 block,
 // dispatch lists) is read through the constant address space: the compiler
 // then issues scalar loads, which complete on lgkmcnt and leave the vector
@@ -143,12 +189,14 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, i
                            const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s);
 
 // Fused front of a small batch (one workgroup): Q8_0 of x (+ block sums),
-// routing, dispatch lists, compaction and the index check.
+// routing, dispatch lists, compaction and the index check.  norm: x is the
+// residual stream and RMSNorm(x) (unit gain, eps) is quantised instead.
 hipError_t launch_prologue_small(const float* x, const float* logits, const float* bias, int64_t T,
                                  int E, int S, int k, float routed_scale, int64_t D, int8_t* xq,
                                  float* xd, int32_t* xsum8, int32_t* idx, float* w,
                                  int32_t* counts, int32_t* lists, int32_t* n_active,
-                                 int32_t* active, int32_t* err, hipStream_t s);
+                                 int32_t* active, int32_t* err, bool norm, float eps,
+                                 hipStream_t s);
 // Largest batch the fused front handles.
 constexpr int64_t kPrologueMaxEntries = 1024;   // T * k
 constexpr int64_t kPrologueMaxTokens = 64;

@@ -260,36 +260,8 @@ __global__ void __launch_bounds__(256) rmsnorm_q8_kernel(const float* __restrict
   __shared__ double red[4];
   __shared__ float rsh;
   const int64_t row = blockIdx.x;
-  const float4* hr = reinterpret_cast<const float4*>(h + row * D);
-  double ss = 0.0;
-  for (int64_t c = threadIdx.x; c < D / 4; c += 256) {
-    const float4 v = hr[c];
-    ss += (double)v.x * (double)v.x;
-    ss += (double)v.y * (double)v.y;
-    ss += (double)v.z * (double)v.z;
-    ss += (double)v.w * (double)v.w;
-  }
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  if (lane == 0) red[wave] = ss;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const double tot = (red[0] + red[1]) + (red[2] + red[3]);
-    const float r = (float)(1.0 / sqrt(tot / (double)D + (double)eps));
-    rsh = r;
-    if (r_out) r_out[row] = r;
-  }
-  __syncthreads();
-  const float r = rsh;
-  for (int64_t c = threadIdx.x; c < D / 4; c += 256) {   // D/4 is a multiple of 8
-    const float4 v = hr[c];
-    const float4 xh = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
-    float dv;
-    int sum;
-    const int packed = q8_quad(xh, &dv, &sum);
-    q[row * (D / 4) + c] = packed;
-    if ((c & 7) == 0) d[row * (D / 32) + (c >> 3)] = dv;
-  }
+  rmsnorm_q8_row(h + row * D, D, eps, q + row * (D / 4), d + row * (D / 32), nullptr,
+                 r_out ? r_out + row : nullptr, red, &rsh);
 }
 
 int64_t grid_for(int64_t work, int64_t per_block, int64_t cap) {

@@ -278,6 +278,8 @@ struct PrologueArgs {
   int32_t* n_active;
   int32_t* active;
   int32_t* err;
+  int norm;        // 1: x is the residual stream h; quantise RMSNorm(h) (unit gain)
+  float eps;
 };
 
 // The whole front of a small batch.  Workgroup 0 (4 wavefronts): routing (one
@@ -292,6 +294,15 @@ __global__ void __launch_bounds__(256) prologue_small_kernel(PrologueArgs a) {
   __shared__ int bad_any;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   if (tid == 0) bad_any = 0;
+  if (blockIdx.x > 0 && a.norm) {
+    // workgroup 1 + t: RMSNorm and Q8_0 of token t (the rmsnorm_q8 arithmetic)
+    __shared__ double red[4];
+    __shared__ float rsh;
+    const int64_t t = blockIdx.x - 1;
+    rmsnorm_q8_row(a.x + t * a.D, a.D, a.eps, reinterpret_cast<int*>(a.xq + t * a.D),
+                   a.xd + t * (a.D / 32), a.xsum8 + t * (a.D / 32), nullptr, red, &rsh);
+    return;
+  }
   if (blockIdx.x > 0) {
     // workgroups 1..: Q8_0 of x in groups of 4 values, 8 lanes per 32-value
     // block (groups never straddle a block: 256-thread strides, n4 % 8 == 0)
@@ -408,11 +419,13 @@ hipError_t launch_prologue_small(const float* x, const float* logits, const floa
                                  int E, int S, int k, float routed_scale, int64_t D, int8_t* xq,
                                  float* xd, int32_t* xsum8, int32_t* idx, float* w,
                                  int32_t* counts, int32_t* lists, int32_t* n_active,
-                                 int32_t* active, int32_t* err, hipStream_t s) {
+                                 int32_t* active, int32_t* err, bool norm, float eps,
+                                 hipStream_t s) {
   PrologueArgs a = {x, logits, bias, T, D, E, S, k, routed_scale, xq, xd, xsum8, idx, w,
-                    counts, lists, n_active, active, err};
+                    counts, lists, n_active, active, err, norm ? 1 : 0, eps};
   int64_t qgroups = (T * D / 4 + 255) / 256;   // one group of 4 values per thread
   if (qgroups > 256) qgroups = 256;
+  if (norm) qgroups = T;                       // one workgroup per token row
   hipLaunchKernelGGL(prologue_small_kernel, dim3((unsigned)(1 + qgroups)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -176,6 +176,25 @@ def test_validation_layer():
     assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK
 
 
+def test_validation_block():
+    """coli_moe_block: the layer's checks plus eps, all before any HIP call."""
+    L = coli.lib()
+    t = _table()
+    ws = L.coli_moe_layer_workspace_bytes(ctypes.byref(t), 4, 2)
+    f = L.coli_moe_block
+    args = lambda tab, T=4, k=2, sc=1.0, eps=1e-6, wsb=ws, h=FAKE: (
+        ctypes.byref(tab), h, FAKE, None, T, k, sc, eps, FAKE, wsb, None)
+    assert f(*args(t, wsb=ws - 1)) == coli.COLI_E_WORKSPACE
+    assert f(*args(t, k=0)) == coli.COLI_E_SHAPE
+    assert f(*args(t, eps=-1e-6)) == coli.COLI_E_INVAL
+    assert f(*args(t, eps=float("nan"))) == coli.COLI_E_INVAL
+    assert f(*args(t, eps=float("inf"))) == coli.COLI_E_INVAL
+    assert f(*args(t, sc=float("nan"))) == coli.COLI_E_INVAL
+    assert f(*args(t, h=None)) == coli.COLI_E_INVAL
+    assert f(*args(t, h=FAKE + 4)) == coli.COLI_E_INVAL     # h must be 16-byte aligned
+    assert f(*args(t, T=0, wsb=0)) == coli.COLI_OK
+
+
 def test_tier_host_checks():
     """Tier entry points: sizes, rank (host logic), and argument checks."""
     import numpy as np

@@ -68,6 +68,21 @@ class GpuStack:
         return h.cpu().numpy(), kept
 
 
+class BlockStack(GpuStack):
+    """The same stack through coli_moe_block (RMSNorm + Q8, routing and
+    dispatch in one front kernel for small batches; h updated in place)."""
+
+    def __init__(self, w, tables, T):
+        super().__init__(w, tables, T)
+        self.ws = torch.empty(coli.coli_moe_layer_workspace_bytes(tables[0], T, w.k),
+                              dtype=torch.uint8, device=dev)
+
+    def layer(self, h, layer, token0):
+        lg = to_dev(synth.logits(self.w, self.T, token0, layer))
+        coli.coli_moe_block(self.tables[layer], h, lg, self.bias[layer], self.w.k, self.ws,
+                            eps=EPS)
+
+
 def oracle_layer(w, ox, h, layer, token0):
     T = h.shape[0]
     xh, _ = oracle.rmsnorm(h, EPS)
@@ -119,6 +134,31 @@ def test_tiny_stack_batched(tiny_stack):
     assert_bitexact("h after 40 layers, 256 tokens", got, ref)
 
 
+def test_tiny_block_stack_token_by_token(tiny_stack):
+    """coli_moe_block, one token per pass (fused front, GEMV path), 40 layers, bit-exact."""
+    w, tables, oxs = tiny_stack
+    n = 8
+    h0 = synth.hidden0(w, n, 300)
+    ref, _ = oracle_stack(w, oxs, h0, 300)
+    stack = BlockStack(w, tables, 1)
+    for t in range(n):
+        got, _ = stack.run(h0[t:t + 1], 300 + t)
+        assert_bitexact(f"block h after 40 layers, token {t}", got, ref[t:t + 1])
+
+
+@pytest.mark.parametrize("T", [4, 64, 256])
+def test_tiny_block_stack_batched(tiny_stack, T):
+    """coli_moe_block with T tokens per pass: the fused front (one RMSNorm
+    workgroup per token) with the GEMV path (4) and the grouped path (64),
+    and the separate RMSNorm / routing kernels with the grouped path (256);
+    40 layers, bit-exact."""
+    w, tables, oxs = tiny_stack
+    h0 = synth.hidden0(w, T, 400)
+    ref, _ = oracle_stack(w, oxs, h0, 400)
+    got, _ = BlockStack(w, tables, T).run(h0, 400)
+    assert_bitexact(f"block h after 40 layers, {T} tokens", got, ref)
+
+
 def test_page_shape_stack_sampled():
     """40 page-shape layers (194 GB of tables) on the GPU for 2 tokens; the
     oracle recomputes layers 0, 1, 20 and 39 from the GPU's input to them."""
@@ -135,5 +175,10 @@ def test_page_shape_stack_sampled():
             hin = h0[t:t + 1] if layer == 0 else kept[layer - 1]
             ref, _ = oracle_layer(w, OracleExperts(w, layer), hin, layer, t)
             assert_bitexact(f"token {t} layer {layer}", kept[layer], ref)
+        # the fused block entry point gives the same stack bit for bit
+        bfinal, bkept = BlockStack(w, tables, 1).run(h0[t:t + 1], t, keep=keep)
+        assert_bitexact(f"token {t} block stack, final h", bfinal, final)
+        for layer in sorted(keep):
+            assert_bitexact(f"token {t} block stack, layer {layer}", bkept[layer], kept[layer])
     del tables
     torch.cuda.empty_cache()
