@@ -388,6 +388,57 @@ def tier_leg(coli, synth, torch, layers=4, slots=64, warm=32, timed=32):
     return res
 
 
+def deep_leg(coli, synth, torch, tokens=48, warm=16):
+    """The deep decode stack: 40 page-shape layers (194 GB of int4 tables, all
+    resident in HBM), Zipf(1.1)-skewed routing per layer, each layer a pre-norm
+    residual block h <- h + MoE(RMSNorm(h)) through coli_moe_block (4 kernels:
+    RMSNorm+Q8, routing and dispatch fused; gate/up; down; combine into h).
+    Tokens run one after another, each through all 40 layers, captured in HIP
+    graphs.  A token streams 40 x 9 experts = 6.81 GB of weights, so nothing
+    is reused from the 256 MB Infinity Cache between a layer's visits."""
+    w = synth.WORKLOADS[4]
+    L = w.layers
+    tables = [build_table(w, coli, synth, torch, layer=l) for l in range(L)]
+    N = warm + tokens
+    lg = [torch.from_numpy(synth.logits(w, N, 0, l)).cuda() for l in range(L)]
+    bias = [torch.from_numpy(synth.router_bias(w, l)).cuda() for l in range(L)]
+    h = torch.from_numpy(synth.hidden0(w, N)).cuda()
+    ws = torch.empty(coli.coli_moe_layer_workspace_bytes(tables[0], 1, w.k), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(t0, t1):
+        for i in range(t0, t1):
+            for l in range(L):
+                coli.coli_moe_block(tables[l], h[i:i + 1], lg[l][i:i + 1], bias[l], w.k, ws)
+
+    g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        run(0, warm)
+    with torch.cuda.graph(g_timed):
+        run(warm, N)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_timed.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    if coli.coli_moe_status(ws) != coli.COLI_OK or not torch.isfinite(h).all():
+        raise RuntimeError("deep leg: device-side check failed")
+    ms = e0.elapsed_time(e1) / tokens
+    per_token = L * (w.k + w.S) * sum(expert_bytes(w))
+    res = {"workload": w.name + ", 40 x 4.86 GB tables in HBM, coli_moe_block per layer",
+           "tokens_timed": tokens, "ms_per_token": round(ms, 4),
+           "us_per_layer": round(1000 * ms / L, 2), "tok_s": round(1000.0 / ms, 1),
+           "weight_bytes_per_token": per_token,
+           "weight_gbps": round(per_token / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(per_token / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del g_warm, g_timed, tables
+    torch.cuda.empty_cache()
+    return res
+
+
 def paths_leg(table, coli, synth, torch, reps=8):
     """The per-shape path choice, measured: the forward of T tokens (page
     shape, router bias N(0, 0.1)) on the GEMV and on the grouped path; the
@@ -464,6 +515,8 @@ def main():
     ap.add_argument("--no-head", action="store_true", help="skip the int8 head and int2 legs")
     ap.add_argument("--no-tier", action="store_true", help="skip the expert-tier leg")
     ap.add_argument("--no-paths", action="store_true", help="skip the path-choice leg")
+    ap.add_argument("--no-deep", action="store_true",
+                    help="skip the 40-layer deep decode stack leg (194 GB of tables)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 8 device-to-device copies of this many bytes (the known-size "
                          "kernel that scales the HBM byte counters under rocprofv3 --pmc)")
@@ -630,6 +683,8 @@ def main():
         out["int2"] = int2_leg(coli, synth, torch, hev)
     if not args.no_tier:
         out["tier"] = tier_leg(coli, synth, torch)
+    if not args.no_deep:
+        out["deep"] = deep_leg(coli, synth, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out), flush=True)
