@@ -35,9 +35,12 @@
 // The SwiGLU, the row scale and the Q8_0 re-quantisation of h are fused into
 // the gate/up epilogue; the routing-weighted combine runs as its own kernel in
 // slot order (shared expert first), which keeps it deterministic.  (Folding it
-// into the down kernel as a last-arriver reduction needs agent-scope release/
-// acquire fences, which write back and invalidate the L2 of every XCD and
-// measured slower on MI355X than the extra launch.)
+// into the down kernel as a last-arriver reduction measured no faster on
+// MI355X: with agent-scope release/acquire fences, which write back and
+// invalidate the L2 of every XCD, it was slower; with write-through output
+// stores, a device-scope counter and coherent loads instead, the last
+// workgroup's store-completion, atomic and load round trips cost what the
+// extra launch does.)
 #include "coli_internal.h"
 
 #include <hip/hip_ext.h>
