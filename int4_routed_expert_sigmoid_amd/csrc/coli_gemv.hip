@@ -558,8 +558,78 @@ __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
 // and stores nothing.
 constexpr int gemv_waves(int maxt) { return maxt >= 4 ? 4 : 1; }
 
+// gate/up of a one-token pass (one wavefront per row group).  The token is
+// token 0 whatever the routing, so its blocks are staged first, with no
+// dependent load before them; the expert's weight ring starts as soon as the
+// active-expert load returns, between the staging loads and the LDS stores.
+template <int PF, int BITS, bool TRACE>
+__device__ __forceinline__ void gate_up_one_token(const GuArgs& a) {
+  const int slot = blockIdx.y, lane = (int)threadIdx.x;
+  const int NB = (int)(a.D / 32);
+  const int64_t G = a.F / 32;
+  const int grp = (int)blockIdx.x;       // grid.x == G at one wavefront per workgroup
+  const int NU = row_chunks(NB, BITS);
+  unsigned char* lds = gemv_lds();
+  Ring<PF> ring;
+  int e = 0, es = -1;
+  stage_token<1>(lds, 0, a.xq, a.xd, a.xsum8, NB, lane, kWave, BITS == 2 ? 2 : 0, [&] {
+    const int n_active = *as_const(a.n_active);
+    e = as_const(a.active)[slot];
+    es = slot < n_active ? storage_of(a.slot_of, a.n_store, e, a.err) : -1;
+    // issued on every path (expert 0 stands in when there is none), so the
+    // memory-counter waits after it count the whole ring
+    const int esafe = es < 0 ? 0 : es;
+    ring.template start<PF>(
+        reinterpret_cast<const char*>(a.gu_q + ((size_t)esafe * G + grp) * (size_t)NU * kWave),
+        16u * (uint32_t)lane, NU);
+  });
+  if (es < 0) return;                    // uniform: one wavefront
+  clear_tail_records<1>(NB, blocks_per_ring(PF, BITS), lane, kWave);
+  const float rs = a.gu_s[((size_t)es * G + grp) * kWave + lane];
+  const int pair = as_const(a.lists)[(size_t)e * a.T];
+  int32_t* trow[1] = {nullptr};
+  if (TRACE) {
+    int32_t* base = lane < 32 ? a.tr_pg : a.tr_pu;
+    if (base) trow[0] = base + ((size_t)pair * a.F + 32 * (size_t)grp + (lane & 31)) * NB;
+  }
+  __syncthreads();
+  float acc[1] = {0.0f};
+  stream_pass<1, PF, BITS, TRACE>(1, ring, acc, trow);
+  const float v = acc[0] * rs;              // g (lanes 0-31) or u (lanes 32-63)
+  const float up = __shfl_down(v, 32);      // lanes 0-31 receive their up row
+  const float h = silu_f32(v) * up;
+  float amax = fabsf(h);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+  const float d = amax / 127.0f;
+  const int q = q8_code(h, d);
+  int qs = q;
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) qs += __shfl_xor(qs, off, 32);
+  if (lane < 32) {
+    const size_t p = (size_t)pair;
+    const size_t r = 32 * (size_t)grp + lane;
+    a.hq[p * a.F + r] = (int8_t)q;
+    if (lane == 0) {
+      a.hd[p * G + grp] = d;
+      a.hsum8[p * G + grp] = -8 * qs;
+    }
+    if (TRACE) {
+      if (a.tr_g) a.tr_g[p * a.F + r] = v;
+      if (a.tr_u) a.tr_u[p * a.F + r] = up;
+      if (a.tr_h) a.tr_h[p * a.F + r] = h;
+    }
+  }
+}
+
 template <int MAXT, int PF, int BITS, bool TRACE>
 __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a) {
+  if constexpr (MAXT == 1) {
+    if (a.T == 1) {
+      gate_up_one_token<PF, BITS, TRACE>(a);
+      return;
+    }
+  }
   constexpr int W = gemv_waves(MAXT);
   const int slot = blockIdx.y;
   const int n_active = *as_const(a.n_active);   // both loads in flight together;
