@@ -40,10 +40,13 @@ __device__ __forceinline__ uint32_t ordered_bits(float c) {
 // experts' sigmoid scores are fetched by their slot lanes from the lanes that
 // computed them (no second read of the logits) and summed in slot order
 // through readlane.
+// KC > 0: k == KC known at compile time (the rounds and the sum unrolled).
+template <int KC = 0>
 __device__ __forceinline__ void route_token(const float* __restrict__ lg,
-                                            const float* __restrict__ bias, int E, int k,
+                                            const float* __restrict__ bias, int E, int k_rt,
                                             float routed_scale, int lane, int* out_idx,
                                             float* out_w) {
+  const int k = KC > 0 ? KC : k_rt;
   // all eight loads first (indices clamped into [0, E)), then the scores
   float lv[4], bv[4];
 #pragma unroll
@@ -282,6 +285,42 @@ struct PrologueArgs {
   float eps;
 };
 
+// One token: every wavefront routes it (the same result in each) and writes
+// its share of the dispatch from registers, with no barrier.  The k experts
+// are distinct and in [0, E) (k <= E), so every entry is listed at position 0
+// of its expert's list and the index check passes.  KC > 0: k == KC known at
+// compile time, so the selected experts are read into scalar registers once
+// and every loop over them is unrolled.
+template <int KC>
+__device__ __forceinline__ void one_token_front(const PrologueArgs& a, int lane, int wave,
+                                                int tid) {
+  const int k = KC > 0 ? KC : a.k, E = a.E, S = a.S;
+  int my_idx;
+  float my_w;
+  route_token<KC>(a.logits, a.bias, E, k, a.routed_scale, lane, &my_idx, &my_w);
+  int rank = 0;   // position of this lane's expert among the selected, ascending
+  for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(my_idx, j) < my_idx;
+  if (wave == 0 && lane < k) {
+    a.idx[lane] = my_idx;
+    a.w[lane] = my_w;
+    a.lists[my_idx] = lane;      // pair 0 * (k + S) + slot
+    a.active[rank] = my_idx;     // the shared expert E sorts after every routed one
+  }
+  for (int e = tid; e < E + S; e += 256) {
+    int c = e == E ? 1 : 0;
+    for (int j = 0; j < k; ++j) c |= __builtin_amdgcn_readlane(my_idx, j) == e;
+    a.counts[e] = c;
+  }
+  if (tid == 0) {
+    if (S) {
+      a.lists[E] = k;            // the shared expert takes slot k
+      a.active[k] = E;
+    }
+    *a.n_active = k + S;
+    *a.err = 0;
+  }
+}
+
 // The whole front of a small batch.  Workgroup 0 (4 wavefronts): routing (one
 // wavefront per token), then the dispatch lists (one thread per routing
 // entry, entries from LDS), the active-expert compaction and the index check;
@@ -322,35 +361,8 @@ __global__ void __launch_bounds__(256) prologue_small_kernel(PrologueArgs a) {
     return;
   }
   if (a.T == 1) {
-    // One token: every wavefront routes it (the same result in each) and
-    // writes its share of the dispatch from registers, with no barrier.  The
-    // k experts are distinct and in [0, E) (k <= E), so every entry is listed
-    // at position 0 of its expert's list and the index check passes.
-    int my_idx;
-    float my_w;
-    route_token(a.logits, a.bias, a.E, a.k, a.routed_scale, lane, &my_idx, &my_w);
-    const int k = a.k, E = a.E, S = a.S;
-    int rank = 0;   // position of this lane's expert among the selected, ascending
-    for (int j = 0; j < k; ++j) rank += __builtin_amdgcn_readlane(my_idx, j) < my_idx;
-    if (wave == 0 && lane < k) {
-      a.idx[lane] = my_idx;
-      a.w[lane] = my_w;
-      a.lists[my_idx] = lane;      // pair 0 * (k + S) + slot
-      a.active[rank] = my_idx;     // the shared expert E sorts after every routed one
-    }
-    for (int e = tid; e < E + S; e += 256) {
-      int c = e == E ? 1 : 0;
-      for (int j = 0; j < k; ++j) c |= __builtin_amdgcn_readlane(my_idx, j) == e;
-      a.counts[e] = c;
-    }
-    if (tid == 0) {
-      if (S) {
-        a.lists[E] = k;            // the shared expert takes slot k
-        a.active[k] = E;
-      }
-      *a.n_active = k + S;
-      *a.err = 0;
-    }
+    if (a.k == 8) one_token_front<8>(a, lane, wave, tid);
+    else one_token_front<0>(a, lane, wave, tid);
     return;
   }
   // workgroup 0: routing, one wavefront per token, then the dispatch
