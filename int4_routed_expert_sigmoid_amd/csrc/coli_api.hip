@@ -93,6 +93,11 @@ MoeWorkspace moe_workspace_layout(void* base, int E, int S, int64_t D, int64_t F
   w.hd = static_cast<float*>(take(sizeof(float) * P * (size_t)(F / 32)));
   w.hsum8 = static_cast<int32_t*>(take(sizeof(int32_t) * P * (size_t)(F / 32)));
   w.o = static_cast<float*>(take(sizeof(float) * P * (size_t)D));
+  if (T == 1) {
+    w.hq_slot = static_cast<int8_t*>(take(A * (size_t)F));
+    w.hd_slot = static_cast<float*>(take(sizeof(float) * A * (size_t)(F / 32)));
+    w.hs_slot = static_cast<int32_t*>(take(sizeof(int32_t) * A * (size_t)(F / 32)));
+  }
   const size_t chunks = (size_t)mfma_max_chunks(T, k, E, S);
   w.xh = static_cast<uint16_t*>(take(2 * (size_t)T * (size_t)D));
   w.h16 = static_cast<uint16_t*>(take(2 * P * (size_t)F));

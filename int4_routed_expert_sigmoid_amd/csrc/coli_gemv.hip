@@ -67,6 +67,9 @@ struct GuArgs {
   int8_t* hq;
   float* hd;
   int32_t* hsum8;
+  int8_t* hq_slot;         // one-token passes: Q8(h) also in active-slot order
+  float* hd_slot;
+  int32_t* hs_slot;
   const int32_t* slot_of;  // expert tier: storage position of each expert, or null
   int n_store;             // positions the table holds
   int32_t* err;
@@ -85,6 +88,9 @@ struct DnArgs {
   const int8_t* hq;
   const float* hd;
   const int32_t* hsum8;
+  const int8_t* hq_slot;   // one-token passes: Q8(h) in active-slot order
+  const float* hd_slot;
+  const int32_t* hs_slot;
   const int32_t* counts;
   const int32_t* lists;
   const int32_t* n_active;
@@ -610,9 +616,14 @@ __device__ __forceinline__ void gate_up_one_token(const GuArgs& a) {
     const size_t p = (size_t)pair;
     const size_t r = 32 * (size_t)grp + lane;
     a.hq[p * a.F + r] = (int8_t)q;
+    if (a.hq_slot) a.hq_slot[(size_t)slot * a.F + r] = (int8_t)q;
     if (lane == 0) {
       a.hd[p * G + grp] = d;
       a.hsum8[p * G + grp] = -8 * qs;
+      if (a.hq_slot) {
+        a.hd_slot[(size_t)slot * G + grp] = d;
+        a.hs_slot[(size_t)slot * G + grp] = -8 * qs;
+      }
     }
     if (TRACE) {
       if (a.tr_g) a.tr_g[p * a.F + r] = v;
@@ -724,8 +735,52 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
   }
 }
 
+// down of a one-token pass (one wavefront per 64-row group).  Its token
+// records are the slot's Q8(h), which gate/up also stored in active-slot
+// order, so they are staged first with no dependent load; the weight ring
+// starts as soon as the active-expert load returns, and the pair (the output
+// row) is looked up while the staging completes.
+template <int PF, int BITS, bool TRACE>
+__device__ __forceinline__ void down_one_token(const DnArgs& a) {
+  const int slot = blockIdx.y, lane = (int)threadIdx.x;
+  const int NB = (int)(a.F / 32);
+  const int grp = (int)blockIdx.x;       // grid.x == D / 64 at one wavefront per workgroup
+  const int NU = row_chunks(NB, BITS);
+  unsigned char* lds = gemv_lds();
+  Ring<PF> ring;
+  int e = 0, es = -1;
+  stage_token<1>(lds, 0, a.hq_slot + (size_t)slot * a.F, a.hd_slot + (size_t)slot * NB,
+                 a.hs_slot + (size_t)slot * NB, NB, lane, kWave, BITS == 2 ? 2 : 0, [&] {
+    const int n_active = *as_const(a.n_active);
+    e = as_const(a.active)[slot];
+    es = slot < n_active ? storage_of(a.slot_of, a.n_store, e, a.err) : -1;
+    // issued on every path (expert 0 stands in when there is none), so the
+    // memory-counter waits after it count the whole ring
+    const int esafe = es < 0 ? 0 : es;
+    ring.template start<PF>(
+        reinterpret_cast<const char*>(a.dn_q + ((size_t)esafe * (a.D / 64) + grp) * (size_t)NU * kWave),
+        16u * (uint32_t)lane, NU);
+  });
+  if (es < 0) return;                    // uniform: one wavefront
+  clear_tail_records<1>(NB, blocks_per_ring(PF, BITS), lane, kWave);
+  const size_t row = 64 * (size_t)grp + lane;
+  const float rs = a.dn_s[(size_t)es * a.D + row];
+  const int pair = as_const(a.lists)[(size_t)e * a.T];
+  int32_t* trow[1] = {(TRACE && a.tr_pd) ? a.tr_pd + ((size_t)pair * a.D + row) * NB : nullptr};
+  __syncthreads();
+  float acc[1] = {0.0f};
+  stream_pass<1, PF, BITS, TRACE>(1, ring, acc, trow);
+  a.o[(size_t)pair * a.D + row] = acc[0] * rs;
+}
+
 template <int MAXT, int PF, int BITS, bool TRACE>
 __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) down_kernel(DnArgs a) {
+  if constexpr (MAXT == 1) {
+    if (a.T == 1 && a.hq_slot) {
+      down_one_token<PF, BITS, TRACE>(a);
+      return;
+    }
+  }
   constexpr int W = gemv_waves(MAXT);
   const int slot = blockIdx.y;
   const int n_active = *as_const(a.n_active);   // both loads in flight together;
@@ -956,6 +1011,9 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   g.hq = ws.hq;
   g.hd = ws.hd;
   g.hsum8 = ws.hsum8;
+  g.hq_slot = ws.hq_slot;
+  g.hd_slot = ws.hd_slot;
+  g.hs_slot = ws.hs_slot;
   g.slot_of = t.slot_of;
   g.n_store = t.slot_of ? t.n_slots : E + S;
   g.err = ws.err;
@@ -970,6 +1028,9 @@ hipError_t launch_moe_forward(const ForwardArgs& f, hipStream_t s) {
   d.hq = ws.hq;
   d.hd = ws.hd;
   d.hsum8 = ws.hsum8;
+  d.hq_slot = ws.hq_slot;
+  d.hd_slot = ws.hd_slot;
+  d.hs_slot = ws.hs_slot;
   d.counts = ws.counts;
   d.lists = ws.lists;
   d.n_active = ws.n_active;

@@ -143,6 +143,11 @@ struct MoeWorkspace {
   float* hd;         // [P][F/32]
   int32_t* hsum8;    // [P][F/32]   -8 * sum of each Q8 block of h
   float* o;          // [P][D]
+  // one-token passes only (else null): Q8(h) again, in active-slot order, so
+  // the down kernel can stage it without looking up the slot's pair
+  int8_t* hq_slot;   // [A][F]
+  float* hd_slot;    // [A][F/32]
+  int32_t* hs_slot;  // [A][F/32]
   // grouped (matrix-core) path only
   uint16_t* xh;      // [T][D/32][32] f16 codes of xq in MFMA operand order
   uint16_t* h16;     // [P][F/32][32] f16 codes of Q8(h) in MFMA operand order
