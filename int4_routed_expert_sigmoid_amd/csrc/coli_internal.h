@@ -101,15 +101,61 @@ __device__ __forceinline__ void rmsnorm_q8_row(const float* __restrict__ hrow, i
   }
   __syncthreads();
   const float r = *rsh;
-  for (int64_t c = threadIdx.x; c < D / 4; c += 256) {   // D/4 is a multiple of 8
-    const float4 v = hr[c];
-    const float4 xh = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
-    float dv;
-    int sum;
-    q[c] = q8_quad(xh, &dv, &sum);
-    if ((c & 7) == 0) {
-      d[c >> 3] = dv;
-      if (xsum8) xsum8[c >> 3] = -8 * sum;
+  // Q8_0 of x = h * r with q8_quad's arithmetic, taken in phases over up to
+  // kNormQuads groups of 4 values per thread with branch-free codes (a zero
+  // scale divides by 1 and its code is selected away), so that the lane
+  // exchanges and the divisions of independent groups overlap.  A group past
+  // the row (whole 8-lane blocks: D/4 and 256 are multiples of 8) computes on
+  // an in-bounds copy and stores nothing.
+  constexpr int kNormQuads = 8;
+  const int64_t n4 = D / 4;
+  for (int64_t c0 = 0; c0 < n4; c0 += 256 * kNormQuads) {
+    int64_t c[kNormQuads];
+    float4 x[kNormQuads];
+    float amax[kNormQuads], dq[kNormQuads];
+    int qv[kNormQuads][4], sum[kNormQuads];
+#pragma unroll
+    for (int u = 0; u < kNormQuads; ++u) {
+      c[u] = c0 + 256 * u + threadIdx.x;
+      const float4 v = hr[c[u] < n4 ? c[u] : (threadIdx.x & 7)];
+      x[u] = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+      amax[u] = fmaxf(fmaxf(fabsf(x[u].x), fabsf(x[u].y)), fmaxf(fabsf(x[u].z), fabsf(x[u].w)));
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+#pragma unroll
+      for (int u = 0; u < kNormQuads; ++u) amax[u] = fmaxf(amax[u], __shfl_xor(amax[u], off, 8));
+    }
+#pragma unroll
+    for (int u = 0; u < kNormQuads; ++u) {
+      dq[u] = amax[u] / 127.0f;
+      const bool zero = dq[u] == 0.0f;
+      const float dd = zero ? 1.0f : dq[u];
+      const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float qf = __builtin_rintf(xs[i] / dd);
+        qf = qf > 127.0f ? 127.0f : qf;
+        qf = qf < -127.0f ? -127.0f : qf;
+        qv[u][i] = zero ? 0 : (int)qf;
+      }
+      sum[u] = qv[u][0] + qv[u][1] + qv[u][2] + qv[u][3];
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+#pragma unroll
+      for (int u = 0; u < kNormQuads; ++u) sum[u] += __shfl_xor(sum[u], off, 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kNormQuads; ++u) {
+      if (c[u] < n4) {
+        q[c[u]] = (qv[u][0] & 0xFF) | ((qv[u][1] & 0xFF) << 8) | ((qv[u][2] & 0xFF) << 16) |
+                  ((int)((unsigned)qv[u][3] << 24));
+        if ((c[u] & 7) == 0) {
+          d[c[u] >> 3] = dq[u];
+          if (xsum8) xsum8[c[u] >> 3] = -8 * sum[u];
+        }
+      }
     }
   }
 }
