@@ -564,6 +564,33 @@ __device__ __forceinline__ void stream_pass(int nt, Ring<PF>& ring, float* acc,
 // and stores nothing.
 constexpr int gemv_waves(int maxt) { return maxt >= 4 ? 4 : 1; }
 
+// Maximum / sum over each 32-lane half of the wavefront, returned in every
+// lane of the half: rotations within the 16-lane rows (DPP row_ror 1, 2, 4,
+// 8), then the half's two rows combined through v_permlane16_swap (its two
+// results hold, in every lane, the lane's own row and the other row of its
+// pair).  Both are exact in any order.
+constexpr int kDppRowRor = 0x120;
+template <int N>
+__device__ __forceinline__ float ror_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowRor + N,
+                                                             0xF, 0xF, false)));
+}
+template <int N>
+__device__ __forceinline__ int ror_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, kDppRowRor + N, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float half_max(float x) {
+  x = ror_max<8>(ror_max<4>(ror_max<2>(ror_max<1>(x))));
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ int half_sum(int x) {
+  x = ror_add<8>(ror_add<4>(ror_add<2>(ror_add<1>(x))));
+  const auto s = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)s[0] + (int)s[1];
+}
+
 // gate/up of a one-token pass (one wavefront per row group).  The token is
 // token 0 whatever the routing, so its blocks are staged first, with no
 // dependent load before them; the expert's weight ring starts as soon as the
@@ -602,16 +629,15 @@ __device__ __forceinline__ void gate_up_one_token(const GuArgs& a) {
   float acc[1] = {0.0f};
   stream_pass<1, PF, BITS, TRACE>(1, ring, acc, trow);
   const float v = acc[0] * rs;              // g (lanes 0-31) or u (lanes 32-63)
-  const float up = __shfl_down(v, 32);      // lanes 0-31 receive their up row
+  // lanes 0-31 receive their up row (lane + 32)
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                   false);
+  const float up = __uint_as_float(sw[1]);
   const float h = silu_f32(v) * up;
-  float amax = fabsf(h);
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+  const float amax = half_max(fabsf(h));
   const float d = amax / 127.0f;
   const int q = q8_code(h, d);
-  int qs = q;
-#pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) qs += __shfl_xor(qs, off, 32);
+  const int qs = half_sum(q);
   if (lane < 32) {
     const size_t p = (size_t)pair;
     const size_t r = 32 * (size_t)grp + lane;
