@@ -24,6 +24,13 @@
 // Nibbles are stored offset-binary (q + 8), so a dot with them is
 // sum (q+8) x = P + 8 sum x; the -8 sum x term is precomputed per block.
 //
+// One-token passes (decode) take their own prologue in both kernels: the
+// token records (token 0 for gate/up; for down, the slot's Q8(h), which
+// gate/up also stores in active-slot order) are loaded at kernel entry with
+// no dependent load before them, and the whole weight ring is issued as soon
+// as the active expert is known; the gate/up epilogue exchanges lanes with
+// permlane swaps and DPP instead of LDS shuffles.
+//
 // int8 tables (the int8 speculative head: discuss.pytorch.kr colibri summary,
 // "colibri의 주요 기능", MTP bullet; jeff.news, MTP section) run the same
 // kernels with two 1 KB wavefront loads per 32-column block: the codes are
