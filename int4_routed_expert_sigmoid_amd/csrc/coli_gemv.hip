@@ -739,16 +739,15 @@ __global__ void __launch_bounds__(64 * gemv_waves(MAXT)) gate_up_kernel(GuArgs a
     for (int j = 0; j < MAXT; ++j) {
       if (j < nt) {
         const float v = acc[j] * rs;              // g (lanes 0-31) or u (lanes 32-63)
-        const float up = __shfl_down(v, 32);      // lanes 0-31 receive their up row
+        // lanes 0-31 receive their up row (lane + 32)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                         false, false);
+        const float up = __uint_as_float(sw[1]);
         const float h = silu_f32(v) * up;
-        float amax = fabsf(h);
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+        const float amax = half_max(fabsf(h));
         const float d = amax / 127.0f;
         const int q = q8_code(h, d);
-        int qs = q;
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) qs += __shfl_xor(qs, off, 32);
+        const int qs = half_sum(q);
         const size_t p = (size_t)pair[j];
         if (live && lane < 32) {
           const size_t r = 32 * (size_t)grp + lane;
