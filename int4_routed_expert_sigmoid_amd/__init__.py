@@ -25,8 +25,10 @@ COLI_E_HIP = -5
 COLI_E_INDEX = -6
 COLI_E_TIER = -7
 COLI_PATH_AUTO, COLI_PATH_GEMV, COLI_PATH_GROUPED = 0, 1, 2
+COLI_GROUPED_MIN_TOKENS = 14
 COLI_MAX_EXPERTS = 256
 COLI_MAX_TOPK = 64
+COLI_MAX_DIM = 32768
 
 EXPORTED = [
     "coli_table_bytes", "coli_table_set_expert", "coli_quant_act_q8", "coli_quant_weight_q4",

@@ -65,6 +65,11 @@ def test_table_bytes():
     assert [s.value for s in sizes] == [257 * 6144 * 1024, 257 * 2 * 2048 * 4,
                                        257 * 6144 * 512, 257 * 6144 * 4]
     assert L.coli_table_bytes(16, 1, 256, 96, 2, None, None, None, None) == 0
+    # the limits of coli.h are accepted, one step past them is not
+    assert L.coli_table_bytes(coli.COLI_MAX_EXPERTS, 1, coli.COLI_MAX_DIM, 64, 4, None, None, None, None) > 0
+    assert L.coli_table_bytes(4, 1, 64, coli.COLI_MAX_DIM, 4, None, None, None, None) > 0
+    assert L.coli_table_bytes(4, 1, coli.COLI_MAX_DIM + 64, 64, 4, None, None, None, None) == 0
+    assert L.coli_table_bytes(4, 1, 64, coli.COLI_MAX_DIM + 32, 4, None, None, None, None) == 0
 
 
 def _table(E=16, S=1, D=256, F=128, ptr=FAKE, bits=4, slots=0, slot_of=None):
@@ -253,3 +258,16 @@ def test_path_choice_host():
     assert f(*args(t, -1)) == coli.COLI_E_INVAL
     t8 = _table(256, 1, 6144, 2048, bits=8)
     assert f(*args(t8, coli.COLI_PATH_GROUPED)) == coli.COLI_E_SHAPE
+
+
+def test_constants_match_header():
+    """The binding's status codes, path ids and limits are the header's."""
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "include", "coli.h")).read()
+    found = {m.group(1): int(m.group(2))
+             for m in re.finditer(r"\b(COLI_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+    found.update({m.group(1): int(m.group(2))
+                  for m in re.finditer(r"#define\s+(COLI_[A-Z_]+)\s+(\d+)", text)})
+    assert len(found) >= 13, sorted(found)
+    for name, value in found.items():
+        assert getattr(coli, name) == value, name

@@ -3,9 +3,14 @@
 Shapes beyond the workloads: every expert selected (k = E) with no shared
 expert, top-1, contraction lengths that leave partial weight-ring passes and
 token-record tails (d_model 320 = 10 blocks, d_ff 96 = 3 blocks, d_ff 160),
-and no shared expert at the tiny shape.  Each runs 1, 2, 5, 16 and 33
-tokens through both expert paths (GEMV, grouped matrix cores), through the
-fused layer entry point, and through the pre-norm block entry point.
+and no shared expert at the tiny shape; and the library's limits
+(COLI_MAX_DIM, COLI_MAX_EXPERTS, COLI_MAX_TOPK in coli.h): d_model 32768,
+d_ff 32768 (the GEMV's token records then leave room for one token per pass,
+so every batch runs one-token passes), and 256 routed experts with top-64 (16
+tokens then fill the fused front's 1024 routing entries exactly).  Each runs
+1, 2, 5, 16 and 33 tokens through both expert paths (GEMV, grouped matrix
+cores), through the fused layer entry point, and through the pre-norm block
+entry point.
 """
 import numpy as np
 import pytest
@@ -31,6 +36,12 @@ SHAPES = {
                                            family=4, tag=12),
     "no shared": synth.Workload("shape d256 f128 e16+0 top2", 256, 128, 16, 0, 2, 1, family=5,
                                 tag=13),
+    "d_model at the limit": synth.Workload("limit d32768 f64 e4+1 top2", 32768, 64, 4, 1, 2, 1,
+                                           family=6, tag=14),
+    "d_ff at the limit": synth.Workload("limit d64 f32768 e4+1 top2", 64, 32768, 4, 1, 2, 1,
+                                        family=7, tag=15),
+    "experts and top-k at the limit": synth.Workload("limit d128 f64 e256+1 top64", 128, 64, 256,
+                                                     1, 64, 1, family=8, tag=16),
 }
 TOKENS = [1, 2, 5, 16, 33]
 
