@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 # HBM bytes per launch of the decode gate/up kernel, from rocprofv3 FETCH_SIZE (x2.0) and
 # WRITE_SIZE (x1.0) runs, each scale taken from a copy of known size
 # (profiles/decode_gate_up_hbm_traffic.md); valid for the kernel as measured there.
-GATE_UP_TRAFFIC_BYTES = 113_807_296
+GATE_UP_TRAFFIC_BYTES = 113_782_374
 INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of MI355X
 METRIC = "MoE-layer decode tok/s + achieved HBM GB/s (int4 experts); prefill int8 TOPS"
 
