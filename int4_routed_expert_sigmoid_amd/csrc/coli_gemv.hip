@@ -933,15 +933,23 @@ hipError_t record(void* ev, hipStream_t s) {
 }
 
 // Weight loads (1 KB per wavefront) in flight per wavefront, by tokens per
-// pass and 16-byte chunks per block.  One-token gate/up passes keep 12: at
-// d_model 6144 (576 wavefronts on the chip) a decode step measured 36.0 us
-// against 37.5 us with 16, 38.4 with 24, 36.7 with 8 and 40.0 with 6 (depths
-// that divide the 192-block row); the one-token down pass is fastest at 8 (4
-// and 16 measured slower).
+// pass and 16-byte chunks per block, as measured at d_model 6144, d_ff 2048
+// with 257 experts.  One-token gate/up passes keep 12 (576 wavefronts on the
+// chip): a decode step took 36.0 us against 37.5 with 16, 38.4 with 24, 36.7
+// with 8 and 40.0 with 6 (depths that divide the 192-block row); one-token
+// down passes are fastest at 8 (4 and 16 slower).  Four-token passes run
+// four wavefronts per workgroup on ~1,800 row groups, and the fewer loads
+// each keeps in flight the better down to gate/up 4, down 2: 99.6 us per
+// pass against 108.6 with 16 and 8 (gate/up 2 with down 2: 110.4); int2
+// tables gain too (86.6 -> 76.2 us), int8 tables (two loads per block) lose
+// (180.1 -> 184.6 us) and keep 16 and 8.  Eight-token passes measured slower
+// with 4 and 2 (208 against 201 us).
 constexpr int pf_gate_up(int maxt, int bits) {
-  return maxt <= 0 || bits <= 0 ? 0 : maxt == 1 ? 12 : 16;
+  return maxt <= 0 || bits <= 0 ? 0 : maxt == 1 ? 12 : maxt == 4 && bits != 8 ? 4 : 16;
 }
-constexpr int pf_down(int maxt, int bits) { return maxt > 0 && bits > 0 ? 8 : 0; }
+constexpr int pf_down(int maxt, int bits) {
+  return maxt <= 0 || bits <= 0 ? 0 : maxt == 4 && bits != 8 ? 2 : 8;
+}
 constexpr size_t kLdsLimit = 65536;
 
 // Stage events of the GEMV kernels, attached to the kernels' own dispatches
