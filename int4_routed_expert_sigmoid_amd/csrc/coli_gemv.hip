@@ -942,13 +942,22 @@ hipError_t record(void* ev, hipStream_t s) {
 // each keeps in flight the better down to gate/up 4, down 2: 99.6 us per
 // pass against 108.6 with 16 and 8 (gate/up 2 with down 2: 110.4); int2
 // tables gain too (86.6 -> 76.2 us), int8 tables (two loads per block) lose
-// (180.1 -> 184.6 us) and keep 16 and 8.  Eight-token passes measured slower
-// with 4 and 2 (208 against 201 us).
+// (180.1 -> 184.6 us) and keep 16 and 8.  With int4 tables, two-token
+// passes are fastest at 16 and 4 (65.1 us against 66.8 with 16 and 8; 8 and
+// 4: 68.1, 12 and 8: 70.5) and eight-token passes at 8 and 4 (199.6 against
+// 201.5 us; 4 and 2: 208).
 constexpr int pf_gate_up(int maxt, int bits) {
-  return maxt <= 0 || bits <= 0 ? 0 : maxt == 1 ? 12 : maxt == 4 && bits != 8 ? 4 : 16;
+  if (maxt <= 0 || bits <= 0) return 0;
+  if (maxt == 1) return 12;
+  if (maxt == 4 && bits != 8) return 4;
+  if (maxt == 8 && bits == 4) return 8;
+  return 16;
 }
 constexpr int pf_down(int maxt, int bits) {
-  return maxt <= 0 || bits <= 0 ? 0 : maxt == 4 && bits != 8 ? 2 : 8;
+  if (maxt <= 0 || bits <= 0) return 0;
+  if (maxt == 4 && bits != 8) return 2;
+  if ((maxt == 2 || maxt == 8) && bits == 4) return 4;
+  return 8;
 }
 constexpr size_t kLdsLimit = 65536;
 
