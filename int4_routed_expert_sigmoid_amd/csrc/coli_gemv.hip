@@ -936,8 +936,9 @@ hipError_t record(void* ev, hipStream_t s) {
 // pass and 16-byte chunks per block, as measured at d_model 6144, d_ff 2048
 // with 257 experts.  One-token gate/up passes keep 12 (576 wavefronts on the
 // chip): a decode step took 36.0 us against 37.5 with 16, 38.4 with 24, 36.7
-// with 8 and 40.0 with 6 (depths that divide the 192-block row); one-token
-// down passes are fastest at 8 (4 and 16 slower).  Four-token passes run
+// with 8 and 40.0 with 6 (depths that divide the 192-block row; 10 ties with
+// 12, 14 ran 36.8); one-token down passes are fastest at 8 (4 and 16
+// slower).  Four-token passes run
 // four wavefronts per workgroup on ~1,800 row groups, and the fewer loads
 // each keeps in flight the better down to gate/up 4, down 2: 99.6 us per
 // pass against 108.6 with 16 and 8 (gate/up 2 with down 2: 110.4); int2
