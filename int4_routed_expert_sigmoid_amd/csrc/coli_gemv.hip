@@ -938,7 +938,9 @@ hipError_t record(void* ev, hipStream_t s) {
 // chip): a decode step took 36.0 us against 37.5 with 16, 38.4 with 24, 36.7
 // with 8 and 40.0 with 6 (depths that divide the 192-block row; 10 ties with
 // 12, 14 ran 36.8); one-token down passes are fastest at 8 (4 and 16
-// slower).  Four-token passes run
+// slower).  int8 tables (two loads per block) keep 8 in one-token gate/up
+// passes: 60.9 us per step against 62.0 with 12, 63.6 with 16, 68.0 with 6
+// and 82.0 with 4.  Four-token passes run
 // four wavefronts per workgroup on ~1,800 row groups, and the fewer loads
 // each keeps in flight the better down to gate/up 4, down 2: 99.6 us per
 // pass against 108.6 with 16 and 8 (gate/up 2 with down 2: 110.4); int2
@@ -949,7 +951,7 @@ hipError_t record(void* ev, hipStream_t s) {
 // 201.5 us; 4 and 2: 208).
 constexpr int pf_gate_up(int maxt, int bits) {
   if (maxt <= 0 || bits <= 0) return 0;
-  if (maxt == 1) return 12;
+  if (maxt == 1) return bits == 8 ? 8 : 12;
   if (maxt == 4 && bits != 8) return 4;
   if (maxt == 8 && bits == 4) return 8;
   return 16;
