@@ -940,7 +940,8 @@ hipError_t record(void* ev, hipStream_t s) {
 // 12, 14 ran 36.8); one-token down passes are fastest at 8 (4 and 16
 // slower).  int8 tables (two loads per block) keep 8 in one-token gate/up
 // passes: 60.9 us per step against 62.0 with 12, 63.6 with 16, 68.0 with 6
-// and 82.0 with 4.  Four-token passes run
+// and 82.0 with 4; int2 tables are fastest at 12 too (28.9 us per step
+// against 29.1 with 8 or 16).  Four-token passes run
 // four wavefronts per workgroup on ~1,800 row groups, and the fewer loads
 // each keeps in flight the better down to gate/up 4, down 2: 99.6 us per
 // pass against 108.6 with 16 and 8 (gate/up 2 with down 2: 110.4); int2
