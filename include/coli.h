@@ -231,7 +231,14 @@ int coli_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S
                   int32_t* err, void* stream);
 
 /* ------------------------------------------------------------------------
- * The MoE FFN forward over a device-resident table.
+ * The MoE FFN forward over a device-resident table: the expert matmuls as
+ * integer dots of int8 (Q8_0) activations with the packed weights
+ * (discuss.pytorch.kr colibri summary, "colibri의 주요 기능", integer-dot
+ * bullet; jeff.news, attention-and-kernels section: DeepSeek-V3-style MoE
+ * with a shared expert; aitrends.kr "GLM-5.2-colibri-int4", "기술적 특징":
+ * U8-packed int4 with per-row F32 scales), with the tokens grouped per
+ * expert so that each selected expert's rows are read once per pass
+ * (alphamatch.ai, "기술적 우수성").
  *   xq [T][D] int8, xd [T][D/32] f32: the Q8_0 tokens.
  *   idx [T][k] int32, w [T][k] f32: the routing (coli_route_topk).
  *   y [T][D] f32: y = moe (accumulate = 0) or y + moe (accumulate = 1), with
@@ -241,8 +248,11 @@ int coli_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S
  * o = W_down hq.  The workspace (caller-owned, device memory) must hold
  * coli_moe_workspace_bytes(table, T, k) bytes; its contents need no
  * initialisation and are clobbered.  Calls that share a workspace must not
- * overlap.  An invalid expert index does not fault: its slot contributes
- * nothing and coli_moe_status() reports COLI_E_INDEX. */
+ * overlap.  Routings from the caller may hold invalid entries: an entry
+ * outside [0, E), or one equal to an earlier slot of the same token, is
+ * dropped (listed for no expert; its slot contributes nothing to y, and the
+ * remaining slots keep their order), coli_moe_status() reports COLI_E_INDEX,
+ * and nothing faults.  coli_route_topk never produces such entries. */
 size_t coli_moe_workspace_bytes(const coli_expert_table* table, int64_t T, int32_t k);
 
 int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const float* xd,
@@ -334,7 +344,10 @@ int coli_moe_forward_profiled(const coli_expert_table* table, const int8_t* xq, 
                               const coli_moe_events* events, void* stream);
 
 /* ------------------------------------------------------------------------
- * The whole layer in one call, from f32 activations and router logits:
+ * The whole layer in one call, from f32 activations and router logits (the
+ * routed MoE FFN of jeff.news, attention-and-kernels section: sigmoid router
+ * with a selection bias, shared + routed experts; the integer-dot expert
+ * matmuls of discuss.pytorch.kr, "colibri의 주요 기능"):
  * Q8_0 of x (coli_quant_act_q8), routing (coli_route_topk, bias may be NULL),
  * then coli_moe_forward, with the same numerics as those calls.  For small
  * batches (T <= 64 and T*k <= 1024: decode and speculative verify) the

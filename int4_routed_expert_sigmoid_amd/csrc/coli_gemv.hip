@@ -883,8 +883,9 @@ __device__ __forceinline__ float4 fma4(float w, float4 a, float4 acc) {
 
 // y[t][r] = o_shared + sum_j w_j o_j, as y = fmaf(w_j, o_j, y) in slot order,
 // four rows per thread.  KU > 0: k == KU, unrolled, every slot's load issued
-// before the ordered fmaf chain; KU == 0: any k.  Slots with an index outside
-// [0, E) are skipped (their o rows were never written).
+// before the ordered fmaf chain; KU == 0: any k.  Slots the dispatch drops
+// are skipped (their o rows were never written): an index outside [0, E), or
+// one equal to an earlier slot's of the same token.
 template <int KU>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ idx,
@@ -906,15 +907,22 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
       wj[j] = w[t * KU + j];         // so no load waits for the index check
       v[j] = ot[j * D4];
     }
+    int ev[KU];
+#pragma unroll
+    for (int j = 0; j < KU; ++j) ev[j] = idx[t * KU + j];
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const int e = idx[t * KU + j];
-      if (e >= 0 && e < E) acc = fma4(wj[j], v[j], acc);
+      bool keep = ev[j] >= 0 && ev[j] < E;
+#pragma unroll
+      for (int i = 0; i < j; ++i) keep = keep && ev[i] != ev[j];
+      if (keep) acc = fma4(wj[j], v[j], acc);
     }
   } else {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
-      if (e < 0 || e >= E) continue;
+      bool keep = e >= 0 && e < E;
+      for (int i = 0; i < j && keep; ++i) keep = idx[t * k + i] != e;
+      if (!keep) continue;
       acc = fma4(w[t * k + j], ot[j * D4], acc);
     }
   }

@@ -133,114 +133,93 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
   }
 }
 
-// Batch-union dispatch in one pass.  Workgroup c owns tokens
-// [64c, 64c + 64) and their k entries each.  An entry of expert e goes to
-// list position (entries of e in all earlier tokens) + (earlier entries of e
-// among its own), the first from an LDS histogram of every preceding entry,
-// the second from a scan of its own entries: each list is in entry order,
-// i.e. ascending token order, with no communication between workgroups and
-// no scratch memory.  Out-of-range entries are left out.  The last
-// workgroup also writes the counts, the active list and the index check (an
-// entry out of range, or equal to an earlier entry of its token).
-constexpr int kDispatchTokens = 64;
-constexpr int kDispatchLoads = 16;   // global loads in flight per thread
+// Batch-union dispatch, expert-major.  Workgroup e < E builds the list of
+// expert e: it sweeps the tokens 256 at a time, one token per thread; a token
+// is listed when one of its slots holds e, at the first such slot (a later
+// slot with the same expert is a repeat and is dropped); list positions are
+// prefix counts of a workgroup-wide ballot, so each list is in ascending
+// token order with no atomics and no scratch memory.  Workgroup E writes the
+// shared expert's list (slot k of every token), checks every entry (out of
+// range, or equal to an earlier entry of its token), marks the experts some
+// kept entry selects, and writes the active list, n_active and the flag.
+// Every workgroup reads the whole index array once, so the cost is linear in
+// T (E + 1 reads of T * k entries, served by L2).
+constexpr int kDispatchThreads = 256;
 
-// hist[e] += entries of expert e among idx[lo, hi), for valid e.
-__device__ __forceinline__ void histogram(const int32_t* __restrict__ idx, int64_t lo, int64_t hi,
-                                          int E, int* hist) {
-  for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += 256 * kDispatchLoads) {
-    int v[kDispatchLoads];
+// Exclusive prefix of `flag` over the workgroup's 256 threads; returns it and
+// sets *total.
+__device__ __forceinline__ int block_prefix(bool flag, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  if (lane == 0) wsum[wave] = __popcll(m);
+  __syncthreads();
+  int base = 0, tot = 0;
 #pragma unroll
-    for (int u = 0; u < kDispatchLoads; ++u) {
-      const int64_t i = i0 + (int64_t)u * 256;
-      v[u] = i < hi ? idx[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kDispatchLoads; ++u)
-      if (v[u] >= 0 && v[u] < E) atomicAdd(&hist[v[u]], 1);
+  for (int w = 0; w < 4; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
   }
+  __syncthreads();   // wsum is reused by the next sweep
+  *total = tot;
+  return base + __popcll(m & lt);
 }
 
-__global__ void __launch_bounds__(256) dispatch_sort_kernel(const int32_t* __restrict__ idx,
-                                                            int64_t T, int k, int E, int S,
-                                                            int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ lists,
-                                                            int32_t* __restrict__ n_active,
-                                                            int32_t* __restrict__ active,
-                                                            int32_t* __restrict__ err) {
-  __shared__ int hist[COLI_MAX_EXPERTS + 1];
-  __shared__ int ent[kDispatchTokens * COLI_MAX_TOPK];
+__global__ void __launch_bounds__(kDispatchThreads) dispatch_expert_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int k, int E, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ lists, int32_t* __restrict__ n_active, int32_t* __restrict__ active,
+    int32_t* __restrict__ err) {
+  __shared__ int wsum[4];
+  __shared__ int present[COLI_MAX_EXPERTS + 1];
   __shared__ int bad_any;
   const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * kDispatchTokens;
-  const int nt = (int)(T - t0 < kDispatchTokens ? T - t0 : kDispatchTokens);
-  const int64_t g0 = t0 * k;   // first entry of this workgroup
-  const int m = nt * k;
-  for (int e = tid; e < E + S; e += 256) hist[e] = 0;
-  if (tid == 0) bad_any = 0;
-  for (int i = tid; i < m; i += 256) ent[i] = idx[g0 + i];
-  __syncthreads();
-  histogram(idx, 0, g0, E, hist);
-  __syncthreads();
-  for (int i = tid; i < m; i += 256) {
-    const int e = ent[i];
-    if (e < 0 || e >= E) continue;
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += ent[j] == e;
-    const int64_t pos = hist[e] + rank;
-    const int64_t g = g0 + i;
-    if (pos < T) lists[(int64_t)e * T + pos] = (int32_t)((g / k) * (k + S) + g % k);
-  }
-  if (S)   // the shared expert serves every token, in slot k
-    for (int i = tid; i < nt; i += 256)
-      lists[(int64_t)E * T + t0 + i] = (int32_t)((t0 + i) * (k + S) + k);
-  if (blockIdx.x != gridDim.x - 1) return;
-  // the last workgroup: its own entries complete the totals; then the index
-  // check over whole-token chunks of every entry staged through LDS
-  __syncthreads();
-  for (int i = tid; i < m; i += 256) {
-    const int e = ent[i];
-    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
-  }
-  int bad = 0;
-  const int64_t n = T * k, chunk = (kDispatchTokens * COLI_MAX_TOPK / k) * k;
-  for (int64_t c0 = 0; c0 < n; c0 += chunk) {
-    const int cm = (int)(n - c0 < chunk ? n - c0 : chunk);
-    __syncthreads();   // the previous chunk's readers are done
-    for (int i0 = tid; i0 < cm; i0 += 256 * kDispatchLoads) {
-      int v[kDispatchLoads];
-#pragma unroll
-      for (int u = 0; u < kDispatchLoads; ++u) {
-        const int i = i0 + u * 256;
-        v[u] = i < cm ? idx[c0 + i] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < kDispatchLoads; ++u)
-        if (i0 + u * 256 < cm) ent[i0 + u * 256] = v[u];
+  const int e = (int)blockIdx.x;
+  if (e < E) {
+    int count = 0;
+    for (int64_t t0 = 0; t0 < T; t0 += kDispatchThreads) {
+      const int64_t t = t0 + tid;
+      int slot = -1;
+      if (t < T)
+        for (int j = k - 1; j >= 0; --j)   // the first slot holding e wins
+          if (idx[t * k + j] == e) slot = j;
+      int total;
+      const int pos = block_prefix(slot >= 0, wsum, &total);
+      if (slot >= 0) lists[(int64_t)e * T + count + pos] = (int32_t)(t * (k + S) + slot);
+      count += total;
     }
-    __syncthreads();
-    for (int t = tid; t < cm / k; t += 256) {
-      const int* et = ent + t * k;
-      for (int j = 0; j < k; ++j) {
-        const int e = et[j];
-        if (e < 0 || e >= E) bad = 1;
-        for (int i = 0; i < j; ++i) bad |= et[i] == e;
-      }
+    if (tid == 0) counts[e] = count;
+    return;
+  }
+  // workgroup E: shared list, index check, active list
+  for (int i = tid; i < E + S; i += kDispatchThreads) present[i] = 0;
+  if (tid == 0) bad_any = 0;
+  __syncthreads();
+  int bad = 0;
+  for (int64_t t = tid; t < T; t += kDispatchThreads) {
+    if (S) lists[(int64_t)E * T + t] = (int32_t)(t * (k + S) + k);
+    for (int j = 0; j < k; ++j) {
+      const int v = idx[t * k + j];
+      bool ok = v >= 0 && v < E;
+      for (int i = 0; i < j && ok; ++i) ok = idx[t * k + i] != v;
+      if (ok) present[v] = 1;
+      else bad = 1;
     }
   }
   if (bad) atomicOr(&bad_any, 1);
+  if (S && tid == 0) {
+    counts[E] = (int32_t)T;
+    present[E] = T > 0;
+  }
   __syncthreads();
-  for (int e = tid; e < E + S; e += 256)
-    counts[e] = e == E ? (int32_t)T : (hist[e] < T ? hist[e] : (int32_t)T);
-  if (tid < kWave) {
+  if (tid < 64) {
     const int lane = tid;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     int base = 0;
-    for (int e0 = 0; e0 < E + S; e0 += kWave) {
-      const int e = e0 + lane;
-      const bool on = e < E + S && (e == E ? T > 0 : hist[e] > 0);
+    for (int e0 = 0; e0 < E + S; e0 += 64) {
+      const int x = e0 + lane;
+      const bool on = x < E + S && present[x];
       const uint64_t msk = __ballot(on);
-      if (on) active[base + __popcll(msk & lt)] = e;
+      if (on) active[base + __popcll(msk & lt)] = x;
       base += __popcll(msk);
     }
     if (lane == 0) {
@@ -453,9 +432,8 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, int32_t* counts,
                            int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
                            const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s) {
-  const int64_t groups = T > 0 ? (T + kDispatchTokens - 1) / kDispatchTokens : 1;
-  hipLaunchKernelGGL(dispatch_sort_kernel, dim3((unsigned)groups), dim3(256), 0, s, idx, T, k, E,
-                     S, counts, lists, n_active, active, err);
+  hipLaunchKernelGGL(dispatch_expert_kernel, dim3((unsigned)(E + 1)), dim3(kDispatchThreads), 0, s,
+                     idx, T, k, E, S, counts, lists, n_active, active, err);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess || !xq || T == 0) return rc;
   const int64_t nb = T * (D / 32);

@@ -46,10 +46,11 @@ _SIG = {
     "orc_matvec": ([_P, ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P, _P], None),
     "orc_expert": ([_P] * 6 + [ctypes.c_int, _I64, _I64] + [_P] * 12, None),
     "orc_moe_layer": ([_P, ctypes.c_int, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P,
-                       ctypes.c_int, _P], ctypes.c_int),
+                       _P, ctypes.c_int, _P], ctypes.c_int),
+    "orc_keep_entries": ([_P, _I64, _I32, _I32, _P], _I64),
     "orc_rmsnorm": ([_P, _I64, _I64, _F, _P, _P], None),
     "orc_router_logits": ([_P, _P, _I64, _I64, _I32, _P], None),
-    "orc_dispatch": ([_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P], ctypes.c_int),
+    "orc_dispatch": ([_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
     "orc_tier_init": ([_I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "orc_tier_plan": ([_I32, _I32, _I32, _P, _I64, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _P,
                        _P, _P, _P], ctypes.c_int),
@@ -249,15 +250,27 @@ class Oracle:
         self.L.orc_route(_ptr(logits), _ptr(bias), T, E, k, routed_scale, _ptr(idx), _ptr(w))
         return idx, w
 
-    def dispatch(self, idx, E, S):
+    def keep_entries(self, idx, E):
+        """keep [T][k] uint8: 1 for an entry the forward serves (in [0, E) and not
+        a repeat of an earlier slot of its token); returns (keep, dropped)."""
         idx = _c(idx, np.int32)
         T, k = idx.shape
+        keep = np.empty((T, k), dtype=np.uint8)
+        n = self.L.orc_keep_entries(_ptr(idx), T, k, E, _ptr(keep))
+        return keep, int(n)
+
+    def dispatch(self, idx, E, S, keep=None):
+        idx = _c(idx, np.int32)
+        T, k = idx.shape
+        if keep is not None:
+            keep = _c(keep, np.uint8)
+            assert keep.shape == idx.shape
         counts = np.zeros(E + S, dtype=np.int32)
         lists = np.full((E + S, T), -1, dtype=np.int32)
         n_active = np.zeros(1, dtype=np.int32)
         active = np.full(E + S, -1, dtype=np.int32)
-        rc = self.L.orc_dispatch(_ptr(idx), T, k, E, S, _ptr(counts), _ptr(lists), _ptr(n_active),
-                                _ptr(active))
+        rc = self.L.orc_dispatch(_ptr(idx), T, k, E, S, _ptr(keep), _ptr(counts), _ptr(lists),
+                                _ptr(n_active), _ptr(active))
         if rc != 0:
             raise ValueError("orc_dispatch rejected the index array")
         return counts, lists, int(n_active[0]), active[: int(n_active[0])]
@@ -310,8 +323,10 @@ class Oracle:
                          _ptr(out["abs_o"]))
         return out
 
-    def moe_layer(self, experts, E, S, xq, xd, idx, w, out=None, accumulate=False):
+    def moe_layer(self, experts, E, S, xq, xd, idx, w, out=None, accumulate=False, keep=None):
         """experts: dict or list mapping expert id (0..E+S-1) -> Expert (missing = unused).
+        keep [T][k] (optional, keep_entries): the entries to serve; without it every
+        entry must be valid.
 
         Returns (out [T][D] fp32, absterm [T][D] fp64)."""
         xq = _c(xq, np.int8)
@@ -319,6 +334,9 @@ class Oracle:
         idx = _c(idx, np.int32)
         w = _c(w, np.float32)
         T, k = idx.shape
+        if keep is not None:
+            keep = _c(keep, np.uint8)
+            assert keep.shape == idx.shape
         any_ex = next(iter(experts.values())) if isinstance(experts, dict) else experts[0]
         D, F, bits = any_ex.D, any_ex.F, any_ex.bits
         table = (ctypes.c_void_p * (6 * (E + S)))()
@@ -334,7 +352,8 @@ class Oracle:
             out = np.array(out, dtype=np.float32, copy=True, order="C")
         absterm = np.empty((T, D), dtype=np.float64)
         rc = self.L.orc_moe_layer(table, bits, E, S, D, F, T, _ptr(xq), _ptr(xd), _ptr(idx),
-                                 _ptr(w), k, _ptr(out), int(bool(accumulate)), _ptr(absterm))
+                                 _ptr(w), k, _ptr(keep), _ptr(out), int(bool(accumulate)),
+                                 _ptr(absterm))
         if rc != 0:
             raise ValueError("orc_moe_layer: a selected expert is missing or an index is invalid")
         return out, absterm

@@ -369,12 +369,38 @@ void orc_expert(const uint8_t* gate_q, const float* gate_s, const uint8_t* up_q,
 }
 
 /* ------------------------------------------------------------------------
+ * Which routing entries a forward serves.  The router never selects an
+ * expert twice for one token nor one outside [0, E), but the forward also
+ * takes routings from its caller; the reading used on both sides: an entry
+ * (t, j) is kept when 0 <= idx[t][j] < E and no earlier slot i < j of the
+ * same token holds the same expert; a dropped entry is not listed for any
+ * expert and contributes nothing to the token's output.  keep[t*k + j] = 1
+ * for a kept entry, else 0; returns the number of dropped entries.
+ */
+int64_t orc_keep_entries(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint8_t* keep) {
+  int64_t dropped = 0;
+  for (int64_t t = 0; t < T; ++t)
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      int ok = e >= 0 && e < E;
+      for (int32_t i = 0; i < j; ++i)
+        if (idx[t * k + i] == e) ok = 0;
+      keep[t * k + j] = (uint8_t)ok;
+      dropped += !ok;
+    }
+  return dropped;
+}
+
+/* ------------------------------------------------------------------------
  * The MoE layer, token by token: y = o_shared (0 without a shared expert),
  * then y = fmaf(w_j, o_idx_j, y) for j = 0..k-1; out = y or out + y.
+ * keep == NULL: every entry must be valid (else -1); otherwise the entries
+ * with keep[t*k + j] == 0 are skipped (orc_keep_entries).
  */
 int orc_moe_layer(const void* const* experts, int bits, int32_t E, int32_t S, int64_t D,
                   int64_t F, int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
-                  const float* w, int32_t k, float* out, int accumulate, double* absterm) {
+                  const float* w, int32_t k, const uint8_t* keep, float* out, int accumulate,
+                  double* absterm) {
   float* g = (float*)malloc(sizeof(float) * (size_t)F);
   float* u = (float*)malloc(sizeof(float) * (size_t)F);
   float* h = (float*)malloc(sizeof(float) * (size_t)F);
@@ -390,6 +416,7 @@ int orc_moe_layer(const void* const* experts, int bits, int32_t E, int32_t S, in
     const float* dt = xd + t * (D / 32);
     for (int64_t r = 0; r < D; ++r) { y[r] = 0.0f; my[r] = 0.0; }
     for (int32_t j = -S; j < k; ++j) {   /* j = -1: the shared expert first */
+      if (j >= 0 && keep && !keep[t * k + j]) continue;
       const int32_t e = j < 0 ? E : idx[t * k + j];
       if (e < 0 || e >= E + S) { rc = -1; break; }
       const void* const* ex = experts + 6 * (int64_t)e;
@@ -453,10 +480,12 @@ void orc_router_logits(const float* x, const float* wr, int64_t T, int64_t D, in
  * selected expert's weights are read once per pass.
  */
 int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
-                 int32_t* counts, int32_t* lists, int32_t* n_active, int32_t* active) {
+                 const uint8_t* keep, int32_t* counts, int32_t* lists, int32_t* n_active,
+                 int32_t* active) {
   for (int32_t e = 0; e < E + S; ++e) counts[e] = 0;
   for (int64_t t = 0; t < T; ++t)
     for (int32_t j = 0; j < k; ++j) {
+      if (keep && !keep[t * k + j]) continue;   /* a dropped entry is not listed */
       if (idx[t * k + j] < 0 || idx[t * k + j] >= E) return -1;
       for (int32_t i = 0; i < j; ++i)
         if (idx[t * k + i] == idx[t * k + j]) return -1;   /* top-k never repeats */
@@ -468,7 +497,8 @@ int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
         continue;
       }
       for (int32_t j = 0; j < k; ++j)
-        if (idx[t * k + j] == e) lists[(int64_t)e * T + counts[e]++] = (int32_t)(t * (k + S) + j);
+        if (idx[t * k + j] == e && (!keep || keep[t * k + j]))
+          lists[(int64_t)e * T + counts[e]++] = (int32_t)(t * (k + S) + j);
     }
   }
   int32_t na = 0;

@@ -89,10 +89,18 @@ void orc_expert(const uint8_t* gate_q, const float* gate_s, const uint8_t* up_q,
  * down_s (NULL rows are allowed for experts no token selects).  The shared
  * expert is index E.  out[T][D] = moe (accumulate = 0) or out + moe (1).
  * absterm[T][D] (optional) receives the fp64 sum of |terms| of each output.
+ * keep[T][k] (optional): entries with keep == 0 are skipped (see
+ * orc_keep_entries); without it every entry must be valid.
  * Returns 0, or -1 if a selected expert is missing / an index is invalid. */
 int orc_moe_layer(const void* const* experts, int bits, int32_t E, int32_t S, int64_t D,
                   int64_t F, int64_t T, const int8_t* xq, const float* xd, const int32_t* idx,
-                  const float* w, int32_t k, float* out, int accumulate, double* absterm);
+                  const float* w, int32_t k, const uint8_t* keep, float* out, int accumulate,
+                  double* absterm);
+
+/* Entries a forward serves: (t, j) is kept when idx[t][j] is in [0, E) and no
+ * earlier slot of token t holds the same expert.  keep[T][k] = 1 / 0; returns
+ * the number of dropped entries. */
+int64_t orc_keep_entries(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint8_t* keep);
 
 /* RMSNorm with unit gain: ss in fp64, r = (float)(1/sqrt(ss/D + eps)), out = h * r. */
 void orc_rmsnorm(const float* h, int64_t T, int64_t D, float eps, float* out, float* r_out);
@@ -108,9 +116,12 @@ void orc_router_logits(const float* x, const float* wr, int64_t T, int64_t D, in
  * list lists[e*T .. e*T+counts[e]) of pair ids p = t*(k+S) + slot in
  * ascending token order (the shared expert E takes slot k of every token).
  * active[0..*n_active) lists the experts with counts > 0 in ascending id.
- * Returns 0, or -1 if an index is outside [0, E) or repeats within a token. */
+ * keep[T][k] (optional): only entries with keep == 1 are listed.
+ * Returns 0, or -1 if a listed index is outside [0, E) or repeats within a
+ * token. */
 int orc_dispatch(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t S,
-                 int32_t* counts, int32_t* lists, int32_t* n_active, int32_t* active);
+                 const uint8_t* keep, int32_t* counts, int32_t* lists, int32_t* n_active,
+                 int32_t* active);
 
 /* Expert tier of one layer (per-layer LRU + pinned hot store + usage
  * counts; the full policy is stated in coli_oracle.c).  State arrays:

@@ -74,7 +74,7 @@ class OracleExperts:
         return self.cache[e]
 
     def table_for(self, idx) -> dict:
-        need = set(int(v) for v in np.asarray(idx).reshape(-1))
+        need = set(int(v) for v in np.asarray(idx).reshape(-1) if 0 <= v < self.w.E)
         if self.w.S:
             need.add(self.w.E)
         return {e: self[e] for e in sorted(need)}

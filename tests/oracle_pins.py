@@ -396,6 +396,61 @@ def pin_moe_invariants(orc):
         assert np.array_equal(y1[t], orc.expert_forward(distinct[int(idx[t, 0])], xq[t], xd[t])["o"])
 
 
+def pin_dropped_entries(orc):
+    """Routings a caller hands to the forward may hold an index outside [0, E)
+    or the same expert twice in one token; the rule: an entry is served when it
+    is in range and no earlier slot of its token holds the same expert.
+    Pinned against a brute-force reading of that rule, and the layer with
+    dropped entries against the strict layer run on each token's kept slots."""
+    def brute(idx, E):
+        keep = np.zeros(idx.shape, np.uint8)
+        for t in range(idx.shape[0]):
+            seen = set()
+            for j in range(idx.shape[1]):
+                e = int(idx[t, j])
+                if 0 <= e < E and e not in seen:
+                    keep[t, j] = 1
+                seen.add(e)
+        return keep
+    hand = [(np.int32([[5, 5]]), 16, [[1, 0]]),
+            (np.int32([[0, 16], [3, -2]]), 16, [[1, 0], [1, 0]]),
+            (np.int32([[3, -1, 3, 7]]), 16, [[1, 0, 0, 1]]),
+            (np.int32([[2, 2, 2, 2], [1, 0, 1, 0]]), 4, [[1, 0, 0, 0], [1, 1, 0, 0]]),
+            (np.int32([[7, 8, 7, 9]]), 8, [[1, 0, 0, 0]])]
+    for idx, E, ref in hand:
+        keep, n = orc.keep_entries(idx, E)
+        assert keep.tolist() == ref, (idx.tolist(), keep.tolist())
+        assert n == int((keep == 0).sum())
+    rng = np.random.default_rng(21)
+    for T, E, k in ((40, 16, 4), (9, 8, 8), (64, 256, 8)):
+        idx = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)
+        idx[::3, 1] = idx[::3, 0]                 # plenty of repeats
+        keep, _ = orc.keep_entries(idx, E)
+        assert np.array_equal(keep, brute(idx, E)), (T, E, k)
+        counts, lists, na, active = orc.dispatch(idx, E, 1, keep=keep)
+        for e in range(E + 1):
+            ref = [t * (k + 1) + (k if e == E else j) for t in range(T) for j in range(k)
+                   if (e == E and j == 0) or (e < E and keep[t, j] and idx[t, j] == e)]
+            assert counts[e] == len(ref) and lists[e, : counts[e]].tolist() == ref, (T, E, e)
+        assert active.tolist() == [e for e in range(E + 1) if counts[e] > 0]
+    # the layer: dropped entries contribute nothing, kept ones keep their order
+    D, F, E, k, T = 256, 128, 16, 4, 6
+    table = {e: _tiny_expert(orc, rng, D, F) for e in range(E + 1)}
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    xq, xd = orc.q8_quant(x)
+    idx = np.int32([[3, 3, 5, 9], [16, 2, -1, 2], [7, 1, 7, 1], [4, 4, 4, 4], [0, 1, 2, 3],
+                    [-5, 20, 16, 99]])
+    w = rng.uniform(0.05, 0.5, size=(T, k)).astype(np.float32)
+    keep, _ = orc.keep_entries(idx, E)
+    y, _ = orc.moe_layer(table, E, 1, xq, xd, idx, w, keep=keep)
+    for t in range(T):
+        J = [j for j in range(k) if keep[t, j]]
+        ys, _ = orc.moe_layer(table, E, 1, xq[t:t + 1], xd[t:t + 1],
+                              idx[t:t + 1, J].reshape(1, len(J)), w[t:t + 1, J].reshape(1, len(J)))
+        assert np.array_equal(y[t], ys[0]), f"token {t} with dropped entries"
+    assert np.array_equal(y[5], orc.expert_forward(table[E], xq[5], xd[5])["o"]), "all dropped"
+
+
 def pin_rmsnorm(orc):
     eps = np.float32(1e-6)
     for c in (1.0, -0.37, 25.0, 1e-4):
@@ -681,4 +736,4 @@ def pin_int2(orc):
 ALL_PINS = [pin_nibble_codec, pin_rint_ties, pin_quant_closed_forms, pin_partials_bruteforce,
             pin_dot_fp64, pin_exp, pin_route, pin_expert_fp64, pin_moe_invariants, pin_rmsnorm,
             pin_dispatch, pin_router_logits, pin_int8_quant, pin_int8_container, pin_tier,
-            pin_int2]
+            pin_int2, pin_dropped_entries]

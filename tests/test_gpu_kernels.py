@@ -184,11 +184,33 @@ def test_dispatch(wl, T):
         assert_bitexact(f"list {e}", lists[e, :counts[e]], rl[e, :rc[e]])
 
 
-def test_dispatch_flags_bad_indices():
-    for bad in (np.int32([[0, 16], [1, 2]]), np.int32([[-1, 3]]), np.int32([[5, 5], [1, 2]])):
-        counts, lists, na, active, err = dispatch(bad, 16, 1)
+def _bad_routings():
+    yield np.int32([[0, 16], [1, 2]]), 16
+    yield np.int32([[-1, 3]]), 16
+    yield np.int32([[5, 5], [1, 2]]), 16
+    yield np.int32([[5, 5], [5, 4]]), 16
+    rng = np.random.default_rng(5)
+    for T, E, k in ((300, 256, 8), (700, 16, 2), (65, 64, 4)):
+        idx = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+        idx[::2, -1] = idx[::2, 0]
+        yield idx, E
+
+
+def test_dispatch_drops_bad_indices():
+    """Out-of-range and repeated entries are left out of every list (the
+    oracle's keep rule), the lists of the rest are exact, and the flag is set;
+    the larger cases span several 256-token sweeps."""
+    for bad, E in _bad_routings():
+        counts, lists, na, active, err = dispatch(bad, E, 1)
         assert err == coli.COLI_E_INDEX
-        assert np.all(counts[:16] <= bad.shape[0])
+        keep, dropped = oracle.keep_entries(bad, E)
+        assert dropped > 0
+        rc, rl, rna, ract = oracle.dispatch(bad, E, 1, keep=keep)
+        assert_bitexact("counts", counts, rc)
+        assert na == rna
+        assert_bitexact("active", active[:na], ract)
+        for e in range(E + 1):
+            assert_bitexact(f"list {e}", lists[e, :counts[e]], rl[e, :rc[e]])
 
 
 def test_rmsnorm_q8():

@@ -155,38 +155,57 @@ def test_tiny_layer_accumulate_and_determinism(tiny):
     assert_bitexact("y (run 2)", g2["y"], g1["y"])
 
 
-def test_invalid_index_is_reported_not_faulting(tiny):
-    w, table, _ = tiny
-    T = 2
-    xq = torch.zeros((T, w.D), dtype=torch.int8, device=dev)
-    xd = torch.ones((T, w.D // 32), dtype=torch.float32, device=dev)
-    idx = to_dev(np.int32([[0, 16], [3, -2]]))
-    wt = torch.full((T, w.k), 0.5, dtype=torch.float32, device=dev)
-    y = torch.empty((T, w.D), dtype=torch.float32, device=dev)
+def _dropped_case(w, table, ox, idx, path, seed):
+    """Forward of a routing with dropped entries (out of range, or a repeat of
+    an earlier slot of the token) against the oracle serving the kept entries."""
+    T = idx.shape[0]
+    x = synth.activations(w, T, seed)
+    xq_h, xd_h = oracle.q8_quant(x)
+    wt_h = np.random.default_rng(seed).uniform(0.05, 0.5, size=idx.shape).astype(np.float32)
+    xq, xd = to_dev(xq_h), to_dev(xd_h)
+    y = torch.full((T, w.D), float("nan"), dtype=torch.float32, device=dev)
     ws = torch.empty(coli.coli_moe_workspace_bytes(table, T, w.k), dtype=torch.uint8, device=dev)
-    coli.coli_moe_forward(table, xq, xd, idx, wt, y, ws)
-    assert coli.coli_moe_status(ws) == coli.COLI_E_INDEX
-    assert torch.isfinite(y).all()
-    # a valid call on the same workspace clears the flag
-    coli.coli_moe_forward(table, xq, xd, to_dev(np.int32([[0, 1], [2, 3]])), wt, y, ws)
-    assert coli.coli_moe_status(ws) == coli.COLI_OK
+    ws.fill_(0x7F)                      # stale contents must not reach y
+    coli.coli_moe_forward_path(table, xq, xd, to_dev(idx), to_dev(wt_h), y, ws, path)
+    keep, dropped = oracle.keep_entries(idx, w.E)
+    assert coli.coli_moe_status(ws) == (coli.COLI_E_INDEX if dropped else coli.COLI_OK)
+    ry, _ = oracle.moe_layer(ox.table_for(idx), w.E, w.S, xq_h, xd_h, idx, wt_h, keep=keep)
+    assert_bitexact(f"y (T={T}, path {path})", y.cpu().numpy(), ry)
+    return ws
 
 
-def test_invalid_index_one_token(tiny):
-    """One token (the quarter-row path): an out-of-range expert leaves its
-    slot without a live expert; the flag is raised and the rest is finite."""
-    w, table, _ = tiny
-    xq = torch.ones((1, w.D), dtype=torch.int8, device=dev)
+@pytest.mark.parametrize("bad", [[[5, 5]], [[0, 16]], [[-1, 3]], [[16, 16]]])
+def test_dropped_entries_one_token(tiny, bad):
+    """One token: a repeated or out-of-range slot contributes nothing (the y of
+    the kept slots, bit-exact), the flag is raised, and the next valid call on
+    the same workspace clears it."""
+    w, table, ox = tiny
+    ws = _dropped_case(w, table, ox, np.int32(bad), coli.COLI_PATH_AUTO, 31)
+    xq = torch.zeros((1, w.D), dtype=torch.int8, device=dev)
     xd = torch.ones((1, w.D // 32), dtype=torch.float32, device=dev)
     wt = torch.full((1, w.k), 0.5, dtype=torch.float32, device=dev)
     y = torch.empty((1, w.D), dtype=torch.float32, device=dev)
-    ws = torch.empty(coli.coli_moe_workspace_bytes(table, 1, w.k), dtype=torch.uint8, device=dev)
-    for bad in ([[0, 16]], [[5, 5]], [[-1, 3]]):
-        coli.coli_moe_forward(table, xq, xd, to_dev(np.int32(bad)), wt, y, ws)
-        assert coli.coli_moe_status(ws) == coli.COLI_E_INDEX, bad
-        assert torch.isfinite(y).all(), bad
     coli.coli_moe_forward(table, xq, xd, to_dev(np.int32([[0, 1]])), wt, y, ws)
     assert coli.coli_moe_status(ws) == coli.COLI_OK
+
+
+@pytest.mark.parametrize("path", ["gemv", "grouped"])
+@pytest.mark.parametrize("T", [2, 9, 100, 333])
+def test_dropped_entries_many_tokens(tiny, path, T):
+    """Batches with repeats and out-of-range slots through both expert paths:
+    T = 2 with a repeat that precedes a valid slot of the next token, and
+    ragged batches past one dispatch sweep (256 tokens)."""
+    w, table, ox = tiny
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.choice(w.E, w.k, replace=False) for _ in range(T)]).astype(np.int32)
+    if T == 2:
+        idx = np.int32([[5, 5], [5, 4]])
+    else:
+        idx[::3, 1] = idx[::3, 0]                        # repeats
+        idx[1::7, 0] = w.E + 3                           # out of range
+        idx[2::11, 1] = -1
+    p = coli.COLI_PATH_GEMV if path == "gemv" else coli.COLI_PATH_GROUPED
+    _dropped_case(w, table, ox, idx, p, 40 + T)
 
 
 # ---------------------------------------------------------------- page-scale layer

@@ -94,6 +94,13 @@ MUTANTS = {
                                "lists[(int64_t)e * T + counts[e]++] = (int32_t)(t * (k + S));"),
     "dispatch accepts repeats": ("if (idx[t * k + i] == idx[t * k + j]) return -1;",
                                  "if (0) return -1;"),
+    "keep ignores repeats": ("        if (idx[t * k + i] == e) ok = 0;", "        if (0) ok = 0;"),
+    "keep compares with later slots": ("      for (int32_t i = 0; i < j; ++i)\n        if (idx[t * k + i] == e) ok = 0;",
+                                       "      for (int32_t i = j + 1; i < k; ++i)\n        if (idx[t * k + i] == e) ok = 0;"),
+    "keep accepts index E": ("      int ok = e >= 0 && e < E;", "      int ok = e >= 0 && e <= E;"),
+    "layer ignores keep": ("      if (j >= 0 && keep && !keep[t * k + j]) continue;", ""),
+    "dispatch lists dropped entries": ("        if (idx[t * k + j] == e && (!keep || keep[t * k + j]))",
+                                       "        if (idx[t * k + j] == e)"),
     "router logits summed in fp32":
         ("    double s = 0.0;\n    for (int64_t d = 0; d < D; ++d) s += (double)wr[e * D + d] * (double)x[t * D + d];",
          "    float s = 0.0f;\n    for (int64_t d = 0; d < D; ++d) s += wr[e * D + d] * x[t * D + d];"),
