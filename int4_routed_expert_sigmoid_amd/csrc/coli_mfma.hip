@@ -5,45 +5,52 @@
 // What is computed (aitrends.kr "GLM-5.2-colibri-int4", "기술적 특징": int4
 // weights with a per-row F32 scale against int8 activations; discuss.pytorch.kr
 // colibri summary, "colibri의 주요 기능": integer-dot expert matmuls, Q8_0
-// activations; batch-union grouping so that each expert's rows are read once
-// per pass): for each dispatched (token, expert) pair and each weight row r,
+// activations; alphamatch.ai "기술적 우수성": batch-union grouping, so that
+// each expert's rows are read once per group of tokens): for each dispatched
+// (token, expert) pair and each weight row r,
 //   P[r][b] = sum over the 32 columns of block b of q_w * q_x   (exact integer)
 //   acc = fmaf(P[r][b], d_b, acc) for b = 0, 1, ... in order; out_r = acc * s_r.
 //
 // Why f16 matrix cores carry the integer dot.  The int4 codes (|q| <= 7) and
 // the Q8 codes (|q| <= 127) are exact f16 values, each product is exact, and
-// every partial sum of a 32-column block is an integer below 2^15, so the fp32
-// accumulation inside v_mfma_f32_32x32x16_f16 is exact: it returns P[r][b]
-// bit-for-bit, already as fp32.  The exact Q8_0 rescale then costs one VALU
-// fmaf per (row, token, block).  With int8 matrix cores the int32 result needs
-// a conversion first, which doubles that VALU stream, and the VALU stream, not
-// the matrix cores, bounds this kernel on gfx950.
+// every partial sum of a 32-column block is an integer below 2^15, so the
+// fp32 accumulation inside v_mfma_f32_16x16x32_f16 (K = 32 = one Q8 block) is
+// exact: it returns P[r][b] bit-for-bit, already as fp32.  The exact Q8_0
+// rescale then costs one VALU fmaf per (row, token, block) and nothing else;
+// an int8 matrix core's int32 result would need a conversion first, doubling
+// that VALU stream, which is what bounds this kernel.
 //
-// Tiling.  One wavefront owns one 64-row group of the table (32 gate + 32 up
-// rows, or 64 down rows) for up to 64 tokens (two 32-token subtiles).  Per
-// 32-column block it loads the group's 1 KB of nibbles (16 B per lane), swaps
-// lane halves so that each lane holds half of the columns of one row of each
-// 32-row tile (v_permlane32_swap), expands nibbles to f16 in registers, and
-// issues two K=16 MFMAs per 32x32 tile.  Four wavefronts of a workgroup take
-// four consecutive row groups of the same tokens and share the token blocks
-// through LDS.  The work list (expert, row quad, token chunk)
-// is built on the device after dispatch; the launch is sized for the worst
-// case and workgroups past the real count return at once.  Consecutive work
-// items are mapped to the same XCD so that chunks of one expert share its
-// weight rows in that XCD's L2.
+// Tiling.  A work item is (expert, four consecutive 64-row groups, up to 128
+// tokens of the expert's list); each of the workgroup's four wavefronts owns
+// one row group (gate/up: 32 gate + 32 up rows; down: 64 rows) against all
+// of the item's tokens, in M = ceil(tokens / 16) subtiles of 16.  Per 32-column
+// block a wavefront loads its group's 1 KB of nibbles (16 B per lane, a ring
+// of buffer loads 4 to 8 blocks deep), moves the four 8-column words of 16-row
+// tiles into MFMA operand position with two v_permlane32_swap and two
+// v_permlane16_swap, expands nibbles to f16 in registers, and issues 4 * M
+// MFMAs whose results are rescaled three MFMAs later, so the fmaf chain of one
+// tile overlaps the matrix pipe's work on the next.  The tokens' f16 operands
+// and block scales are staged into LDS one stage ahead (two slots; a stage is
+// 16 / M blocks, one barrier per stage); the 16 lanes of a 16-byte LDS read hit 16 different
+// bank groups through an XOR swizzle.  The work list is built on the device
+// after dispatch; the launch is sized for the worst case and workgroups past
+// the real count return at once.  Each XCD takes every eighth chunk of the
+// list, heaviest first, with its row quads in a row (see locate).
 #include "coli_internal.h"
 
 namespace coli {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kChunk = 64;        // tokens per work item (two 32-token subtiles)
-constexpr int kGroupsPerWg = 4;   // row groups per workgroup (one per wavefront)
-constexpr int kPfW = 4;           // weight blocks in flight per wavefront
+constexpr int kSub = 16;                 // tokens per matrix-core subtile
+constexpr int kMaxSub = 8;               // subtiles per work item
+constexpr int kChunk = kSub * kMaxSub;   // tokens per work item
+constexpr int kGroupsPerWg = 4;          // row groups per workgroup (one per wavefront)
+constexpr int kLag = 3;                  // MFMAs between a result and its rescale
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBufferConfig = 0x00020000;
@@ -69,8 +76,8 @@ __device__ __forceinline__ UnpackConsts unpack_consts() {
 // f16 values.  A nibble OR-ed into the low mantissa bits of 1024.0 (0x6400)
 // gives 1024 + n, one OR-ed four bits higher gives 1024 + 16n; subtracting
 // 1032 or 1152 leaves q or 16q.  Element order (columns): 0, 2, 4, 6, 1, 3, 5,
-// 7, where the elements 2, 3, 6, 7 carry 16q; the activation operand carries
-// x / 16 in those places, so every product is exactly q * x.
+// 7, where the elements 2, 3, 6, 7 carry 16q; the token operand carries x / 16
+// in those places, so every product is exactly q * x.
 __device__ __forceinline__ half8 nibbles_to_f16(uint32_t w, const UnpackConsts& c) {
   const half2v b1 = {(_Float16)1032.0f, (_Float16)1032.0f};
   const half2v b16 = {(_Float16)1152.0f, (_Float16)1152.0f};
@@ -85,47 +92,32 @@ __device__ __forceinline__ half8 nibbles_to_f16(uint32_t w, const UnpackConsts& 
   return r;
 }
 
-// The matrix-core operands of one table chunk.  Lane L of a row group holds
-// row L's 32 columns as words w0..w3 (columns 0-7, 8-15, 16-23, 24-31).  A
-// 32x32x16 MFMA wants lane l to hold row (l & 31) with columns 16 * (l >> 5)
-// onward.  Swapping w0/w1 of the upper lanes with w2/w3 of the lower lanes
-// gives every lane the right half of tile 0 (rows 0-31 of the group) in
-// (t0a, t0b) and of tile 1 (rows 32-63) in (t1a, t1b).
-struct TileOps {
-  half8 t0a, t0b, t1a, t1b;
-};
-
-__device__ __forceinline__ TileOps tile_operands(u32x4 w, const UnpackConsts& c) {
-  const auto s0 = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
-  const auto s1 = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
-  TileOps o;
-  o.t0a = nibbles_to_f16(s0[0], c);
-  o.t0b = nibbles_to_f16(s1[0], c);
-  o.t1a = nibbles_to_f16(s0[1], c);
-  o.t1b = nibbles_to_f16(s1[1], c);
-  return o;
+// The four 16-row tile operands of one table chunk.  Lane 16 * q + j holds
+// row 16 * q + j of the group as words 0..3 (columns 0-7, 8-15, 16-23,
+// 24-31).  A 16x16x32 MFMA wants, in lane 16 * g + j of tile t, word g of row
+// 16 * t + j: a transpose of (16-lane row, word) over 4 x 4, done as a swap of
+// the off-diagonal 2 x 2 quadrants across the wavefront halves followed by a
+// swap inside each 32-lane half.
+__device__ __forceinline__ void tile_words(u32x4 w, uint32_t (&t)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  t[0] = c[0];
+  t[1] = c[1];
+  t[2] = d[0];
+  t[3] = d[1];
 }
 
-__device__ __forceinline__ f32x16 mfma(half8 a, half8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(half8 a, half8 b) {
+  const f32x4 z = {};
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
 }
 
-// The ordered rescale acc = fmaf(P, d, acc) of every element of a tile, kept
-// where it is written: the empty volatile asm statements make P an input
-// produced at this point and acc an output consumed here, so the compiler
-// neither hoists the fmaf group above the preceding MFMAs nor sinks it into
-// the next block.
-__device__ __forceinline__ void rescale(f32x16& acc, f32x16 p, float d) {
-  asm volatile("" : "+v"(p));
+// acc = fmaf(P, d, acc) for the four elements of a tile that a lane holds.
+__device__ __forceinline__ void rescale(f32x4& acc, f32x4 p, float d) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(p[i], d, acc[i]);
-  asm volatile("" : "+v"(acc));
-}
-
-// Row of a 32x32 tile held by register i of lane l; the lane's column (token)
-// is l & 31.
-__device__ __forceinline__ int tile_row(int i, int lane) {
-  return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+  for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(p[i], d, acc[i]);
 }
 
 struct Item {
@@ -133,15 +125,19 @@ struct Item {
   bool ok;
 };
 
-// Work item of this workgroup: logical index L = XCD-major remap of
-// blockIdx.x over the real item count.
-__device__ __forceinline__ Item locate(const int2* items, const int32_t* total) {
+// Work item of this workgroup.  The lists are chunk-major (the row quads of
+// one chunk are consecutive, q per chunk) and sorted by descending work.
+// Workgroups are dispatched to the eight XCDs round robin by blockIdx.x, and
+// XCD x takes chunks x, x + 8, x + 16, ... with all q row quads of a chunk in
+// a row: every XCD gets the same mix of heavy and light chunks, and the row
+// quads of a chunk, which stage the same tokens, share them in that XCD's L2.
+__device__ __forceinline__ Item locate(const int2* items, const int32_t* total, int q) {
   Item it = {};
   const int tot = *as_const(total);
-  const int per = (tot + 7) >> 3;
   const int bid = (int)blockIdx.x;
-  const int L = (bid & 7) * per + (bid >> 3);
-  it.ok = (bid >> 3) < per && L < tot;
+  const int k = bid >> 3;
+  const int L = ((k / q) * 8 + (bid & 7)) * q + k % q;
+  it.ok = L < tot;
   if (!it.ok) return it;
   const cptr<int32_t> v = as_const(reinterpret_cast<const int32_t*>(items) + 2 * (size_t)L);
   const int x = v[0];
@@ -151,515 +147,514 @@ __device__ __forceinline__ Item locate(const int2* items, const int32_t* total) 
   return it;
 }
 
-struct GuArgs {
-  const u32x4* gu_q;
-  const float* gu_s;
-  const u32x4* xh;       // [T][NB][4] 16-byte pieces of f16 codes
-  const float* xd;       // [T][NB]
-  const int32_t* counts;
-  const int32_t* lists;
-  const int2* items;
-  const int32_t* total;
-  uint32_t* h16;         // [P][G][16] words: f16 codes of Q8(h)
-  float* hd;             // [P][G]
-  int8_t* hq;            // [P][F] (traced runs only)
-  int64_t T, D, F;
-  int k, S;
-  int32_t* tr_pg;
-  int32_t* tr_pu;
-  float* tr_g;
-  float* tr_u;
-  float* tr_h;
-};
-
-struct DnArgs {
-  const u32x4* dn_q;
-  const float* dn_s;
-  const u32x4* h16;      // [P][G][4] pieces
-  const float* hd;
-  const int32_t* counts;
-  const int32_t* lists;
-  const int2* items;
-  const int32_t* total;
-  float* o;              // [P][D]
-  int64_t T, D, F;
-  int k, S;
-  int32_t* tr_pd;
-};
-
-// ---------------------------------------------------------------------------
-// Streaming one row group against the chunk's tokens.
-//
-// Weights: a kPfW-deep register ring of 16-byte buffer loads per lane; the
-// operands of block b + 1 are unpacked while the MFMAs of block b run.
-// Tokens: the workgroup stages kStage blocks of its 64 tokens' f16 pieces and
-// block scales in LDS (two stage slots); each wavefront loads a quarter of a
-// stage into registers one stage ahead and stores it to the free slot, and a
-// barrier per stage publishes it.  Inside a token's 64-byte block the four
-// 16-byte pieces sit at position piece ^ ((token >> 2) & 3), so the 16 lanes
-// of one LDS read hit 16 different 16-byte bank groups.
-constexpr int kStage = 4;   // blocks per LDS stage (= one turn of the weight ring)
-static_assert(kPfW == kStage, "one weight ring turn per stage");
-
-struct StageLds {
-  uint4 x[2][kStage][kChunk][4];
-  float d[2][kChunk][kStage];
-};
-
-struct WeightRows {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t off;   // this lane's chunk offset within a block (16 * lane)
-};
-
-// The lane's share of stage loads: token 16 * wave + lane / 4 of the chunk,
-// piece (lane & 3) ^ swizzle, and the scales of blocks 2 * (lane & 3) + {0, 1}
-// (lanes with (lane & 3) >= kStage / 2 load nothing for the scales).
-struct TokenRows {
-  __amdgpu_buffer_rsrc_t rs;
-  uint32_t off;       // byte offset of the token row's piece in block 0
-  const float* d;     // the token's scales
-  int NB;
-};
-
-struct StageRegs {
-  u32x4 x[kStage];
-  float d0, d1;
-};
-
-__device__ __forceinline__ void stage_load(const TokenRows& t, int b0, int lane, StageRegs& r) {
-#pragma unroll
-  for (int j = 0; j < kStage; ++j) {
-    const int b = b0 + j < t.NB ? b0 + j : t.NB - 1;
-    r.x[j] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, t.off + 64u * (uint32_t)b, 0, 0);
-  }
-  const int bd = b0 + 2 * (lane & 3);
-  r.d0 = t.d[bd < t.NB ? bd : t.NB - 1];
-  r.d1 = t.d[bd + 1 < t.NB ? bd + 1 : t.NB - 1];
-}
-
-__device__ __forceinline__ void stage_store(StageLds& L, int slot, int wave, int lane,
-                                            const StageRegs& r) {
-  uint4* xs = &L.x[slot][0][0][0] + 64 * wave + lane;
-#pragma unroll
-  for (int j = 0; j < kStage; ++j) xs[j * kChunk * 4] = __builtin_bit_cast(uint4, r.x[j]);
-  if (2 * (lane & 3) < kStage) {
-    float* ds = &L.d[slot][16 * wave + (lane >> 2)][2 * (lane & 3)];
-    ds[0] = r.d0;
-    ds[1] = r.d1;
-  }
-}
-
-template <int NSUB>
-struct Acc {
-  f32x16 t0[NSUB], t1[NSUB];   // tile 0 (rows 0-31 of the group), tile 1 (rows 32-63)
-};
-
-// Token operands (two K-halves per subtile) of block J of a stage slot.
-template <int NSUB>
-struct BOps {
-  half8 k0[NSUB], k1[NSUB];
-};
-
-template <int NSUB>
-__device__ __forceinline__ void read_bops(const StageLds& L, int slot, int J, int p0, int p1,
-                                          int lane, BOps<NSUB>& o) {
-  const uint4* xs = &L.x[slot][J][0][0];
-  const int n = lane & 31;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    o.k0[s] = __builtin_bit_cast(half8, xs[(32 * s + n) * 4 + p0]);
-    o.k1[s] = __builtin_bit_cast(half8, xs[(32 * s + n) * 4 + p1]);
-  }
-}
-
-#define COLI_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-// Block b = b0 + J of stage slot `slot`, in an order that keeps the matrix
-// pipe and the VALU busy together: the MFMAs of subtile 0, the first half of
-// the next block's nibble expansion, the rescale of tile 0, the MFMAs of
-// subtile 1, the rescale of tile 1, the second half of the expansion, then
-// the rescales of subtile 1.  The next block's token operands are read from
-// LDS while this block computes (within a stage).
-template <int NSUB, bool TRACE, int J>
-__device__ __forceinline__ void block_step(const StageLds& L, int slot, int b0, int NB,
-                                           const WeightRows& wr, u32x4 (&wq)[kPfW], TileOps& cur,
-                                           BOps<NSUB>& bo, const UnpackConsts& uc,
-                                           const float (&dv)[NSUB][kStage], int p0, int p1,
-                                           Acc<NSUB>& acc, int32_t* const (&tr0)[NSUB],
-                                           int32_t* const (&tr1)[NSUB], int lane) {
-  const int b = b0 + J;
-  const f32x16 z = {};
-  f32x16 p[NSUB][2];
-  p[0][0] = mfma(cur.t0a, bo.k0[0], z);
-  p[0][1] = mfma(cur.t1a, bo.k0[0], z);
-  p[0][0] = mfma(cur.t0b, bo.k1[0], p[0][0]);
-  p[0][1] = mfma(cur.t1b, bo.k1[0], p[0][1]);
-  COLI_FENCE();
-  BOps<NSUB> bn = bo;
-  if (J + 1 < kStage) read_bops<NSUB>(L, slot, J + 1, p0, p1, lane, bn);
-  constexpr int JN = (J + 1) % kPfW;   // ring slot of block b + 1
-  const u32x4 w = wq[JN];
-  const auto sa = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
-  TileOps nx;
-  nx.t0a = nibbles_to_f16(sa[0], uc);
-  nx.t1a = nibbles_to_f16(sa[1], uc);
-  COLI_FENCE();
-  rescale(acc.t0[0], p[0][0], dv[0][J]);
-  COLI_FENCE();
-  if (NSUB > 1) {
-    p[NSUB - 1][0] = mfma(cur.t0a, bo.k0[NSUB - 1], z);
-    p[NSUB - 1][1] = mfma(cur.t1a, bo.k0[NSUB - 1], z);
-    p[NSUB - 1][0] = mfma(cur.t0b, bo.k1[NSUB - 1], p[NSUB - 1][0]);
-    p[NSUB - 1][1] = mfma(cur.t1b, bo.k1[NSUB - 1], p[NSUB - 1][1]);
-    COLI_FENCE();
-  }
-  rescale(acc.t1[0], p[0][1], dv[0][J]);
-  COLI_FENCE();
-  const auto sb = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
-  nx.t0b = nibbles_to_f16(sb[0], uc);
-  nx.t1b = nibbles_to_f16(sb[1], uc);
-  const int bnx = b + 1 + kPfW < NB ? b + 1 + kPfW : NB - 1;
-  wq[JN] = __builtin_amdgcn_raw_buffer_load_b128(wr.rs, wr.off + 1024u * (uint32_t)bnx, 0, 0);
-  COLI_FENCE();
-  if (NSUB > 1) {
-    rescale(acc.t0[NSUB - 1], p[NSUB - 1][0], dv[NSUB - 1][J]);
-    rescale(acc.t1[NSUB - 1], p[NSUB - 1][1], dv[NSUB - 1][J]);
-  }
-  if (TRACE) {
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = tile_row(i, lane);
-        if (tr0[s]) tr0[s][(size_t)rr * NB + b] = (int32_t)p[s][0][i];
-        if (tr1[s]) tr1[s][(size_t)rr * NB + b] = (int32_t)p[s][1][i];
-      }
-    }
-  }
-  cur = nx;
-  bo = bn;
-}
-
-template <int NSUB, bool TRACE, bool GUARD, int J>
-__device__ __forceinline__ void stage_steps(const StageLds& L, int slot, int b0, int NB,
-                                            const WeightRows& wr, u32x4 (&wq)[kPfW],
-                                            TileOps& cur, BOps<NSUB>& bo, const UnpackConsts& uc,
-                                            const float (&dv)[NSUB][kStage], int p0, int p1,
-                                            Acc<NSUB>& acc, int32_t* const (&tr0)[NSUB],
-                                            int32_t* const (&tr1)[NSUB], int lane) {
-  if constexpr (J < kStage) {
-    if (!GUARD || b0 + J < NB)
-      block_step<NSUB, TRACE, J>(L, slot, b0, NB, wr, wq, cur, bo, uc, dv, p0, p1, acc, tr0, tr1,
-                                 lane);
-    stage_steps<NSUB, TRACE, GUARD, J + 1>(L, slot, b0, NB, wr, wq, cur, bo, uc, dv, p0, p1, acc,
-                                           tr0, tr1, lane);
-  }
-}
-
-template <int NSUB, bool TRACE, bool GUARD>
-__device__ __forceinline__ void stage_compute(const StageLds& L, int slot, int b0, int NB,
-                                              const WeightRows& wr, u32x4 (&wq)[kPfW],
-                                              TileOps& cur, const UnpackConsts& uc, int p0, int p1,
-                                              Acc<NSUB>& acc, int32_t* const (&tr0)[NSUB],
-                                              int32_t* const (&tr1)[NSUB], int lane) {
-  const int n = lane & 31;
-  float dv[NSUB][kStage];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const float4 v = *reinterpret_cast<const float4*>(&L.d[slot][32 * s + n][0]);
-    dv[s][0] = v.x;
-    dv[s][1] = v.y;
-    dv[s][2] = v.z;
-    dv[s][3] = v.w;
-  }
-  BOps<NSUB> bo;
-  read_bops<NSUB>(L, slot, 0, p0, p1, lane, bo);
-  stage_steps<NSUB, TRACE, GUARD, 0>(L, slot, b0, NB, wr, wq, cur, bo, uc, dv, p0, p1, acc, tr0,
-                                     tr1, lane);
-}
-
-// All NB blocks of one row group against NSUB subtiles of the chunk's tokens.
-// Every wavefront of the workgroup takes part in the staging and barriers;
-// COMPUTE is false for a wavefront whose row group is past the matrix.  The
-// loop over full stages issues the same loads on every path (indices past the
-// end are clamped), so the compiler's memory-counter waits stay exact and the
-// weight and stage prefetches stay in flight; a partial last stage runs after it.
-template <int NSUB, bool TRACE, bool COMPUTE>
-__device__ __forceinline__ void stream_loop(StageLds& L, const WeightRows& wr,
-                                            const TokenRows& tk, Acc<NSUB>& acc,
-                                            int32_t* const (&tr0)[NSUB],
-                                            int32_t* const (&tr1)[NSUB], int wave, int lane) {
-  const int NB = tk.NB;
-  const int NS = (NB + kStage - 1) / kStage, NSF = NB / kStage;
-  const UnpackConsts uc = unpack_consts();
-  u32x4 wq[kPfW];
-  TileOps cur = {};
-  if (COMPUTE) {
-#pragma unroll
-    for (int j = 0; j < kPfW; ++j) {
-      const int b = j < NB ? j : NB - 1;
-      wq[j] = __builtin_amdgcn_raw_buffer_load_b128(wr.rs, wr.off + 1024u * (uint32_t)b, 0, 0);
-    }
-  }
-  StageRegs R;
-  stage_load(tk, 0, lane, R);
-  stage_store(L, 0, wave, lane, R);
-  stage_load(tk, kStage, lane, R);
-  if (COMPUTE) {
-    cur = tile_operands(wq[0], uc);
-    const int b = kPfW < NB ? kPfW : NB - 1;
-    wq[0] = __builtin_amdgcn_raw_buffer_load_b128(wr.rs, wr.off + 1024u * (uint32_t)b, 0, 0);
-  }
-  __syncthreads();
-  const int n = lane & 31, h = lane >> 5, sw = (n >> 2) & 3;
-  const int p0 = (2 * h) ^ sw, p1 = (2 * h + 1) ^ sw;
-  int st = 0;
-  for (; st < NSF; ++st) {
-    const int slot = st & 1;
-    if (COMPUTE)
-      stage_compute<NSUB, TRACE, false>(L, slot, st * kStage, NB, wr, wq, cur, uc, p0, p1, acc,
-                                        tr0, tr1, lane);
-    stage_store(L, slot ^ 1, wave, lane, R);
-    stage_load(tk, (st + 2) * kStage, lane, R);
-    __syncthreads();
-  }
-  if (COMPUTE && st < NS)
-    stage_compute<NSUB, TRACE, true>(L, st & 1, st * kStage, NB, wr, wq, cur, uc, p0, p1, acc,
-                                     tr0, tr1, lane);
-}
-
-template <int NSUB, bool TRACE>
-__device__ __forceinline__ void stream_group(StageLds& L, const WeightRows& wr,
-                                             const TokenRows& tk, bool compute, Acc<NSUB>& acc,
-                                             int32_t* const (&tr0)[NSUB],
-                                             int32_t* const (&tr1)[NSUB], int wave, int lane) {
-  if (compute) stream_loop<NSUB, TRACE, true>(L, wr, tk, acc, tr0, tr1, wave, lane);
-  else stream_loop<NSUB, TRACE, false>(L, wr, tk, acc, tr0, tr1, wave, lane);
-}
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferConfig);
 }
 
-// Chunk entry of this lane's stage loads and of its subtile columns.
-struct ChunkTokens {
-  int n_valid;          // tokens in the chunk (1..64)
-  int load_entry;       // list entry of token 16 * wave + lane / 4 (clamped)
-  int pair[2];          // list entries of the lane's columns in subtiles 0, 1 (clamped)
+// Arguments of both matrix kernels.  Token operands: tok [rows][NB][4] 16-byte
+// pieces of f16 codes (piece g of a block = its columns 8g .. 8g + 7 in the
+// expansion's element order), tokd [rows][NB] block scales; a list entry p
+// names row p / KS (gate/up: the token of pair p) or p (down: the pair).
+struct GArgs {
+  const u32x4* wq;        // [E+S][RG][NB][64] 16-byte lane chunks
+  const float* ws;        // gate/up: [E+S][RG][64] lane-ordered; down: [E+S][D]
+  const uint4* tok;
+  const float* tokd;
+  const int32_t* counts;
+  const int32_t* lists;
+  const int2* items;
+  const int32_t* total;
+  int64_t T, D, F;
+  int NB, RG, KS, row_div;
+  int Q;                  // row quads per chunk (items per chunk)
+  // gate/up results
+  uint32_t* h16;          // [P][F/32][4 pieces][4 words]
+  float* hd;              // [P][F/32]
+  int8_t* hq;             // [P][F] (traced runs only)
+  // down result
+  float* o;               // [P][D]
+  // traces (null = skip)
+  int32_t* tr_p0;         // gate partials / down partials
+  int32_t* tr_p1;         // up partials
+  float* tr_g;
+  float* tr_u;
+  float* tr_h;
 };
 
-__device__ __forceinline__ ChunkTokens chunk_tokens(const int32_t* lists, int64_t T, int e,
-                                                    int chunk, int cnt, int wave, int lane) {
-  ChunkTokens c;
-  const int rem = cnt - chunk * kChunk;
-  c.n_valid = rem < kChunk ? rem : kChunk;
-  const int32_t* list = lists + (size_t)e * T + (size_t)chunk * kChunk;
-  const int lt = 16 * wave + (lane >> 2);
-  c.load_entry = list[lt < c.n_valid ? lt : c.n_valid - 1];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int i = 32 * s + (lane & 31);
-    c.pair[s] = list[i < c.n_valid ? i : c.n_valid - 1];
+// Pipeline shape per subtile count M.  S blocks are staged per barrier and
+// the weight ring is R blocks deep: few tokens per item make a block cheap, so
+// small M needs more blocks in flight per wavefront and fewer barriers, and
+// has the registers for them (the accumulators are 16 M).  The staged pieces
+// per thread (M * S / 4, 16 B each) stay at 16 VGPRs or less.  The ring has
+// R + 1 slots and a block refills the slot the previous block consumed: the
+// lane swaps that move a chunk into operand position overwrite their inputs,
+// so the slot being consumed cannot take its own refill without a copy and a
+// wait for the load at the loop's back edge.  U is the loop unroll: a
+// multiple of R + 1 and of 2 S, so ring positions and LDS slots are
+// compile-time constants; the block loop runs to NB rounded up to U (see
+// stream).  Each M is one copy of the unrolled loop, so U is kept small: the
+// instruction cache is shared by the workgroups of neighbouring CUs.
+template <int M>
+struct Cfg {
+  static constexpr int S = M <= 2 ? 8 : M <= 4 ? 4 : M <= 6 ? 2 : 1;
+  static constexpr int RS = M <= 4 ? 8 : 4;             // ring slots
+  static constexpr int R = RS - 1;                      // blocks in flight
+  static constexpr int U = (2 * S > RS ? 2 * S : RS);
+  static constexpr int PT = (64 * M * S + 255) / 256;   // staged pieces per thread
+  static constexpr int XS = 64 * M * S;                 // 16-byte pieces per stage
+  static constexpr int DS = 16 * M * S;                 // scales per stage
+  static_assert(U % RS == 0 && U % (2 * S) == 0, "static ring and slot positions");
+  static_assert(DS <= 256, "one scale per thread");
+};
+
+// LDS of the staging: two slots of one stage each.  In block j of a stage,
+// piece g of token t sits at 16-byte slot 64 M j + 4 t + (g ^ ((t >> 1) & 3)),
+// so the 16 lanes of one operand read hit 16 different bank groups; the
+// scales are [j][16 M].  Sized for the largest stage (M S = 16).
+struct Stage {
+  uint4 x[2][1024];
+  float d[2][256];
+};
+
+// The thread's share of a stage: pieces q = tid + 256 i (block q / 64M of the
+// stage, token (q % 64M) / 4, piece q & 3) and, for tid < 16 M S, the scale of
+// token tid % 16M in block tid / 16M.  Loads are issued for blocks past the
+// end too (clamped to the last block), stores only for the stage's pieces.
+template <int M>
+struct StageSrc {
+  const uint4 *x0, *x1, *x2, *x3;   // block 0 piece of the token of each share
+  const float* d;                   // block 0 scale of the scale share's token
+};
+
+// Share i of a thread (named members: they must stay in registers).
+template <int I, class A, class V>
+__device__ __forceinline__ V& share(A& a) {
+  if constexpr (I == 0) return a.x0;
+  else if constexpr (I == 1) return a.x1;
+  else if constexpr (I == 2) return a.x2;
+  else return a.x3;
+}
+
+template <int I>
+__device__ __forceinline__ uint4& pick(uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
+  if constexpr (I == 0) return x0;
+  else if constexpr (I == 1) return x1;
+  else if constexpr (I == 2) return x2;
+  else return x3;
+}
+
+template <int M, int I = 0>
+__device__ __forceinline__ void stage_load(const StageSrc<M>& s, int st, int NB, int tid,
+                                           uint4& x0, uint4& x1, uint4& x2, uint4& x3,
+                                           float& d) {
+  using C = Cfg<M>;
+  if constexpr (I < C::PT) {
+    const int q = tid + 256 * I;
+    int b = st * C::S + q / (64 * M);
+    b = b < NB ? b : NB - 1;
+    pick<I>(x0, x1, x2, x3) = share<I, const StageSrc<M>, const uint4* const>(s)[(size_t)b * 4];
+    stage_load<M, I + 1>(s, st, NB, tid, x0, x1, x2, x3, d);
+  } else {
+    // a block past the end gets scale 0: fmaf(P, 0, acc) leaves acc exactly
+    // as it is (acc is never -0: it starts at +0 and an fmaf that cancels
+    // exactly rounds to +0)
+    const int b = st * C::S + (tid < C::DS ? tid : 0) / (16 * M);
+    const float v = s.d[b < NB ? b : NB - 1];   // issued on every path
+    d = b < NB ? v : 0.0f;
   }
-  return c;
 }
 
-// Piece offset of a token row for this lane's stage loads.
-__device__ __forceinline__ uint32_t load_piece_off(int64_t row, int NB, int wave, int lane) {
-  const int lt = 16 * wave + (lane >> 2);
-  const int piece = (lane & 3) ^ ((lt >> 2) & 3);
-  return (uint32_t)((uint64_t)row * (uint64_t)NB * 64u) + 16u * (uint32_t)piece;
+template <int M, int I = 0>
+__device__ __forceinline__ void stage_store(Stage& L, int slot, int tid, uint4& x0, uint4& x1,
+                                            uint4& x2, uint4& x3, float d) {
+  using C = Cfg<M>;
+  if constexpr (I < C::PT) {
+    const int q = tid + 256 * I;
+    if (C::XS % 256 == 0 || q < C::XS) {
+      const int j = q / (64 * M), rr = q % (64 * M), t = rr >> 2, g = rr & 3;
+      L.x[slot][64 * M * j + 4 * t + (g ^ ((t >> 1) & 3))] = pick<I>(x0, x1, x2, x3);
+    }
+    stage_store<M, I + 1>(L, slot, tid, x0, x1, x2, x3, d);
+  } else {
+    if (tid < C::DS) L.d[slot][tid] = d;
+  }
 }
 
-// ---------------------------------------------------------------------------
-// gate/up: g and u of one 32-row tile pair, SwiGLU, Q8_0 of h per token.
-template <int NSUB, bool TRACE>
-__device__ __forceinline__ void gate_up_body(const GuArgs& a, StageLds& L, const Item& it,
-                                             const ChunkTokens& ct, int grp, bool compute,
-                                             int wave, int lane) {
-  const int NB = (int)(a.D / 32);
-  const int64_t G = a.F / 32;
-  const int KS = a.k + a.S;
-  const int n = lane & 31, hl = lane >> 5;
-  const int nt = ct.n_valid;
-  WeightRows wr;
-  const int gsafe = compute ? grp : 0;
-  wr.rs = make_rsrc(a.gu_q + ((size_t)it.e * G + gsafe) * (size_t)NB * kWave, (uint64_t)NB * 1024u);
-  wr.off = 16u * (uint32_t)lane;
-  TokenRows tk;
-  tk.NB = NB;
-  tk.rs = make_rsrc(a.xh, (uint64_t)a.T * (uint64_t)a.D * 2u);
-  const int64_t lt = ct.load_entry / KS;
-  tk.off = load_piece_off(lt, NB, wave, lane);
-  tk.d = a.xd + lt * NB;
-  int32_t* tr0[NSUB];
-  int32_t* tr1[NSUB];
+// Per-wavefront state of the block loop.
+template <int M>
+struct Acc {
+  f32x4 a[M][4];   // [subtile][tile]: rows 4 * (lane >> 4) + i of tile t, token lane & 15
+};
+
+struct Trace {
+  int32_t* p[kMaxSub][4];   // row base (times NB) of each (subtile, tile) element 0, or null
+};
+
+// One block of the stream: expand the weights, read the tokens' operands,
+// issue the MFMAs subtile by subtile and rescale each result kLag MFMAs later.
+// The kLag results still pending at the end of the block (subtile M - 1, the
+// last kLag tiles) are carried in p[] with their scale in dprev and rescaled
+// at the start of the next block.
+template <int M, bool TRACE>
+__device__ __forceinline__ void block_step(const Stage& L, int slot, int jst, int xoff, int n,
+                                           u32x4 w, const UnpackConsts& uc, Acc<M>& acc,
+                                           f32x4 (&p)[4], float& dprev, const Trace& tr, int b,
+                                           int NB) {
+  float d[M];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    tr0[s] = tr1[s] = nullptr;
-    if (TRACE && compute && 32 * s + n < nt) {
-      const size_t row0 = ((size_t)ct.pair[s] * a.F + 32 * (size_t)grp) * NB;
-      if (a.tr_pg) tr0[s] = a.tr_pg + row0;
-      if (a.tr_pu) tr1[s] = a.tr_pu + row0;
+  for (int s = 0; s < M; ++s) d[s] = L.d[slot][kSub * M * jst + kSub * s + n];
+  const uint4* xs = &L.x[slot][64 * M * jst + xoff];
+  half8 B[M];
+  B[0] = __builtin_bit_cast(half8, xs[0]);
+  if (M > 1) B[1] = __builtin_bit_cast(half8, xs[64]);
+  uint32_t tw[4];
+  tile_words(w, tw);
+  half8 A[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) A[t] = nibbles_to_f16(tw[t], uc);
+#pragma unroll
+  for (int s = 0; s < M; ++s) {
+    if (s + 2 < M) B[s + 2] = __builtin_bit_cast(half8, xs[64 * (s + 2)]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 4 * s + t;
+      p[i & 3] = mfma(A[t], B[s]);
+      if (TRACE && tr.p[s][t] && b < NB) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tr.p[s][t][(size_t)r * NB + b] = (int32_t)p[i & 3][r];
+      }
+      // the result kLag MFMAs back: this block's item i - kLag, or one of the
+      // last kLag of the previous block (subtile M - 1)
+      const int j = i - kLag;
+      if (j >= 0) rescale(acc.a[j >> 2][j & 3], p[j & 3], d[j >> 2]);
+      else rescale(acc.a[M - 1][4 + j], p[4 + j], dprev);
     }
   }
-  Acc<NSUB> acc;
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc.t0[s][i] = acc.t1[s][i] = 0.0f;
-  }
-  stream_group<NSUB, TRACE>(L, wr, tk, compute, acc, tr0, tr1, wave, lane);
-  if (!compute) return;
+  dprev = d[M - 1];
+}
 
-  const float* sg = a.gu_s + ((size_t)it.e * G + grp) * kWave;
+// All NB blocks of one row group against the item's M subtiles.  Every
+// wavefront of the workgroup takes part in the staging and the barriers;
+// `compute` is false for a wavefront whose row group is past the matrix.
+// Stage st is loaded into registers one stage ahead and stored to slot
+// st & 1 after the barrier that ends stage st - 1 (all reads of that slot,
+// two stages back, are done by then).
+template <int M, bool TRACE>
+__device__ __forceinline__ void stream_loop(Stage& L, const GArgs& a, __amdgpu_buffer_rsrc_t wrs,
+                                            const StageSrc<M>& src, bool compute, Acc<M>& acc,
+                                            const Trace& tr, int tid, int lane) {
+  using C = Cfg<M>;
+  const int NB = a.NB;
+  const UnpackConsts uc = unpack_consts();
+  // the lane's operand: piece (lane >> 4) of token (lane & 15) of each
+  // subtile, at 16-byte slot xoff (+ 64 per subtile)
+  const int n = lane & 15, g = lane >> 4;
+  const int xoff = 4 * n + (g ^ ((n >> 1) & 3));
+  const uint32_t voff = 16u * (uint32_t)lane;
+  u32x4 wq[C::RS];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    const bool valid = 32 * s + n < nt;
-    const size_t p = (size_t)ct.pair[s];
-    float h[16];
-    float amax = 0.0f;
+  for (int j = 0; j < C::R; ++j)
+    wq[j] = __builtin_amdgcn_raw_buffer_load_b128(wrs, voff + 1024u * (uint32_t)(j < NB ? j : NB - 1),
+                                                  0, 0);
+  uint4 r0 = {}, r1 = {}, r2 = {}, r3 = {};
+  float rd = 0.0f;
+  stage_load<M>(src, 0, NB, tid, r0, r1, r2, r3, rd);
+  stage_store<M>(L, 0, tid, r0, r1, r2, r3, rd);
+  stage_load<M>(src, 1, NB, tid, r0, r1, r2, r3, rd);
+  __syncthreads();
+  f32x4 p[4] = {};
+  float dprev = 0.0f;
+  // NB rounded up to U: the blocks past the end repeat the last block's
+  // weights and tokens with scale 0 (stage_load), so they change nothing
+  const int NBU = (NB + C::U - 1) / C::U * C::U;
+  for (int b = 0; b < NBU; b += C::U) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = tile_row(i, lane);
-      const float g = acc.t0[s][i] * sg[r];
-      const float u = acc.t1[s][i] * sg[32 + r];
-      h[i] = silu_f32(g) * u;
-      amax = fmaxf(amax, fabsf(h[i]));
-      if (TRACE && valid) {
-        const size_t o = p * a.F + 32 * (size_t)grp + r;
-        if (a.tr_g) a.tr_g[o] = g;
-        if (a.tr_u) a.tr_u[o] = u;
-        if (a.tr_h) a.tr_h[o] = h[i];
+    for (int j = 0; j < C::U; ++j) {
+      const int bb = b + j, jst = j % C::S, slot = (j / C::S) & 1;
+      {
+        // block bb + R into the slot block bb - 1 used (free since then),
+        // issued by every wavefront (one past the matrix reads row group 0),
+        // so that the memory-counter waits of the staging are exact
+        const int bn = bb + C::R < NB ? bb + C::R : NB - 1;
+        wq[(j + C::R) % C::RS] =
+            __builtin_amdgcn_raw_buffer_load_b128(wrs, voff + 1024u * (uint32_t)bn, 0, 0);
+      }
+      if (compute)
+        block_step<M, TRACE>(L, slot, jst, xoff, n, wq[j % C::RS], uc, acc, p, dprev, tr, bb, NB);
+      // blocks stay in program order: the scheduler would otherwise hoist the
+      // next blocks' loads into this one and run out of registers
+      __builtin_amdgcn_sched_barrier(0);
+      if (jst == C::S - 1) {   // end of stage st = bb / S
+        // unconditional, so that the memory-counter waits are exact: the
+        // stores past the last stage go to a slot nobody reads, the loads past
+        // the end read the last block
+        stage_store<M>(L, slot ^ 1, tid, r0, r1, r2, r3, rd);
+        stage_load<M>(src, bb / C::S + 2, NB, tid, r0, r1, r2, r3, rd);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 32));   // the token's other 16 rows
-    const float d = amax / 127.0f;
-    int q[16];
+  }
+  if (compute) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = q8_code(h[i], d);
-    if (!valid) continue;
-    if (hl == 0) a.hd[p * G + grp] = d;
-    // f16 codes in the piece order the down projection reads: word 4m + hl
-    // holds rows (8m + 4hl, 8m + 4hl + 2), word 4m + 2 + hl rows (+1, +3);
-    // the upper lanes' words are operand elements 2, 3, 6, 7, stored as q / 16.
-    const float sc = hl ? 0.0625f : 1.0f;
-    uint32_t* hw = a.h16 + (p * G + grp) * 16;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const half2v lo = {(_Float16)((float)q[4 * m + 0] * sc), (_Float16)((float)q[4 * m + 2] * sc)};
-      const half2v hi = {(_Float16)((float)q[4 * m + 1] * sc), (_Float16)((float)q[4 * m + 3] * sc)};
-      hw[4 * m + hl] = __builtin_bit_cast(uint32_t, lo);
-      hw[4 * m + 2 + hl] = __builtin_bit_cast(uint32_t, hi);
-    }
-    if (TRACE && a.hq) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        a.hq[p * a.F + 32 * (size_t)grp + tile_row(i, lane)] = (int8_t)q[i];
-    }
+    for (int t = 4 - kLag; t < 4; ++t) rescale(acc.a[M - 1][t], p[t], dprev);
   }
 }
 
-template <bool TRACE>
-__global__ void __launch_bounds__(256) mfma_gate_up_kernel(GuArgs a) {
-  __shared__ StageLds lds;
-  const Item it = locate(a.items, a.total);
-  if (!it.ok) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int grp = it.quad * kGroupsPerWg + wave;
-  const bool compute = grp < (int)(a.F / 32);
-  const int cnt = as_const(a.counts)[it.e];
-  const ChunkTokens ct = chunk_tokens(a.lists, a.T, it.e, it.chunk, cnt, wave, lane);
-  if (ct.n_valid > 32) gate_up_body<2, TRACE>(a, lds, it, ct, grp, compute, wave, lane);
-  else gate_up_body<1, TRACE>(a, lds, it, ct, grp, compute, wave, lane);
+template <int M, bool TRACE>
+__device__ __forceinline__ void stream(Stage& L, const GArgs& a, __amdgpu_buffer_rsrc_t wrs,
+                                       const StageSrc<M>& src, bool compute, Acc<M>& acc,
+                                       const Trace& tr, int tid, int lane) {
+  stream_loop<M, TRACE>(L, a, wrs, src, compute, acc, tr, tid, lane);
+}
+
+// Entries of this item: list entry of token t (clamped into the valid range).
+struct ChunkInfo {
+  const int32_t* list;
+  int nv;   // tokens in the item (1..128)
+};
+
+__device__ __forceinline__ int entry_of(const ChunkInfo& c, int t) {
+  return c.list[t < c.nv ? t : c.nv - 1];
+}
+
+template <int M, int I = 0>
+__device__ __forceinline__ void stage_src_share(const GArgs& a, const ChunkInfo& c, int tid,
+                                                StageSrc<M>& s) {
+  if constexpr (I < Cfg<M>::PT) {
+    const int q = tid + 256 * I;
+    const int64_t r = entry_of(c, (q % (64 * M)) >> 2) / a.row_div;
+    share<I, StageSrc<M>, const uint4*>(s) = a.tok + (size_t)r * a.NB * 4 + (q & 3);
+    stage_src_share<M, I + 1>(a, c, tid, s);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ StageSrc<M> stage_src(const GArgs& a, const ChunkInfo& c, int tid) {
+  using C = Cfg<M>;
+  StageSrc<M> s = {};
+  stage_src_share<M>(a, c, tid, s);
+  const int64_t rd = entry_of(c, (tid < C::DS ? tid : 0) % (16 * M)) / a.row_div;
+  s.d = a.tokd + (size_t)rd * a.NB;
+  return s;
 }
 
 // ---------------------------------------------------------------------------
-// down: o = s_r * acc for 64 rows (two 32-row tiles) of the chunk's pairs.
-template <int NSUB, bool TRACE>
-__device__ __forceinline__ void down_body(const DnArgs& a, StageLds& L, const Item& it,
-                                          const ChunkTokens& ct, int grp, bool compute, int wave,
-                                          int lane) {
-  const int NB = (int)(a.F / 32);
-  const int64_t G = a.F / 32;
-  const int64_t RG = a.D / 64;
-  const int n = lane & 31, hl = lane >> 5;
-  const int nt = ct.n_valid;
-  WeightRows wr;
+// gate/up: g and u of the group's 32 rows for M subtiles of tokens, SwiGLU,
+// Q8_0 of h per token (the group's 32 rows are one Q8 block of h), and the
+// f16 codes of Q8(h) in the down projection's operand order.
+template <int M, bool TRACE>
+__device__ __forceinline__ void gate_up_item(const GArgs& a, Stage& L, const Item& it,
+                                             const ChunkInfo& c, int grp, bool compute,
+                                             int tid, int lane) {
+  const int G16 = (int)(a.F / 32);
+  const int n = lane & 15, gq = lane >> 4;
   const int gsafe = compute ? grp : 0;
-  wr.rs = make_rsrc(a.dn_q + ((size_t)it.e * RG + gsafe) * (size_t)NB * kWave, (uint64_t)NB * 1024u);
-  wr.off = 16u * (uint32_t)lane;
-  TokenRows tk;
-  tk.NB = NB;
-  const int64_t P = a.T * (int64_t)(a.k + a.S);
-  tk.rs = make_rsrc(a.h16, (uint64_t)P * (uint64_t)a.F * 2u);
-  tk.off = load_piece_off(ct.load_entry, NB, wave, lane);
-  tk.d = a.hd + (size_t)ct.load_entry * G;
-  int32_t* tr0[NSUB];
-  int32_t* tr1[NSUB];
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.wq + ((size_t)it.e * a.RG + gsafe) * (size_t)a.NB * kWave,
+                (uint64_t)a.NB * 1024u);
+  Trace tr = {};
+  if (TRACE && compute) {
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    tr0[s] = tr1[s] = nullptr;
-    if (TRACE && compute && 32 * s + n < nt && a.tr_pd) {
-      tr0[s] = a.tr_pd + ((size_t)ct.pair[s] * a.D + 64 * (size_t)grp) * NB;
-      tr1[s] = tr0[s] + (size_t)32 * NB;
+    for (int s = 0; s < M; ++s) {
+      if (kSub * s + n >= c.nv) continue;
+      const size_t pr = (size_t)c.list[kSub * s + n];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int32_t* base = t < 2 ? a.tr_p0 : a.tr_p1;
+        const int row = 32 * grp + 16 * (t & 1) + 4 * gq;
+        if (base) tr.p[s][t] = base + (pr * a.F + row) * a.NB;
+      }
     }
   }
-  Acc<NSUB> acc;
+  Acc<M> acc;
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
+  for (int s = 0; s < M; ++s)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc.t0[s][i] = acc.t1[s][i] = 0.0f;
-  }
-  stream_group<NSUB, TRACE>(L, wr, tk, compute, acc, tr0, tr1, wave, lane);
+    for (int t = 0; t < 4; ++t) acc.a[s][t] = f32x4{};
+  const StageSrc<M> src = stage_src<M>(a, c, tid);
+  stream<M, TRACE>(L, a, wrs, src, compute, acc, tr, tid, lane);
   if (!compute) return;
 
-  const float* sr = a.dn_s + (size_t)it.e * a.D + 64 * (size_t)grp;
+  // lane-ordered scales of the group: lane row 16 t + 4 gq + i
+  const float* sg = a.ws + ((size_t)it.e * a.RG + grp) * kWave;
+  float sc[4][4];
 #pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    if (32 * s + n >= nt) continue;
-    float* orow = a.o + (size_t)ct.pair[s] * a.D + 64 * (size_t)grp;
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int r = 8 * m + 4 * hl;   // rows r .. r + 3 of each tile
-      float4 v0, v1;
-      v0.x = acc.t0[s][4 * m + 0] * sr[r + 0];
-      v0.y = acc.t0[s][4 * m + 1] * sr[r + 1];
-      v0.z = acc.t0[s][4 * m + 2] * sr[r + 2];
-      v0.w = acc.t0[s][4 * m + 3] * sr[r + 3];
-      v1.x = acc.t1[s][4 * m + 0] * sr[32 + r + 0];
-      v1.y = acc.t1[s][4 * m + 1] * sr[32 + r + 1];
-      v1.z = acc.t1[s][4 * m + 2] * sr[32 + r + 2];
-      v1.w = acc.t1[s][4 * m + 3] * sr[32 + r + 3];
-      *reinterpret_cast<float4*>(orow + r) = v0;
-      *reinterpret_cast<float4*>(orow + 32 + r) = v1;
+    for (int i = 0; i < 4; ++i) sc[t][i] = sg[16 * t + 4 * gq + i];
+  // one subtile per pass, always from acc.a[0]: the next subtile's
+  // accumulators move down after each pass, so the epilogue (two divisions
+  // per value) is emitted once per M rather than M times
+#pragma unroll 1
+  for (int s = 0; s < M; ++s) {
+    const bool valid = kSub * s + n < c.nv;
+    const size_t p = (size_t)entry_of(c, kSub * s + n);
+    float h[2][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gv = acc.a[0][hh][i] * sc[hh][i];
+        const float uv = acc.a[0][2 + hh][i] * sc[2 + hh][i];
+        h[hh][i] = silu_f32(gv) * uv;
+        amax = fmaxf(amax, fabsf(h[hh][i]));
+        if (TRACE && valid) {
+          const size_t o = p * a.F + 32 * (size_t)grp + 16 * hh + 4 * gq + i;
+          if (a.tr_g) a.tr_g[o] = gv;
+          if (a.tr_u) a.tr_u[o] = uv;
+          if (a.tr_h) a.tr_h[o] = h[hh][i];
+        }
+      }
     }
+    // the token's 32 rows sit in lanes n, n + 16, n + 32, n + 48
+    {
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(amax),
+                                                        __float_as_uint(amax), false, false);
+      amax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax),
+                                                        __float_as_uint(amax), false, false);
+      amax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    }
+    const float d = amax / 127.0f;
+    int q[2][4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[hh][i] = q8_code(h[hh][i], d);
+    // f16 pieces of Q8(h): rows 16 hh + 8 m + {0, 2, 4, 6, 1, 3, 5, 7} form
+    // piece 2 hh + m, the rows 4..7 of each eight as q / 16.  This lane holds
+    // rows 4 gq .. 4 gq + 3 of each half: words 0 and 2 of piece gq >> 1 for
+    // even gq, words 1 and 3 for odd gq; a swap between 16-lane rows gives
+    // each lane two adjacent words.
+    const float scl = (gq & 1) ? 0.0625f : 1.0f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const half2v x = {(_Float16)((float)q[hh][0] * scl), (_Float16)((float)q[hh][2] * scl)};
+      const half2v y = {(_Float16)((float)q[hh][1] * scl), (_Float16)((float)q[hh][3] * scl)};
+      const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                       __builtin_bit_cast(uint32_t, y), false,
+                                                       false);
+      if (valid) {
+        uint32_t* dst = a.h16 + ((p * G16 + grp) * 4 + 2 * hh + (gq >> 1)) * 4 + 2 * (gq & 1);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(sw[0], sw[1]);
+      }
+    }
+    if (valid && gq == 0) a.hd[p * G16 + grp] = d;
+    if (TRACE && valid && a.hq) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a.hq[p * a.F + 32 * (size_t)grp + 16 * hh + 4 * gq + i] = (int8_t)q[hh][i];
+    }
+#pragma unroll
+    for (int r = 0; r + 1 < M; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc.a[r][t] = acc.a[r + 1][t];
   }
 }
 
-template <bool TRACE>
-__global__ void __launch_bounds__(256) mfma_down_kernel(DnArgs a) {
-  __shared__ StageLds lds;
-  const Item it = locate(a.items, a.total);
+// down: o = s_r * acc for the group's 64 rows and the item's pairs.
+template <int M, bool TRACE>
+__device__ __forceinline__ void down_item(const GArgs& a, Stage& L, const Item& it,
+                                          const ChunkInfo& c, int grp, bool compute, int tid,
+                                          int lane) {
+  const int n = lane & 15, gq = lane >> 4;
+  const int gsafe = compute ? grp : 0;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(a.wq + ((size_t)it.e * a.RG + gsafe) * (size_t)a.NB * kWave,
+                (uint64_t)a.NB * 1024u);
+  Trace tr = {};
+  if (TRACE && compute && a.tr_p0) {
+#pragma unroll
+    for (int s = 0; s < M; ++s) {
+      if (kSub * s + n >= c.nv) continue;
+      const size_t pr = (size_t)c.list[kSub * s + n];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        tr.p[s][t] = a.tr_p0 + (pr * a.D + 64 * (size_t)grp + 16 * t + 4 * gq) * a.NB;
+    }
+  }
+  Acc<M> acc;
+#pragma unroll
+  for (int s = 0; s < M; ++s)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc.a[s][t] = f32x4{};
+  const StageSrc<M> src = stage_src<M>(a, c, tid);
+  stream<M, TRACE>(L, a, wrs, src, compute, acc, tr, tid, lane);
+  if (!compute) return;
+  const float* sr = a.ws + (size_t)it.e * a.D + 64 * (size_t)grp;
+  float4 sc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sc[t] = *reinterpret_cast<const float4*>(sr + 16 * t + 4 * gq);
+#pragma unroll 1
+  for (int s = 0; s < M; ++s) {
+    if (kSub * s + n < c.nv) {
+      float* orow = a.o + (size_t)c.list[kSub * s + n] * a.D + 64 * (size_t)grp;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float4 v = make_float4(acc.a[0][t][0] * sc[t].x, acc.a[0][t][1] * sc[t].y,
+                                     acc.a[0][t][2] * sc[t].z, acc.a[0][t][3] * sc[t].w);
+        *reinterpret_cast<float4*>(orow + 16 * t + 4 * gq) = v;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r + 1 < M; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc.a[r][t] = acc.a[r + 1][t];
+  }
+}
+
+template <bool DOWN, bool TRACE>
+__global__ void __launch_bounds__(256, 2) mfma_ffn_kernel(GArgs a) {
+  __shared__ Stage lds;
+  const Item it = locate(a.items, a.total, a.Q);
   if (!it.ok) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int tid = (int)threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = it.quad * kGroupsPerWg + wave;
-  const bool compute = grp < (int)(a.D / 64);
+  const bool compute = grp < a.RG;
   const int cnt = as_const(a.counts)[it.e];
-  const ChunkTokens ct = chunk_tokens(a.lists, a.T, it.e, it.chunk, cnt, wave, lane);
-  if (ct.n_valid > 32) down_body<2, TRACE>(a, lds, it, ct, grp, compute, wave, lane);
-  else down_body<1, TRACE>(a, lds, it, ct, grp, compute, wave, lane);
+  ChunkInfo c;
+  c.list = a.lists + (size_t)it.e * a.T + (size_t)it.chunk * kChunk;
+  const int rem = cnt - it.chunk * kChunk;
+  c.nv = rem < kChunk ? rem : kChunk;
+  const int M = (c.nv + kSub - 1) / kSub;
+#define COLI_ITEM(MM)                                                                   \
+  case MM:                                                                              \
+    if (DOWN) down_item<MM, TRACE>(a, lds, it, c, grp, compute, tid, lane);             \
+    else gate_up_item<MM, TRACE>(a, lds, it, c, grp, compute, tid, lane);               \
+    break;
+  switch (M) {
+    COLI_ITEM(1)
+    COLI_ITEM(2)
+    COLI_ITEM(3)
+    COLI_ITEM(4)
+    COLI_ITEM(5)
+    COLI_ITEM(6)
+    COLI_ITEM(7)
+    COLI_ITEM(8)
+    default: break;
+  }
+#undef COLI_ITEM
 }
 
 // ---------------------------------------------------------------------------
 // Front of the grouped path, after dispatch.  Workgroup 0 builds the work
-// lists: per active expert c = ceil(count / 64) chunks, and per chunk qg
-// gate/up and qd down row quads; items of one expert are contiguous, ordered
-// (quad, chunk) with the chunk fastest.  The other workgroups write the f16
+// lists: an expert of n tokens has n / 128 full chunks (M = 8) and, when
+// n % 128 > 0, one last chunk of M = ceil((n % 128) / 16) subtiles; every
+// chunk is qg gate/up and qd down items, one per row quad.  The lists hold the
+// M = 8 chunks first, then the last chunks by descending M, so workgroups
+// running side by side mostly execute the same code (each M is its own
+// unrolled loop; a last chunk of M = 8 follows the full ones); inside a
+// group the experts are in ascending order, and each chunk's q items (one per
+// row quad) are consecutive.  The other workgroups write the f16
 // codes of the Q8 activations in the piece order the MFMA operands read:
-// piece 2h + m of block b holds columns 16h + 8m + {0, 2, 4, 6, 1, 3, 5, 7},
-// the columns 4, 6, 5, 7 of each eight as q / 16 (exact in f16).
+// piece g of block b holds columns 8g + {0, 2, 4, 6, 1, 3, 5, 7}, the columns
+// 4, 6, 5, 7 of each eight as q / 16 (exact in f16).
 struct FrontArgs {
   const int32_t* counts;
   const int32_t* n_active;
@@ -673,55 +668,86 @@ struct FrontArgs {
   int64_t T, D;
 };
 
+// Exclusive prefix over the workgroup of v (256 threads); *total = the sum.
+__device__ __forceinline__ int wg_exclusive(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(x, off);
+    if (lane >= off) x += u;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// nc chunks c0 .. c0 + nc - 1 of expert e from chunk position pos, q row
+// quads each: items (e | quad << 16, chunk), chunk-major; one wavefront.
+__device__ __forceinline__ void emit_items(int2* items, int q, int pos, int e, int c0, int nc,
+                                           int lane) {
+  for (int i = lane; i < nc * q; i += kWave)
+    items[(size_t)pos * q + i] = make_int2(e | ((i % q) << 16), c0 + i / q);
+}
+
 __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
   if (blockIdx.x == 0) {
-    __shared__ int pre[512 + 1];
-    __shared__ int act[512];
     __shared__ int wsum[4];
+    __shared__ int4 plan[512];   // per active expert: e, full chunks, their position, last's
     const int nact = *a.n_active;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    // active experts and their chunk counts, two per thread
-    const int e0 = 2 * t < nact ? a.active[2 * t] : 0;
-    const int e1 = 2 * t + 1 < nact ? a.active[2 * t + 1] : 0;
-    const int n0 = 2 * t < nact ? a.counts[e0] : 0;
-    const int n1 = 2 * t + 1 < nact ? a.counts[e1] : 0;
-    act[2 * t] = e0;
-    act[2 * t + 1] = e1;
-    const int c0 = (n0 + kChunk - 1) / kChunk, c1 = (n1 + kChunk - 1) / kChunk;
-    int v = c0 + c1;   // inclusive scan of the pair sums across the workgroup
+    // two active experts per thread: full chunks f, last-chunk subtiles m
+    int e[2], f[2], m[2];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(v, off);
-      if (lane >= off) v += u;
+    for (int i = 0; i < 2; ++i) {
+      const int s = 2 * t + i;
+      e[i] = s < nact ? a.active[s] : 0;
+      const int n = s < nact ? a.counts[e[i]] : 0;
+      f[i] = n / kChunk;
+      m[i] = (n % kChunk + kSub - 1) / kSub;
     }
-    if (lane == 63) wsum[wave] = v;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    const int excl = base + v - (c0 + c1);
-    pre[2 * t] = excl;
-    pre[2 * t + 1] = excl + c0;
-    if (t == 255) pre[512] = base + v;
-    __syncthreads();
-    const int chunks = pre[512];
+    int g8;
+    const int p8 = wg_exclusive(f[0] + f[1], wsum, &g8);
+    int start = g8;          // first chunk position of the current M group
+    int last[2] = {-1, -1};  // chunk position of each expert's last chunk
+#pragma unroll 1
+    for (int mm = kMaxSub; mm >= 1; --mm) {   // a last chunk of 113..127 tokens has M = 8
+      int gm;
+      const int r = wg_exclusive((m[0] == mm) + (m[1] == mm), wsum, &gm);
+      if (m[0] == mm) last[0] = start + r;
+      if (m[1] == mm) last[1] = start + r + (m[0] == mm);
+      start += gm;
+    }
+    plan[2 * t] = make_int4(e[0], f[0], p8, last[0]);
+    plan[2 * t + 1] = make_int4(e[1], f[1], p8 + f[0], last[1]);
     if (t == 0) {
-      a.totals[0] = chunks * a.qg;
-      a.totals[1] = chunks * a.qd;
+      a.totals[0] = start * a.qg;
+      a.totals[1] = start * a.qd;
     }
+    __syncthreads();
     for (int s = wave; s < nact; s += 4) {
-      const int e = act[s];
-      const int c = pre[s + 1] - pre[s];
-      for (int i = lane; i < c * a.qg; i += kWave)
-        a.gu_items[pre[s] * a.qg + i] = make_int2(e | ((i / c) << 16), i % c);
-      for (int i = lane; i < c * a.qd; i += kWave)
-        a.dn_items[pre[s] * a.qd + i] = make_int2(e | ((i / c) << 16), i % c);
+      const int4 pl = plan[s];
+      emit_items(a.gu_items, a.qg, pl.z, pl.x, 0, pl.y, lane);
+      emit_items(a.dn_items, a.qd, pl.z, pl.x, 0, pl.y, lane);
+      if (pl.w >= 0) {
+        emit_items(a.gu_items, a.qg, pl.w, pl.x, pl.y, 1, lane);
+        emit_items(a.dn_items, a.qd, pl.w, pl.x, pl.y, 1, lane);
+      }
     }
     return;
   }
   const int64_t pieces = a.T * (a.D / 32) * 4;
   const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
   for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < pieces; i += stride) {
-    // piece i = (token, block, 2h + m): source columns 16h + 8m .. + 7 of the block
+    // piece i = (token, block, g): source columns 8g .. 8g + 7 of the block
     const int64_t col0 = (i >> 2) * 32 + (i & 3) * 8;
     const uint2 src = *reinterpret_cast<const uint2*>(a.xq + col0);
     const int8_t* c = reinterpret_cast<const int8_t*>(&src);
@@ -741,8 +767,10 @@ __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
 }  // namespace
 
 bool mfma_path_fits(int64_t T, int64_t D, int64_t F, int k, int S) {
-  const int64_t P = T * (int64_t)(k + S);
-  return T * D * 2 < 0x7FFFFFFFll && P * F * 2 < 0x7FFFFFFFll && D % 64 == 0 && F % 32 == 0;
+  (void)T;
+  (void)k;
+  (void)S;
+  return D % 64 == 0 && F % 32 == 0;
 }
 
 bool grouped_applies(const coli_expert_table& t, int64_t T, int k) {
@@ -784,56 +812,61 @@ hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t 
                            hipStream_t s) {
   const int E = t.n_routed, S = t.n_shared;
   const int64_t max_chunks = mfma_max_chunks(T, k, E, S);
-  GuArgs g = {};
-  g.gu_q = reinterpret_cast<const u32x4*>(t.gu_q);
-  g.gu_s = t.gu_s;
-  g.xh = reinterpret_cast<const u32x4*>(ws.xh);
-  g.xd = xd;
+  GArgs g = {};
+  g.wq = reinterpret_cast<const u32x4*>(t.gu_q);
+  g.ws = t.gu_s;
+  g.tok = reinterpret_cast<const uint4*>(ws.xh);
+  g.tokd = xd;
   g.counts = ws.counts;
   g.lists = ws.lists;
   g.items = reinterpret_cast<const int2*>(ws.gu_items);
   g.total = ws.totals;
-  g.h16 = reinterpret_cast<uint32_t*>(ws.h16);
-  g.hd = ws.hd;
-  g.hq = tr ? ws.hq : nullptr;
   g.T = T;
   g.D = t.d_model;
   g.F = t.d_ff;
-  g.k = k;
-  g.S = S;
-  DnArgs d = {};
-  d.dn_q = reinterpret_cast<const u32x4*>(t.dn_q);
-  d.dn_s = t.dn_s;
-  d.h16 = reinterpret_cast<const u32x4*>(ws.h16);
-  d.hd = ws.hd;
-  d.counts = ws.counts;
-  d.lists = ws.lists;
+  g.NB = (int)(t.d_model / 32);
+  g.RG = (int)(t.d_ff / 32);
+  g.KS = k + S;
+  g.row_div = k + S;
+  g.Q = mfma_quads_gate_up(t.d_ff);
+  g.h16 = reinterpret_cast<uint32_t*>(ws.h16);
+  g.hd = ws.hd;
+  g.hq = tr ? ws.hq : nullptr;
+  GArgs d = g;
+  d.wq = reinterpret_cast<const u32x4*>(t.dn_q);
+  d.ws = t.dn_s;
+  d.tok = reinterpret_cast<const uint4*>(ws.h16);
+  d.tokd = ws.hd;
   d.items = reinterpret_cast<const int2*>(ws.dn_items);
   d.total = ws.totals + 1;
+  d.NB = (int)(t.d_ff / 32);
+  d.RG = (int)(t.d_model / 64);
+  d.row_div = 1;
+  d.Q = mfma_quads_down(t.d_model);
+  d.h16 = nullptr;
+  d.hd = nullptr;
+  d.hq = nullptr;
   d.o = ws.o;
-  d.T = T;
-  d.D = t.d_model;
-  d.F = t.d_ff;
-  d.k = k;
-  d.S = S;
-  const unsigned grid_gu = (unsigned)((max_chunks * mfma_quads_gate_up(t.d_ff) + 7) / 8 * 8);
-  const unsigned grid_dn = (unsigned)((max_chunks * mfma_quads_down(t.d_model) + 7) / 8 * 8);
+  // enough workgroups for ceil(chunks / 8) chunks on each XCD (see locate)
+  const int64_t per_xcd = (max_chunks + 7) / 8;
+  const unsigned grid_gu = (unsigned)(per_xcd * 8 * mfma_quads_gate_up(t.d_ff));
+  const unsigned grid_dn = (unsigned)(per_xcd * 8 * mfma_quads_down(t.d_model));
   if (tr) {
-    g.tr_pg = tr->p_gate;
-    g.tr_pu = tr->p_up;
+    g.tr_p0 = tr->p_gate;
+    g.tr_p1 = tr->p_up;
     g.tr_g = tr->g;
     g.tr_u = tr->u;
     g.tr_h = tr->h;
-    d.tr_pd = tr->p_down;
-    hipLaunchKernelGGL(mfma_gate_up_kernel<true>, dim3(grid_gu), dim3(256), 0, s, g);
+    d.tr_p0 = tr->p_down;
+    hipLaunchKernelGGL((mfma_ffn_kernel<false, true>), dim3(grid_gu), dim3(256), 0, s, g);
   } else {
-    hipLaunchKernelGGL(mfma_gate_up_kernel<false>, dim3(grid_gu), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((mfma_ffn_kernel<false, false>), dim3(grid_gu), dim3(256), 0, s, g);
   }
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess) return rc;
   if (ev_down && (rc = hipEventRecord(static_cast<hipEvent_t>(ev_down), s)) != hipSuccess) return rc;
-  if (tr) hipLaunchKernelGGL(mfma_down_kernel<true>, dim3(grid_dn), dim3(256), 0, s, d);
-  else hipLaunchKernelGGL(mfma_down_kernel<false>, dim3(grid_dn), dim3(256), 0, s, d);
+  if (tr) hipLaunchKernelGGL((mfma_ffn_kernel<true, true>), dim3(grid_dn), dim3(256), 0, s, d);
+  else hipLaunchKernelGGL((mfma_ffn_kernel<true, false>), dim3(grid_dn), dim3(256), 0, s, d);
   return hipGetLastError();
 }
 

@@ -247,6 +247,8 @@ def test_path_choice_host():
     assert path(t, 13) == coli.COLI_PATH_GEMV
     assert path(t, 14) == coli.COLI_PATH_GROUPED
     assert path(t, 2048) == coli.COLI_PATH_GROUPED
+    # no size limit on the grouped path: 2^17 tokens (1.2 M pairs) stay grouped
+    assert path(t, 1 << 17) == coli.COLI_PATH_GROUPED
     assert path(_table(256, 1, 6144, 2048, bits=8), 2048) == coli.COLI_PATH_GEMV   # int8
     assert path(_table(256, 1, 6144, 2048, slots=64, slot_of=FAKE), 2048) == coli.COLI_PATH_GEMV
     assert path(t, 4, 0) == coli.COLI_E_SHAPE
