@@ -159,26 +159,63 @@ def test_tiny_block_stack_batched(tiny_stack, T):
     assert_bitexact(f"block h after 40 layers, {T} tokens", got, ref)
 
 
-def test_page_shape_stack_sampled():
-    """40 page-shape layers (194 GB of tables) on the GPU for 2 tokens; the
-    oracle recomputes layers 0, 1, 20 and 39 from the GPU's input to them."""
+def test_page_shape_stack_full():
+    """8 tokens through all 40 page-shape layers (194 GB of tables), one token
+    per pass through coli_moe_block, as the benchmark runs the deep stack
+    (also captured in a HIP graph and replayed), against the oracle's own
+    40-layer stack from the same h0, every layer's output bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
     w = DEEP
+    n = 8
     tables = [build_table(w, layer) for layer in range(w.layers)]
-    check = (0, 1, 20, 39)
-    keep = set(check) | {c - 1 for c in check if c > 0}
-    h0 = synth.hidden0(w, 2)
-    for t in range(2):
-        stack = GpuStack(w, tables, 1)
-        final, kept = stack.run(h0[t:t + 1], t, keep=keep)
-        assert np.isfinite(final).all()
-        for layer in check:
-            hin = h0[t:t + 1] if layer == 0 else kept[layer - 1]
-            ref, _ = oracle_layer(w, OracleExperts(w, layer), hin, layer, t)
-            assert_bitexact(f"token {t} layer {layer}", kept[layer], ref)
-        # the fused block entry point gives the same stack bit for bit
-        bfinal, bkept = BlockStack(w, tables, 1).run(h0[t:t + 1], t, keep=keep)
-        assert_bitexact(f"token {t} block stack, final h", bfinal, final)
-        for layer in sorted(keep):
-            assert_bitexact(f"token {t} block stack, layer {layer}", bkept[layer], kept[layer])
-    del tables
+    h0 = synth.hidden0(w, n)
+    every = set(range(w.layers))
+    got = []
+    for t in range(n):
+        final, kept = BlockStack(w, tables, 1).run(h0[t:t + 1], t, keep=every)
+        got.append(kept)
+    # the same stack captured in one graph (all tokens, all layers) and replayed
+    lg = [to_dev(synth.logits(w, n, 0, layer)) for layer in range(w.layers)]
+    bias = [to_dev(synth.router_bias(w, layer)) for layer in range(w.layers)]
+    hg = to_dev(h0)
+    ws = torch.empty(coli.coli_moe_layer_workspace_bytes(tables[0], 1, w.k), dtype=torch.uint8,
+                     device=dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(n):
+            for layer in range(w.layers):
+                coli.coli_moe_block(tables[layer], hg[t:t + 1], lg[layer][t:t + 1], bias[layer],
+                                    w.k, ws, eps=EPS)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert coli.coli_moe_status(ws) == coli.COLI_OK
+    hgraph = hg.cpu().numpy()
+    del graph, tables
     torch.cuda.empty_cache()
+    # the oracle: routing does not depend on h (synthetic logits), so each
+    # layer's experts are known up front and generated in a pool, one layer
+    # ahead of the layer being computed
+    idxs = [oracle.route(synth.logits(w, n, 0, layer), synth.router_bias(w, layer), w.k)[0]
+            for layer in range(w.layers)]
+
+    def experts_of(layer):
+        ox = OracleExperts(w, layer)
+        need = sorted(set(int(e) for e in idxs[layer].reshape(-1)) | {w.E})
+        with ThreadPoolExecutor(4) as pool:
+            list(pool.map(lambda e: ox[e], need))
+        return ox
+
+    h = h0.copy()
+    with ThreadPoolExecutor(1) as ahead:
+        nxt = ahead.submit(experts_of, 0)
+        for layer in range(w.layers):
+            ox = nxt.result()
+            if layer + 1 < w.layers:
+                nxt = ahead.submit(experts_of, layer + 1)
+            h, idx = oracle_layer(w, ox, h, layer, 0)
+            assert np.array_equal(idx, idxs[layer])
+            for t in range(n):
+                assert_bitexact(f"token {t} after layer {layer}", got[t][layer], h[t:t + 1])
+            if layer % 10 == 9:
+                print(f"deep stack: {layer + 1} of {w.layers} layers bit-exact", flush=True)
+    assert_bitexact("graph replay, h after 40 layers", hgraph, h)

@@ -243,23 +243,34 @@ def test_verify_layer_traced(big):
     assert_within_tol("y", g["y"], r["y"], r["absterm"])
 
 
-def test_prefill_layer_sampled(big):
-    """2048 tokens in one pass; the oracle recomputes a sample of tokens."""
-    table, ox = big
+def _prefill_full(table, ox, bias_free):
+    """Every token of the 2048-token pass, as the benchmark runs it (one
+    coli_moe_layer call: fused Q8 + routing front, dispatch, grouped matrix-core
+    kernels, combine), against the oracle on all 2048 tokens."""
     w = synth.WORKLOADS[3]
-    T = 2048
+    T = w.T
     x, lg, b = synth.activations(w, T), synth.logits(w, T), synth.router_bias(w)
-    g = GpuLayer(table, w, T).run(x, lg, b)
+    if bias_free:
+        b = np.zeros_like(b)
+    assert coli.coli_moe_path(table, T, w.k) == coli.COLI_PATH_GROUPED
+    g = run_layer(table, w, x, lg, b)
     xq, xd = oracle.q8_quant(x)
     idx, wt = oracle.route(lg, b, w.k)
-    assert_bitexact("xq", g["xq"], xq)
-    assert_bitexact("idx", g["idx"], idx)
-    assert_bitexact("w", g["w"], wt)
-    sample = [0, 1, 777, 2047]
-    ys, A = oracle.moe_layer(ox.table_for(idx[sample]), w.E, w.S, xq[sample], xd[sample],
-                             idx[sample], wt[sample])
-    assert_bitexact("y sample", g["y"][sample], ys)
-    assert_within_tol("y sample", g["y"][sample], ys, A)
+    print(f"prefill full ({'bias 0' if bias_free else 'bias N(0,0.1)'}): GPU done, oracle on "
+          f"{T} tokens", flush=True)
+    ry, A = oracle.moe_layer(ox.table_for(idx), w.E, w.S, xq, xd, idx, wt)
+    counts = np.bincount(idx.reshape(-1), minlength=w.E)
+    # the busiest experts span many 128-token work items and end in a partial one
+    assert counts.max() > 3 * 128 and counts.max() % 128 != 0
+    assert_bitexact("y, all 2048 tokens", g["y"], ry)
+    assert_within_tol("y, all 2048 tokens", g["y"], ry, A)
+
+
+def test_prefill_layer_full(big):
+    """2048 tokens, router bias N(0, 0.1): 185 experts, up to 610 tokens each."""
+    table, ox = big
+    _prefill_full(table, ox, bias_free=False)
+    ox.cache.clear()
 
 
 # ---------------------------------------------------------------- coli_moe_layer (fused front)
