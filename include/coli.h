@@ -386,6 +386,24 @@ int coli_moe_block(const coli_expert_table* table, float* h, const float* logits
                    const float* bias, int64_t T, int32_t k, float routed_scale, float eps,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* coli_moe_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same result bit for bit.
+ * The workspace is a file-scope device array of COLI_NOALLOC_BYTES
+ * (64 MiB) that each GPU the library runs on holds until the process ends;
+ * the call allocates and frees nothing.  A call needing more than that
+ * (coli_moe_layer_workspace_bytes(table, T, k) > COLI_NOALLOC_BYTES; at
+ * d_model 6144, d_ff 2048, top-8 with a shared expert: above 221 tokens)
+ * returns COLI_E_WORKSPACE before any launch.  Resident tables only
+ * (slot_of == NULL, else COLI_E_INVAL): with the routing inside the call no
+ * index error can arise, so no status needs reading back.  Every call on one
+ * GPU uses the same array: calls on one stream are ordered, but calls that
+ * overlap on one GPU (other streams, other threads) race. */
+#define COLI_NOALLOC_BYTES 67108864 /* 64 MiB */
+int coli_moe_layer_noalloc(const coli_expert_table* table, const float* x, const float* logits,
+                           const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                           int accumulate, void* stream);
+
 /* Synchronises `stream`, then reports the device-side checks of the last
  * forward or layer call that used `workspace`: COLI_OK, COLI_E_INDEX or
  * COLI_E_TIER. */

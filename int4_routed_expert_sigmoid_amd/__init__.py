@@ -26,6 +26,7 @@ COLI_E_INDEX = -6
 COLI_E_TIER = -7
 COLI_PATH_AUTO, COLI_PATH_GEMV, COLI_PATH_GROUPED = 0, 1, 2
 COLI_GROUPED_MIN_TOKENS = 14
+COLI_NOALLOC_BYTES = 64 << 20
 COLI_MAX_EXPERTS = 256
 COLI_MAX_TOPK = 64
 COLI_MAX_DIM = 32768
@@ -38,6 +39,7 @@ EXPORTED = [
     "coli_moe_forward", "coli_moe_forward_traced", "coli_moe_forward_profiled",
     "coli_moe_forward_path", "coli_moe_path",
     "coli_moe_layer_workspace_bytes", "coli_moe_layer", "coli_moe_layer_ex", "coli_moe_block",
+    "coli_moe_layer_noalloc",
     "coli_moe_status", "coli_status_string", "coli_last_hip_error",
     "coli_tier_table_bytes", "coli_tier_init", "coli_tier_plan", "coli_tier_fetch",
     "coli_tier_status", "coli_tier_rank",
@@ -121,6 +123,8 @@ def lib():
                                    _P, sz, _P, _P, _P], ctypes.c_int),
             "coli_moe_block": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, ctypes.c_float, _P,
                                 sz, _P], ctypes.c_int),
+            "coli_moe_layer_noalloc": ([_P, _P, _P, _P, _I64, _I32, ctypes.c_float, _P,
+                                        ctypes.c_int, _P], ctypes.c_int),
             "coli_moe_status": ([_P, sz, _P], ctypes.c_int),
             "coli_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "coli_tier_table_bytes": ([_I32, _I64, _I64, _I32, _P, _P, _P, _P], sz),
@@ -448,6 +452,18 @@ def coli_moe_block(table: ExpertTable, h, logits, bias, k, workspace, eps=1e-6,
            lib().coli_moe_block(table.ref(), _ptr(h), _ptr(logits), _ptr(bias), h.shape[0], k,
                                 routed_scale, eps, _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def coli_moe_layer_noalloc(table: ExpertTable, x, logits, bias, k, y, routed_scale=1.0,
+                           accumulate=False, stream=None):
+    """coli_moe_layer on the library's own device scratch (no workspace argument)."""
+    import torch
+    _dtype(x, torch.float32, "x"); _dtype(logits, torch.float32, "logits")
+    _dtype(bias, torch.float32, "bias"); _dtype(y, torch.float32, "y")
+    _check("coli_moe_layer_noalloc",
+           lib().coli_moe_layer_noalloc(table.ref(), _ptr(x), _ptr(logits), _ptr(bias), x.shape[0],
+                                        k, routed_scale, _ptr(y), int(bool(accumulate)),
+                                        _stream(stream)))
 
 
 def coli_moe_status(workspace, stream=None) -> int:

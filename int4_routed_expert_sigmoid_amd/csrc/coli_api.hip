@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "coli_internal.h"
 
@@ -487,6 +488,56 @@ int coli_moe_layer(const coli_expert_table* table, const float* x, const float* 
                    int accumulate, void* workspace, size_t ws_bytes, void* stream) {
   return coli_moe_layer_ex(table, x, logits, bias, T, k, routed_scale, y, accumulate, workspace,
                            ws_bytes, nullptr, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free layer: coli_moe_layer with its workspace in a file-scope
+// device array instead of a caller's buffer.  Each device holds its own copy
+// of the array (loaded with the code object, kept until the process ends);
+// host code reaches it only through the device address hipGetSymbolAddress
+// gives on that device, looked up once per device.
+namespace {
+
+constexpr size_t kNoAllocBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];   // device address of `scratch` per device (null: not looked up)
+
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return COLI_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return COLI_E_DEVICE;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return COLI_OK;
+}
+
+}  // namespace
+
+int coli_moe_layer_noalloc(const coli_expert_table* table, const float* x, const float* logits,
+                           const float* bias, int64_t T, int32_t k, float routed_scale, float* y,
+                           int accumulate, void* stream) {
+  int rc = table_check(table);
+  if (rc) return rc;
+  if (table->slot_of) return COLI_E_INVAL;   // resident tables only (see coli.h)
+  if (k < 1 || k > table->n_routed || k > COLI_MAX_TOPK || T < 0) return COLI_E_SHAPE;
+  if (T * (int64_t)(k + table->n_shared) > 0x7FFFFFFF) return COLI_E_SHAPE;
+  if (coli_moe_layer_workspace_bytes(table, T, k) > kNoAllocBytes) return COLI_E_WORKSPACE;
+  if (T == 0) return COLI_OK;
+  if ((rc = check_device())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_on_current_device(&ws))) return rc;
+  return layer_impl(table, x, logits, bias, T, k, routed_scale, y, accumulate, ws, kNoAllocBytes,
+                    nullptr, nullptr, false, 0.0f, stream);
 }
 
 int coli_moe_status(const void* workspace, size_t ws_bytes, void* stream) {
