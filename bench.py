@@ -34,6 +34,11 @@ HBM_PEAK_GBPS = 8000.0
 # (profiles/decode_gate_up_hbm_traffic.md); valid for the kernel as measured there.
 GATE_UP_TRAFFIC_BYTES = 113_782_374
 INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of MI355X
+F16_PEAK_TFLOPS = 2500.0  # dense f16 matrix-core peak of MI355X
+# fp32 FMAs per second of the vector ALUs without packed instructions: 256 CUs x
+# 64 lanes x 2.4 GHz (the 157.3 TFLOP/s vector peak counts packed FMAs, 128 per CU
+# per clock, at 2 flops each)
+VALU_FMA_PEAK_T = 256 * 64 * 2.4e9 / 1e12
 METRIC = "MoE-layer decode tok/s + achieved HBM GB/s (int4 experts); prefill int8 TOPS"
 
 
@@ -122,15 +127,140 @@ def cpu_baseline(w, synth, seconds):
     return {"value": tokens / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{len(sample)} decode tokens of the same layer (their {len(experts)} "
                       f"experts generated and quantised untimed), cycled for {el:.1f} s "
-                      f"({tokens} token-layers); quantise+route+MoE per token"}
+                      f"({tokens} token-layers); quantise+route+MoE per token",
+            "host": host_description(),
+            "context": PAGES_CPU_CONTEXT}
 
 
-def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
-    """2048 tokens through the same layer in one coli_moe_layer call (the
+# The pages' own CPU figures (context only; other machines, whole-model decode
+# for the tok/s figures): jeff.news kernel section (int8 matmul on AVX2),
+# discuss.pytorch.kr "colibri의 성능" table (cold decode on the 25 GB WSL2
+# laptop), and the Apple M5 Max decode figure quoted there.
+PAGES_CPU_CONTEXT = {
+    "int8_matmul_avx2_gflops": 119,
+    "cold_decode_tok_s_wsl2_laptop": [0.05, 0.1],
+    "decode_tok_s_m5_max": 1.06,
+}
+
+
+def host_description():
+    """nproc, the CPU model and the RAM of the host the oracle runs on."""
+    model, ram_kb = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    ram_kb = int(line.split()[1])
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model, "ram_gib": round(ram_kb / 2**20, 1)}
+
+
+def cpu_full(synth, seconds=5.0):
+    """The oracle on every workload at all threads and at one thread (a
+    reported baseline; expert generation and quantisation untimed).  Decode
+    and verify tokens are cycled for `seconds`; the 2048-token prefill runs in
+    full at all threads and on its first 64 tokens at one thread; the 40-layer
+    stack runs 8 tokens (all threads) or 1 token (one thread) through all 40
+    layers.  Sampled rates are extrapolated to the whole workload and say so."""
+    import oracle
+    res = {"host": host_description(), "context": PAGES_CPU_CONTEXT, "runs": []}
+    all_threads = oracle.num_threads()
+
+    def experts_for(w, layer, idx):
+        need = sorted(set(int(e) for e in idx.reshape(-1)) | {w.E})
+        return {e: oracle.Expert.quantize(*[synth.weight_host(w, layer, e, m) for m in range(3)])
+                for e in need}
+
+    def layer_tokens(w, T, seed=0):
+        x, lg, b = synth.activations(w, T, seed), synth.logits(w, T, seed), synth.router_bias(w)
+        xq, xd = oracle.q8_quant(x)
+        idx, wt = oracle.route(lg, b, w.k)
+        return xq, xd, idx, wt
+
+    def note(r):
+        res["runs"].append(r)
+        print(f"cpu_full: {r['workload']}, {r['threads']} threads: {r['seconds']} s", file=sys.stderr,
+              flush=True)
+
+    expert_bytes_w = sum(expert_bytes(synth.WORKLOADS[1]))
+    macs_per_pair = 3 * synth.WORKLOADS[1].D * synth.WORKLOADS[1].F
+    for threads in (all_threads, 1):
+        oracle.set_threads(threads)
+        # decode (1 token per layer call) and verify (4 tokens in one call)
+        for wl, T in ((1, 1), (2, 4)):
+            w = synth.WORKLOADS[wl]
+            xq, xd, idx, wt = layer_tokens(w, 4)
+            ex = experts_for(w, 0, idx)
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < seconds:
+                for t0k in range(0, 4, T):
+                    oracle.moe_layer(ex, w.E, w.S, xq[t0k:t0k + T], xd[t0k:t0k + T],
+                                     idx[t0k:t0k + T], wt[t0k:t0k + T])
+                    n += T
+            el = time.perf_counter() - t0
+            note({"workload": w.name, "threads": threads, "tokens": n,
+                                "seconds": round(el, 2), "tok_s": round(n / el, 2),
+                                "int_ops_per_s": round(n * (w.k + w.S) * 2 * macs_per_pair / el, 1),
+                                "weight_gb_s": round(n * (w.k + w.S) * expert_bytes_w / el / 1e9, 3)})
+        # prefill: 2048 tokens (first 64 at one thread)
+        w = synth.WORKLOADS[3]
+        xq, xd, idx, wt = layer_tokens(w, w.T)
+        Tn = w.T if threads > 1 else 64
+        ex = experts_for(w, 0, idx[:Tn])
+        t0 = time.perf_counter()
+        oracle.moe_layer(ex, w.E, w.S, xq[:Tn], xd[:Tn], idx[:Tn], wt[:Tn])
+        el = time.perf_counter() - t0
+        del ex
+        r = {"workload": w.name, "threads": threads, "tokens": Tn, "seconds": round(el, 2),
+             "tok_s": round(Tn / el, 2),
+             "int_ops_per_s": round(Tn * (w.k + w.S) * 2 * macs_per_pair / el, 1)}
+        if Tn < w.T:
+            r["extrapolated_ms_per_pass"] = round(el / Tn * w.T * 1000, 1)
+            r["note"] = f"first {Tn} of {w.T} tokens timed; the pass time is extrapolated"
+        else:
+            r["ms_per_pass"] = round(el * 1000, 1)
+        note(r)
+        # deep stack: 8 tokens (1 at one thread) through all 40 layers
+        w = synth.WORKLOADS[4]
+        n = 8 if threads > 1 else 1
+        h = synth.hidden0(w, n)
+        el = 0.0
+        for layer in range(w.layers):
+            idx, wt = oracle.route(synth.logits(w, n, 0, layer), synth.router_bias(w, layer), w.k)
+            ex = experts_for(w, layer, idx)   # untimed
+            t0 = time.perf_counter()
+            xh, _ = oracle.rmsnorm(h, 1e-6)
+            xq, xd = oracle.q8_quant(xh)
+            h, _ = oracle.moe_layer(ex, w.E, w.S, xq, xd, idx, wt, out=h, accumulate=True)
+            el += time.perf_counter() - t0
+            del ex
+            if layer % 8 == 7:
+                print(f"cpu_full: deep stack, {threads} threads, layer {layer + 1}", file=sys.stderr,
+                      flush=True)
+        note({"workload": w.name, "threads": threads, "tokens": n,
+                            "seconds": round(el, 2), "ms_per_token": round(el / n * 1000, 1),
+                            "tok_s": round(n / el, 3),
+                            "extrapolated_s_for_256_tokens": round(el / n * w.steps, 1),
+                            "note": f"{n} of {w.steps} tokens through all {w.layers} layers "
+                                    f"timed; the 256-token time is extrapolated"})
+    oracle.set_threads(all_threads)
+    return res
+
+
+def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False, T=None):
+    """2048 tokens (or T) through the same layer in one coli_moe_layer call (the
     grouped matrix-core path): pass time, int8-equivalent TOPS of the expert
-    matmuls, and the per-stage split measured with HIP events."""
+    matmuls, the per-stage split measured with HIP events, and the roofline of
+    the two matrix kernels against the VALU roof of the exact Q8_0 rescale."""
     w = synth.WORKLOADS[3]
-    T = w.T
+    T = T or w.T
     x = torch.from_numpy(synth.activations(w, T)).cuda()
     lg = torch.from_numpy(synth.logits(w, T)).cuda()
     b = torch.from_numpy(synth.router_bias(w)).cuda()
@@ -176,8 +306,14 @@ def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
     ops_dn = 2.0 * pairs * w.D * w.F
     tops = (ops_gu + ops_dn) / (ms * 1e-3) / 1e12
     used = int((counts > 0).sum())
+    # the exact Q8_0 path costs one fp32 fmaf per (row, pair, 32-column block)
+    rescale = pairs * (2 * w.F * (w.D // 32) + w.D * (w.F // 32))
+    mm_ms = gu_ms + dn_ms
+    fma_rate = rescale / (mm_ms * 1e-3) / 1e12
+    mm_tops = (ops_gu + ops_dn) / (mm_ms * 1e-3) / 1e12
+    name = w.name if T == w.T else w.name.replace(f"t{w.T}", f"t{T}")
     return {
-        "workload": w.name + (" (router bias 0)" if bias_free else ""),
+        "workload": name + (" (router bias 0)" if bias_free else ""),
         "tokens": T, "experts_used": used + w.S, "max_tokens_per_expert": int(counts.max()),
         "ms_per_pass": round(ms, 4), "tok_s": round(T / (ms * 1e-3), 1),
         "int8_tops": round(tops, 1), "int8_peak_tops": INT8_PEAK_TOPS,
@@ -187,7 +323,58 @@ def prefill_leg(table, coli, synth, torch, hev, steps, warmup, bias_free=False):
         "gate_up_tops": round(ops_gu / (gu_ms * 1e-3) / 1e12, 1),
         "down_tops": round(ops_dn / (dn_ms * 1e-3) / 1e12, 1),
         "weight_gbps": round((used + w.S) * sum(expert_bytes(w)) / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "mfma_ffn_kernel (gate/up + down)", "bound": "alu",
+                     "achieved": round(fma_rate, 2), "peak": VALU_FMA_PEAK_T,
+                     "unit": "T fp32 fmaf/s (exact Q8_0 rescale, unpacked)",
+                     "frac": round(fma_rate / VALU_FMA_PEAK_T, 4),
+                     "matrix_tops": round(mm_tops, 1),
+                     "frac_of_f16_mfma_peak": round(mm_tops / F16_PEAK_TFLOPS, 4),
+                     "frac_of_int8_mfma_peak": round(mm_tops / INT8_PEAK_TOPS, 4),
+                     "rescale_fmas": rescale},
     }
+
+
+def decode_cold_leg(step, pool, torch, layer_bytes, tokens=32, reps=4, flush_bytes=512 << 20):
+    """Decode steps with a cold Infinity Cache.  Before each step a 512 MiB
+    buffer is written, so no expert's rows are left in the 256 MB Infinity
+    Cache (the shared expert, which every warm step re-reads 170 MB after its
+    last use, included).  Three HIP graphs of `tokens` steps are replayed back
+    to back, as the headline steps are: writes + steps, the writes alone, and
+    the steps alone; the cold step time is (writes + steps - writes) / tokens,
+    so the writes stay outside it."""
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+
+    def graph(with_flush, with_steps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(tokens):
+                if with_flush:
+                    flush.fill_(float(j + 1))   # a fill kernel (nonzero value)
+                if with_steps:
+                    step(j % pool)
+        return g
+
+    gs = {"cold": graph(True, True), "flush": graph(True, False), "warm": graph(False, True)}
+
+    def timed(g):
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t = {k: timed(g) for k, g in gs.items()}
+    cold = (t["cold"] - t["flush"]) / tokens
+    warm = t["warm"] / tokens
+    del gs, flush
+    return {"tokens": tokens, "flush_bytes": flush_bytes,
+            "cold_ms_per_step": round(cold, 5), "cold_tok_s": round(1000.0 / cold, 1),
+            "cold_weight_gbps": round(layer_bytes / (cold * 1e-3) / 1e9, 1),
+            "warm_ms_per_step": round(warm, 5), "flush_ms": round(t["flush"] / tokens, 4)}
 
 
 def head_leg(coli, synth, torch, hev):
@@ -509,6 +696,10 @@ def main():
     ap.add_argument("--pool", type=int, default=64, help="distinct tokens cycled by the steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle on every workload at all threads and one thread "
+                         "(several minutes; reported under cpu_full)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode leg")
     ap.add_argument("--eager", action="store_true", help="launch steps directly, no HIP graph")
     ap.add_argument("--prefill-steps", type=int, default=20,
                     help="timed 2048-token passes of the prefill leg (0: skip it)")
@@ -668,10 +859,18 @@ def main():
         "wall_s": round(wall, 3),
         "setup_s": round(setup_s, 1),
     }
+    if not args.no_cold:
+        out["decode_cold"] = decode_cold_leg(step, P, torch, layer_bytes)
     if args.prefill_steps > 0:
         out["prefill"] = [prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3),
                           prefill_leg(table, coli, synth, torch, hev, args.prefill_steps, 3,
                                       bias_free=True)]
+        # a larger pass (about 288 tokens per used expert), labelled: the
+        # kernels' matrix-core ceiling with fewer partial work items
+        big = prefill_leg(table, coli, synth, torch, hev, max(2, args.prefill_steps // 4), 2,
+                          T=8192)
+        big["label"] = "8192-token sweep point (not a configured workload)"
+        out["prefill"].append(big)
     if not args.no_paths:
         out["paths"] = paths_leg(table, coli, synth, torch)
     verify = synth.WORKLOADS[2]
@@ -687,6 +886,8 @@ def main():
         out["deep"] = deep_leg(coli, synth, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
+    if args.cpu_full:
+        out["cpu_full"] = cpu_full(synth)
     print(json.dumps(out), flush=True)
 
 

@@ -23,6 +23,7 @@ _F = ctypes.c_float
 
 _SIG = {
     "orc_num_threads": ([], ctypes.c_int),
+    "orc_set_threads": ([ctypes.c_int], None),
     "orc_expf": ([_F], _F),
     "orc_sigmoidf": ([_F], _F),
     "orc_siluf": ([_F], _F),
@@ -129,6 +130,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.L.orc_num_threads())
+
+    def set_threads(self, n: int) -> None:
+        """OpenMP threads of the calling thread's later oracle calls."""
+        self.L.orc_set_threads(int(n))
 
     # ---------------------------------------------------------------- scalar math
     def expf(self, x: float) -> float:

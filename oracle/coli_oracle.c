@@ -47,6 +47,9 @@
 /* Threads the OpenMP loops of this library use (reported with timings). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads of the calling thread's later parallel regions (timing runs only). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ------------------------------------------------------------------------
  * exp(x) in fp32 (Cody & Waite, "Software Manual for the Elementary
  * Functions", 1980: argument reduction by n*ln2 with ln2 split in a high

@@ -22,6 +22,7 @@ extern "C" {
 
 /* OpenMP threads used by the parallel loops. */
 int orc_num_threads(void);
+void orc_set_threads(int n);
 
 /* exp / sigmoid / silu in fp32 (Cody-Waite reduction + degree-7 Taylor). */
 float orc_expf(float x);
