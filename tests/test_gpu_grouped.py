@@ -1,7 +1,7 @@
 """Parity of the grouped (matrix-core) expert path against the oracle (GPU).
 
-From COLI_GROUPED_MIN_TOKENS (14) tokens per pass the forward runs the grouped kernels: per active
-expert, chunks of up to 64 tokens against 64-row weight groups.  These tests
+From COLI_GROUPED_MIN_TOKENS (9) tokens per pass the forward runs the grouped kernels: per active
+expert, chunks of up to 128 tokens against 64-row weight groups.  These tests
 check every int32 block partial, g, u, h, Q8(h) and per-pair output
 bit-for-bit, over routings that exercise full, partial and single-token
 chunks, plus the layer output.
