@@ -102,6 +102,8 @@ MoeWorkspace moe_workspace_layout(void* base, int E, int S, int64_t D, int64_t F
   const size_t chunks = (size_t)mfma_max_chunks(T, k, E, S);
   w.xh = static_cast<uint16_t*>(take(2 * (size_t)T * (size_t)D));
   w.h16 = static_cast<uint16_t*>(take(2 * P * (size_t)F));
+  w.xbias = reinterpret_cast<float*>(w.xsum8);
+  w.hbias = reinterpret_cast<float*>(w.hsum8);
   w.gu_items = static_cast<int32_t*>(take(8 * chunks * (size_t)mfma_quads_gate_up(F)));
   w.dn_items = static_cast<int32_t*>(take(8 * chunks * (size_t)mfma_quads_down(D)));
   w.totals = static_cast<int32_t*>(take(2 * sizeof(int32_t)));

@@ -197,6 +197,10 @@ struct MoeWorkspace {
   // grouped (matrix-core) path only
   uint16_t* xh;      // [T][D/32][32] f16 codes of xq in MFMA operand order
   uint16_t* h16;     // [P][F/32][32] f16 codes of Q8(h) in MFMA operand order
+  // accumulator inputs of the matrix-core operands, per Q8 block (the memory
+  // of xsum8 and hsum8, which the grouped path does not use)
+  float* xbias;      // [T][D/32]
+  float* hbias;      // [P][F/32]
   int32_t* gu_items; // [chunks * gate/up quads][2] work items
   int32_t* dn_items; // [chunks * down quads][2]
   int32_t* totals;   // [2] item counts

@@ -13,9 +13,10 @@
 //
 // Why f16 matrix cores carry the integer dot.  The int4 codes (|q| <= 7) and
 // the Q8 codes (|q| <= 127) are exact f16 values, each product is exact, and
-// every partial sum of a 32-column block is an integer below 2^15, so the
-// fp32 accumulation inside v_mfma_f32_16x16x32_f16 (K = 32 = one Q8 block) is
-// exact: it returns P[r][b] bit-for-bit, already as fp32.  The exact Q8_0
+// every partial sum of a 32-column block is an integer below 2^23 (the weight
+// operand carries an offset, cancelled through the accumulator input; see
+// nibbles_to_f16), so the fp32 accumulation inside v_mfma_f32_16x16x32_f16
+// (K = 32 = one Q8 block) is exact: it returns P[r][b] bit-for-bit, as fp32.  The exact Q8_0
 // rescale then costs one VALU fmaf per (row, token, block) and nothing else;
 // an int8 matrix core's int32 result would need a conversion first, doubling
 // that VALU stream, which is what bounds this kernel.
@@ -73,19 +74,33 @@ __device__ __forceinline__ UnpackConsts unpack_consts() {
 
 // Eight offset-binary nibbles of one table word (byte j: column j in the low
 // nibble, column 4 + j in the high nibble; nibble n = q + 8) as eight exact
-// f16 values.  A nibble OR-ed into the low mantissa bits of 1024.0 (0x6400)
-// gives 1024 + n, one OR-ed four bits higher gives 1024 + 16n; subtracting
-// 1032 or 1152 leaves q or 16q.  Element order (columns): 0, 2, 4, 6, 1, 3, 5,
-// 7, where the elements 2, 3, 6, 7 carry 16q; the token operand carries x / 16
-// in those places, so every product is exactly q * x.
+// f16 values, offset: a nibble OR-ed into the low mantissa bits of 1024.0
+// (0x6400) gives 1024 + n = q + 1032, one OR-ed four bits higher gives
+// 1024 + 16n = 16q + 1152.  Element order (columns): 0, 2, 4, 6, 1, 3, 5, 7,
+// where the elements 2, 3, 6, 7 (columns 4-7 of each eight) carry 16q + 1152;
+// the token operand carries x there as x / 16.  A block's dot product is then
+// P + 1032 SL + 72 SH, SL and SH the token's code sums over the columns 0-3
+// and 4-7 of each eight.  Either the offsets are subtracted here (OFFSET
+// false: q and 16q, two more instructions per word), or (OFFSET true)
+// -(1032 SL + 72 SH), staged with the token, is the matrix-core instruction's
+// accumulator input, so its result is P all the same.  No partial sum
+// reaches 2^23 (32 products of at most 1039 * 127, and the offset below
+// 1104 * 16 * 127), so every step of that sum is exact in fp32.
+template <bool OFFSET>
 __device__ __forceinline__ half8 nibbles_to_f16(uint32_t w, const UnpackConsts& c) {
-  const half2v b1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const half2v b16 = {(_Float16)1152.0f, (_Float16)1152.0f};
   const uint32_t w8 = w >> 8;
-  const half2v h0 = __builtin_bit_cast(half2v, (w & c.lo) | c.magic) - b1;
-  const half2v h1 = __builtin_bit_cast(half2v, (w & c.hi) | c.magic) - b16;
-  const half2v h2 = __builtin_bit_cast(half2v, (w8 & c.lo) | c.magic) - b1;
-  const half2v h3 = __builtin_bit_cast(half2v, (w8 & c.hi) | c.magic) - b16;
+  half2v h0 = __builtin_bit_cast(half2v, (w & c.lo) | c.magic);
+  half2v h1 = __builtin_bit_cast(half2v, (w & c.hi) | c.magic);
+  half2v h2 = __builtin_bit_cast(half2v, (w8 & c.lo) | c.magic);
+  half2v h3 = __builtin_bit_cast(half2v, (w8 & c.hi) | c.magic);
+  if constexpr (!OFFSET) {
+    const half2v b1 = {(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2v b16 = {(_Float16)1152.0f, (_Float16)1152.0f};
+    h0 -= b1;
+    h1 -= b16;
+    h2 -= b1;
+    h3 -= b16;
+  }
   half8 r;
   r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
   r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
@@ -109,9 +124,8 @@ __device__ __forceinline__ void tile_words(u32x4 w, uint32_t (&t)[4]) {
   t[3] = d[1];
 }
 
-__device__ __forceinline__ f32x4 mfma(half8 a, half8 b) {
-  const f32x4 z = {};
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, z, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // acc = fmaf(P, d, acc) for the four elements of a tile that a lane holds.
@@ -154,13 +168,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Arguments of both matrix kernels.  Token operands: tok [rows][NB][4] 16-byte
 // pieces of f16 codes (piece g of a block = its columns 8g .. 8g + 7 in the
-// expansion's element order), tokd [rows][NB] block scales; a list entry p
-// names row p / KS (gate/up: the token of pair p) or p (down: the pair).
+// expansion's element order), tokd [rows][NB] block scales, tokb [rows][NB]
+// the accumulator inputs -(1032 SL + 72 SH); a list entry p names row p / KS
+// (gate/up: the token of pair p) or p (down: the pair).
 struct GArgs {
   const u32x4* wq;        // [E+S][RG][NB][64] 16-byte lane chunks
   const float* ws;        // gate/up: [E+S][RG][64] lane-ordered; down: [E+S][D]
   const uint4* tok;
   const float* tokd;
+  const float* tokb;
   const int32_t* counts;
   const int32_t* lists;
   const int2* items;
@@ -171,6 +187,7 @@ struct GArgs {
   // gate/up results
   uint32_t* h16;          // [P][F/32][4 pieces][4 words]
   float* hd;              // [P][F/32]
+  float* hb;              // [P][F/32] accumulator inputs of Q8(h)
   int8_t* hq;             // [P][F] (traced runs only)
   // down result
   float* o;               // [P][D]
@@ -194,9 +211,14 @@ struct GArgs {
 // multiple of R + 1 and of 2 S, so ring positions and LDS slots are
 // compile-time constants; the block loop runs to NB rounded up to U (see
 // stream).  Each M is one copy of the unrolled loop, so U is kept small: the
-// instruction cache is shared by the workgroups of neighbouring CUs.
+// instruction cache is shared by the workgroups of neighbouring CUs.  OFFSET
+// (see nibbles_to_f16) trades two VALU instructions per weight word for one
+// 16-byte LDS read per subtile and block: it pays while the expansion is
+// shared by few subtiles, and costs once the LDS reads of the operands
+// dominate.
 template <int M>
 struct Cfg {
+  static constexpr bool OFFSET = M <= 2;
   static constexpr int S = M <= 2 ? 8 : M <= 4 ? 4 : M <= 6 ? 2 : 1;
   static constexpr int RS = M <= 4 ? 8 : 4;             // ring slots
   static constexpr int R = RS - 1;                      // blocks in flight
@@ -211,9 +233,12 @@ struct Cfg {
 // LDS of the staging: two slots of one stage each.  In block j of a stage,
 // piece g of token t sits at 16-byte slot 64 M j + 4 t + (g ^ ((t >> 1) & 3)),
 // so the 16 lanes of one operand read hit 16 different bank groups; the
-// scales are [j][16 M].  Sized for the largest stage (M S = 16).
+// scales are [j][16 M], the accumulator inputs [j][16 M] four copies each
+// (one 16-byte read fills the four accumulator registers of a lane).  Sized
+// for the largest stage (M S = 16).
 struct Stage {
   uint4 x[2][1024];
+  f32x4 k[2][256];
   float d[2][256];
 };
 
@@ -225,6 +250,7 @@ template <int M>
 struct StageSrc {
   const uint4 *x0, *x1, *x2, *x3;   // block 0 piece of the token of each share
   const float* d;                   // block 0 scale of the scale share's token
+  const float* k;                   // its block 0 accumulator input
 };
 
 // Share i of a thread (named members: they must stay in registers).
@@ -247,27 +273,27 @@ __device__ __forceinline__ uint4& pick(uint4& x0, uint4& x1, uint4& x2, uint4& x
 template <int M, int I = 0>
 __device__ __forceinline__ void stage_load(const StageSrc<M>& s, int st, int NB, int tid,
                                            uint4& x0, uint4& x1, uint4& x2, uint4& x3,
-                                           float& d) {
+                                           float& d, float& k, bool& dok) {
   using C = Cfg<M>;
   if constexpr (I < C::PT) {
     const int q = tid + 256 * I;
     int b = st * C::S + q / (64 * M);
     b = b < NB ? b : NB - 1;
     pick<I>(x0, x1, x2, x3) = share<I, const StageSrc<M>, const uint4* const>(s)[(size_t)b * 4];
-    stage_load<M, I + 1>(s, st, NB, tid, x0, x1, x2, x3, d);
+    stage_load<M, I + 1>(s, st, NB, tid, x0, x1, x2, x3, d, k, dok);
   } else {
-    // a block past the end gets scale 0: fmaf(P, 0, acc) leaves acc exactly
-    // as it is (acc is never -0: it starts at +0 and an fmaf that cancels
-    // exactly rounds to +0)
+    // a block past the end gets scale 0 (applied at the store: a use of the
+    // loaded value here would wait for every load issued before it)
     const int b = st * C::S + (tid < C::DS ? tid : 0) / (16 * M);
-    const float v = s.d[b < NB ? b : NB - 1];   // issued on every path
-    d = b < NB ? v : 0.0f;
+    d = s.d[b < NB ? b : NB - 1];   // issued on every path
+    if constexpr (C::OFFSET) k = s.k[b < NB ? b : NB - 1];
+    dok = b < NB;
   }
 }
 
 template <int M, int I = 0>
 __device__ __forceinline__ void stage_store(Stage& L, int slot, int tid, uint4& x0, uint4& x1,
-                                            uint4& x2, uint4& x3, float d) {
+                                            uint4& x2, uint4& x3, float d, float k, bool dok) {
   using C = Cfg<M>;
   if constexpr (I < C::PT) {
     const int q = tid + 256 * I;
@@ -275,9 +301,14 @@ __device__ __forceinline__ void stage_store(Stage& L, int slot, int tid, uint4& 
       const int j = q / (64 * M), rr = q % (64 * M), t = rr >> 2, g = rr & 3;
       L.x[slot][64 * M * j + 4 * t + (g ^ ((t >> 1) & 3))] = pick<I>(x0, x1, x2, x3);
     }
-    stage_store<M, I + 1>(L, slot, tid, x0, x1, x2, x3, d);
+    stage_store<M, I + 1>(L, slot, tid, x0, x1, x2, x3, d, k, dok);
   } else {
-    if (tid < C::DS) L.d[slot][tid] = d;
+    // fmaf(P, 0, acc) leaves acc exactly as it is (acc is never -0: it starts
+    // at +0 and an fmaf that cancels exactly rounds to +0)
+    if (tid < C::DS) {
+      L.d[slot][tid] = dok ? d : 0.0f;
+      if constexpr (C::OFFSET) L.k[slot][tid] = f32x4{k, k, k, k};
+    }
   }
 }
 
@@ -305,21 +336,33 @@ __device__ __forceinline__ void block_step(const Stage& L, int slot, int jst, in
 #pragma unroll
   for (int s = 0; s < M; ++s) d[s] = L.d[slot][kSub * M * jst + kSub * s + n];
   const uint4* xs = &L.x[slot][64 * M * jst + xoff];
+  constexpr bool OFS = Cfg<M>::OFFSET;
+  const f32x4* ks = &L.k[slot][kSub * M * jst + n];
   half8 B[M];
+  f32x4 K[M] = {};
   B[0] = __builtin_bit_cast(half8, xs[0]);
-  if (M > 1) B[1] = __builtin_bit_cast(half8, xs[64]);
+  if (OFS) K[0] = ks[0];
+  if (M > 1) {
+    B[1] = __builtin_bit_cast(half8, xs[64]);
+    if (OFS) K[1] = ks[kSub];
+  }
+  // the operand reads go out before the expansion, which covers their latency
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t tw[4];
   tile_words(w, tw);
   half8 A[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) A[t] = nibbles_to_f16(tw[t], uc);
+  for (int t = 0; t < 4; ++t) A[t] = nibbles_to_f16<OFS>(tw[t], uc);
 #pragma unroll
   for (int s = 0; s < M; ++s) {
-    if (s + 2 < M) B[s + 2] = __builtin_bit_cast(half8, xs[64 * (s + 2)]);
+    if (s + 2 < M) {
+      B[s + 2] = __builtin_bit_cast(half8, xs[64 * (s + 2)]);
+      if (OFS) K[s + 2] = ks[kSub * (s + 2)];
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = 4 * s + t;
-      p[i & 3] = mfma(A[t], B[s]);
+      p[i & 3] = mfma(A[t], B[s], K[s]);
       if (TRACE && tr.p[s][t] && b < NB) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) tr.p[s][t][(size_t)r * NB + b] = (int32_t)p[i & 3][r];
@@ -358,10 +401,11 @@ __device__ __forceinline__ void stream_loop(Stage& L, const GArgs& a, __amdgpu_b
     wq[j] = __builtin_amdgcn_raw_buffer_load_b128(wrs, voff + 1024u * (uint32_t)(j < NB ? j : NB - 1),
                                                   0, 0);
   uint4 r0 = {}, r1 = {}, r2 = {}, r3 = {};
-  float rd = 0.0f;
-  stage_load<M>(src, 0, NB, tid, r0, r1, r2, r3, rd);
-  stage_store<M>(L, 0, tid, r0, r1, r2, r3, rd);
-  stage_load<M>(src, 1, NB, tid, r0, r1, r2, r3, rd);
+  float rd = 0.0f, rk = 0.0f;
+  bool rok = false;
+  stage_load<M>(src, 0, NB, tid, r0, r1, r2, r3, rd, rk, rok);
+  stage_store<M>(L, 0, tid, r0, r1, r2, r3, rd, rk, rok);
+  stage_load<M>(src, 1, NB, tid, r0, r1, r2, r3, rd, rk, rok);
   __syncthreads();
   f32x4 p[4] = {};
   float dprev = 0.0f;
@@ -389,8 +433,8 @@ __device__ __forceinline__ void stream_loop(Stage& L, const GArgs& a, __amdgpu_b
         // unconditional, so that the memory-counter waits are exact: the
         // stores past the last stage go to a slot nobody reads, the loads past
         // the end read the last block
-        stage_store<M>(L, slot ^ 1, tid, r0, r1, r2, r3, rd);
-        stage_load<M>(src, bb / C::S + 2, NB, tid, r0, r1, r2, r3, rd);
+        stage_store<M>(L, slot ^ 1, tid, r0, r1, r2, r3, rd, rk, rok);
+        stage_load<M>(src, bb / C::S + 2, NB, tid, r0, r1, r2, r3, rd, rk, rok);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -437,6 +481,7 @@ __device__ __forceinline__ StageSrc<M> stage_src(const GArgs& a, const ChunkInfo
   stage_src_share<M>(a, c, tid, s);
   const int64_t rd = entry_of(c, (tid < C::DS ? tid : 0) % (16 * M)) / a.row_div;
   s.d = a.tokd + (size_t)rd * a.NB;
+  s.k = a.tokb + (size_t)rd * a.NB;
   return s;
 }
 
@@ -524,6 +569,16 @@ __device__ __forceinline__ void gate_up_item(const GArgs& a, Stage& L, const Ite
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[hh][i] = q8_code(h[hh][i], d);
+    // accumulator input of the down operand: this lane's rows are columns
+    // 4 (gq & 1) + i of their eights (rows 4..7 of an eight carry q / 16)
+    int kb = (gq & 1) ? 72 : 1032;
+    kb *= q[0][0] + q[0][1] + q[0][2] + q[0][3] + q[1][0] + q[1][1] + q[1][2] + q[1][3];
+    {
+      const auto k16 = __builtin_amdgcn_permlane16_swap((uint32_t)kb, (uint32_t)kb, false, false);
+      kb = (int)k16[0] + (int)k16[1];
+      const auto k32 = __builtin_amdgcn_permlane32_swap((uint32_t)kb, (uint32_t)kb, false, false);
+      kb = (int)k32[0] + (int)k32[1];
+    }
     // f16 pieces of Q8(h): rows 16 hh + 8 m + {0, 2, 4, 6, 1, 3, 5, 7} form
     // piece 2 hh + m, the rows 4..7 of each eight as q / 16.  This lane holds
     // rows 4 gq .. 4 gq + 3 of each half: words 0 and 2 of piece gq >> 1 for
@@ -542,7 +597,10 @@ __device__ __forceinline__ void gate_up_item(const GArgs& a, Stage& L, const Ite
         *reinterpret_cast<uint2*>(dst) = make_uint2(sw[0], sw[1]);
       }
     }
-    if (valid && gq == 0) a.hd[p * G16 + grp] = d;
+    if (valid && gq == 0) {
+      a.hd[p * G16 + grp] = d;
+      a.hb[p * G16 + grp] = -(float)kb;
+    }
     if (TRACE && valid && a.hq) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -654,7 +712,8 @@ __global__ void __launch_bounds__(256, 2) mfma_ffn_kernel(GArgs a) {
 // row quad) are consecutive.  The other workgroups write the f16
 // codes of the Q8 activations in the piece order the MFMA operands read:
 // piece g of block b holds columns 8g + {0, 2, 4, 6, 1, 3, 5, 7}, the columns
-// 4, 6, 5, 7 of each eight as q / 16 (exact in f16).
+// 4, 6, 5, 7 of each eight as q / 16 (exact in f16), and each block's
+// accumulator input -(1032 SL + 72 SH) (see nibbles_to_f16).
 struct FrontArgs {
   const int32_t* counts;
   const int32_t* n_active;
@@ -665,6 +724,7 @@ struct FrontArgs {
   int qg, qd;
   const int8_t* xq;
   uint4* xh;
+  float* xb;
   int64_t T, D;
 };
 
@@ -761,6 +821,12 @@ __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
     h[6] = (_Float16)((float)c[5] * 0.0625f);
     h[7] = (_Float16)((float)c[7] * 0.0625f);
     a.xh[i] = __builtin_bit_cast(uint4, h);
+    // the block's four pieces are lanes 4 m .. 4 m + 3 of this wavefront
+    // (the piece count and the stride are multiples of 4)
+    int kb = 1032 * ((int)c[0] + c[1] + c[2] + c[3]) + 72 * ((int)c[4] + c[5] + c[6] + c[7]);
+    kb += __shfl_xor(kb, 1);
+    kb += __shfl_xor(kb, 2);
+    if ((i & 3) == 0) a.xb[i >> 2] = -(float)kb;
   }
 }
 
@@ -798,6 +864,7 @@ hipError_t launch_mfma_front(const coli_expert_table& t, const int8_t* xq, int64
   f.qd = mfma_quads_down(t.d_model);
   f.xq = xq;
   f.xh = reinterpret_cast<uint4*>(ws.xh);
+  f.xb = ws.xbias;
   f.T = T;
   f.D = t.d_model;
   const int64_t pieces = T * (t.d_model / 32) * 4;
@@ -817,6 +884,7 @@ hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t 
   g.ws = t.gu_s;
   g.tok = reinterpret_cast<const uint4*>(ws.xh);
   g.tokd = xd;
+  g.tokb = ws.xbias;
   g.counts = ws.counts;
   g.lists = ws.lists;
   g.items = reinterpret_cast<const int2*>(ws.gu_items);
@@ -831,12 +899,14 @@ hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t 
   g.Q = mfma_quads_gate_up(t.d_ff);
   g.h16 = reinterpret_cast<uint32_t*>(ws.h16);
   g.hd = ws.hd;
+  g.hb = ws.hbias;
   g.hq = tr ? ws.hq : nullptr;
   GArgs d = g;
   d.wq = reinterpret_cast<const u32x4*>(t.dn_q);
   d.ws = t.dn_s;
   d.tok = reinterpret_cast<const uint4*>(ws.h16);
   d.tokd = ws.hd;
+  d.tokb = ws.hbias;
   d.items = reinterpret_cast<const int2*>(ws.dn_items);
   d.total = ws.totals + 1;
   d.NB = (int)(t.d_ff / 32);
@@ -845,6 +915,7 @@ hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t 
   d.Q = mfma_quads_down(t.d_model);
   d.h16 = nullptr;
   d.hd = nullptr;
+  d.hb = nullptr;
   d.hq = nullptr;
   d.o = ws.o;
   // enough workgroups for ceil(chunks / 8) chunks on each XCD (see locate)
