@@ -633,7 +633,7 @@ def paths_leg(table, coli, synth, torch, reps=8):
     w = synth.WORKLOADS[3]
     b = torch.from_numpy(synth.router_bias(w)).cuda()
     rows = []
-    for T in (4, 8, 9, 10, 11, 12, 14, 16, 24, 32, 64, 128, 512):
+    for T in (4, 5, 6, 7, 8, 9, 10, 12, 14, 16, 24, 32, 64, 128, 512):
         x = torch.from_numpy(synth.activations(w, T, 4000)).cuda()
         lg = torch.from_numpy(synth.logits(w, T, 4000)).cuda()
         xq = torch.empty((T, w.D), dtype=torch.int8, device="cuda")
