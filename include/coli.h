@@ -268,15 +268,16 @@ int coli_moe_forward(const coli_expert_table* table, const int8_t* xq, const flo
  *                      tokens per expert; resident int4 tables only.
  *   COLI_PATH_AUTO     GROUPED from the measured crossover in tokens per
  *                      pass (COLI_GROUPED_MIN_TOKENS: at d_model 6144,
- *                      d_ff 2048, 256 + 1 experts, top-8 the two tie at 8
- *                      tokens and the grouped path wins from 9), GEMV below
- *                      it and wherever GROUPED does not apply.
+ *                      d_ff 2048, 256 + 1 experts, top-8 the GEMV wins at 4
+ *                      tokens, the grouped path from 5, where the GEMV
+ *                      moves to its 8-token kernel), GEMV below it and
+ *                      wherever GROUPED does not apply.
  * (An f32-weight path would move 8x the bytes of an HBM-bound GEMV, so it
  * is never the faster one here.) */
 #define COLI_PATH_AUTO 0
 #define COLI_PATH_GEMV 1
 #define COLI_PATH_GROUPED 2
-#define COLI_GROUPED_MIN_TOKENS 9
+#define COLI_GROUPED_MIN_TOKENS 5
 
 /* coli_moe_forward on the given path.  COLI_PATH_GROUPED on a table it does
  * not apply to returns COLI_E_SHAPE. */

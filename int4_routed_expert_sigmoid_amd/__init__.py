@@ -25,7 +25,7 @@ COLI_E_HIP = -5
 COLI_E_INDEX = -6
 COLI_E_TIER = -7
 COLI_PATH_AUTO, COLI_PATH_GEMV, COLI_PATH_GROUPED = 0, 1, 2
-COLI_GROUPED_MIN_TOKENS = 9
+COLI_GROUPED_MIN_TOKENS = 5
 COLI_NOALLOC_BYTES = 64 << 20
 COLI_MAX_EXPERTS = 256
 COLI_MAX_TOPK = 64

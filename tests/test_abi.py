@@ -244,8 +244,8 @@ def test_path_choice_host():
     t = _table(256, 1, 6144, 2048)
     path = lambda tab, T, k=8: L.coli_moe_path(ctypes.byref(tab), T, k)
     assert path(t, 1) == coli.COLI_PATH_GEMV
-    assert path(t, 8) == coli.COLI_PATH_GEMV
-    assert path(t, 9) == coli.COLI_PATH_GROUPED
+    assert path(t, 4) == coli.COLI_PATH_GEMV
+    assert path(t, 5) == coli.COLI_PATH_GROUPED
     assert path(t, 2048) == coli.COLI_PATH_GROUPED
     # no size limit on the grouped path: 2^17 tokens (1.2 M pairs) stay grouped
     assert path(t, 1 << 17) == coli.COLI_PATH_GROUPED

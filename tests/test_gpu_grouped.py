@@ -1,6 +1,6 @@
 """Parity of the grouped (matrix-core) expert path against the oracle (GPU).
 
-From COLI_GROUPED_MIN_TOKENS (9) tokens per pass the forward runs the grouped kernels: per active
+From COLI_GROUPED_MIN_TOKENS (5) tokens per pass the forward runs the grouped kernels: per active
 expert, chunks of up to 128 tokens against 64-row weight groups.  These tests
 check every int32 block partial, g, u, h, Q8(h) and per-pair output
 bit-for-bit, over routings that exercise full, partial and single-token

@@ -134,7 +134,7 @@ def test_tiny_layer_traced(tiny):
 
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 17, 64])
 def test_tiny_layer_token_counts(tiny, T):
-    """Ragged batches: GEMV pass sizes (1-8 tokens), the grouped path from 9, partial chunks."""
+    """Ragged batches: GEMV pass sizes (1-4 tokens), the grouped path from 5, partial chunks."""
     w, table, ox = tiny
     x, lg, b = synth.activations(w, T, 100), synth.logits(w, T, 100), synth.router_bias(w)
     g = GpuLayer(table, w, T).run(x, lg, b)
