@@ -75,11 +75,18 @@ __device__ __forceinline__ int q8_quad(float4 v, float* d_out, int* sum_out) {
 // eps)) in fp64, x = h * r in fp32, then q8_quad.  Writes the packed codes,
 // the block scales, and when non-null the blocks' -8 * code sums and r.
 // red / rsh: workgroup LDS (4 doubles, 1 float).  Every thread must call it.
+// RMSNorm of one row h (sum of squares in fp64, in one fixed order) and Q8_0
+// of x = h * r.  part / nparts: this workgroup quantises Q8 blocks
+// [part * ceil(NB / nparts), ...) of the row only; every part computes the
+// same r (same data, same order), so a row may be split over workgroups.
+// NQ: groups of 4 values per thread and phase (1 when a part is at most 256
+// groups).
+template <int NQ = 8>
 __device__ __forceinline__ void rmsnorm_q8_row(const float* __restrict__ hrow, int64_t D, float eps,
                                                int* __restrict__ q, float* __restrict__ d,
                                                int32_t* __restrict__ xsum8,
                                                float* __restrict__ r_out, double* red,
-                                               float* rsh) {
+                                               float* rsh, int part = 0, int nparts = 1) {
   const float4* hr = reinterpret_cast<const float4*>(hrow);
   double ss = 0.0;
   for (int64_t c = threadIdx.x; c < D / 4; c += 256) {
@@ -97,19 +104,21 @@ __device__ __forceinline__ void rmsnorm_q8_row(const float* __restrict__ hrow, i
     const double tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float r = (float)(1.0 / sqrt(tot / (double)D + (double)eps));
     *rsh = r;
-    if (r_out) *r_out = r;
+    if (r_out && part == 0) *r_out = r;
   }
   __syncthreads();
   const float r = *rsh;
   // Q8_0 of x = h * r with q8_quad's arithmetic, taken in phases over up to
-  // kNormQuads groups of 4 values per thread with branch-free codes (a zero
+  // NQ groups of 4 values per thread with branch-free codes (a zero
   // scale divides by 1 and its code is selected away), so that the lane
   // exchanges and the divisions of independent groups overlap.  A group past
   // the row (whole 8-lane blocks: D/4 and 256 are multiples of 8) computes on
   // an in-bounds copy and stores nothing.
-  constexpr int kNormQuads = 8;
-  const int64_t n4 = D / 4;
-  for (int64_t c0 = 0; c0 < n4; c0 += 256 * kNormQuads) {
+  constexpr int kNormQuads = NQ;
+  const int64_t nb = D / 32, per = (nb + nparts - 1) / nparts;
+  const int64_t b0 = (int64_t)part * per, b1 = b0 + per < nb ? b0 + per : nb;
+  const int64_t n4 = 8 * b1;   // end of this part's groups of 4
+  for (int64_t c0 = 8 * b0; c0 < n4; c0 += 256 * kNormQuads) {
     int64_t c[kNormQuads];
     float4 x[kNormQuads];
     float amax[kNormQuads], dq[kNormQuads];

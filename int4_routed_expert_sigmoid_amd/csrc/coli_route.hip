@@ -243,6 +243,10 @@ __global__ void __launch_bounds__(256) xsum8_kernel(const int8_t* __restrict__ x
   }
 }
 
+// Workgroups of the fused front per token row in norm mode: the row's D / 4
+// groups of 4 values at one per thread.
+__host__ __device__ inline int norm_parts(int64_t D) { return (int)((D / 4 + 255) / 256); }
+
 struct PrologueArgs {
   const float* x;
   const float* logits;
@@ -313,12 +317,17 @@ __global__ void __launch_bounds__(256) prologue_small_kernel(PrologueArgs a) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   if (tid == 0) bad_any = 0;
   if (blockIdx.x > 0 && a.norm) {
-    // workgroup 1 + t: RMSNorm and Q8_0 of token t (the rmsnorm_q8 arithmetic)
+    // workgroups 1 + t * P + p: RMSNorm and Q8_0 of token t (the rmsnorm_q8
+    // arithmetic), the quantisation split into P parts of at most 256 groups
+    // of 4 values (one per thread); each part reduces the whole row itself
     __shared__ double red[4];
     __shared__ float rsh;
-    const int64_t t = blockIdx.x - 1;
-    rmsnorm_q8_row(a.x + t * a.D, a.D, a.eps, reinterpret_cast<int*>(a.xq + t * a.D),
-                   a.xd + t * (a.D / 32), a.xsum8 + t * (a.D / 32), nullptr, red, &rsh);
+    const int parts = norm_parts(a.D);
+    const int64_t t = (blockIdx.x - 1) / parts;
+    const int part = (int)((blockIdx.x - 1) % parts);
+    rmsnorm_q8_row<1>(a.x + t * a.D, a.D, a.eps, reinterpret_cast<int*>(a.xq + t * a.D),
+                      a.xd + t * (a.D / 32), a.xsum8 + t * (a.D / 32), nullptr, red, &rsh, part,
+                      parts);
     return;
   }
   if (blockIdx.x > 0) {
@@ -416,7 +425,7 @@ hipError_t launch_prologue_small(const float* x, const float* logits, const floa
                     counts, lists, n_active, active, err, norm ? 1 : 0, eps};
   int64_t qgroups = (T * D / 4 + 255) / 256;   // one group of 4 values per thread
   if (qgroups > 256) qgroups = 256;
-  if (norm) qgroups = T;                       // one workgroup per token row
+  if (norm) qgroups = T * norm_parts(D);       // norm_parts workgroups per token row
   hipLaunchKernelGGL(prologue_small_kernel, dim3((unsigned)(1 + qgroups)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
