@@ -134,25 +134,35 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
 }
 
 // Batch-union dispatch, expert-major.  Workgroup e < E builds the list of
-// expert e: it sweeps the tokens 256 at a time, one token per thread; a token
-// is listed when one of its slots holds e, at the first such slot (a later
-// slot with the same expert is a repeat and is dropped); list positions are
-// prefix counts of a workgroup-wide ballot, so each list is in ascending
-// token order with no atomics and no scratch memory.  Workgroup E writes the
+// expert e: it sweeps the tokens 1024 at a time, four consecutive tokens per
+// thread; a token is listed when one of its slots holds e, at the first such
+// slot (a later slot with the same expert is a repeat and is dropped); list
+// positions are a workgroup-wide prefix of the threads' counts (three
+// ballots), so each list is in ascending token order with no atomics and no
+// scratch memory.  Workgroup E writes the
 // shared expert's list (slot k of every token), checks every entry (out of
 // range, or equal to an earlier entry of its token), marks the experts some
 // kept entry selects, and writes the active list, n_active and the flag.
 // Every workgroup reads the whole index array once, so the cost is linear in
-// T (E + 1 reads of T * k entries, served by L2).
+// T (E + 1 reads of T * k entries, served by L2); with k = 8 the last
+// workgroup loads four tokens' entries per thread before checking any, so its
+// sweep is not a chain of dependent loads.
 constexpr int kDispatchThreads = 256;
+constexpr int kDispatchTokens = 4;   // consecutive tokens per thread and sweep
 
-// Exclusive prefix of `flag` over the workgroup's 256 threads; returns it and
-// sets *total.
-__device__ __forceinline__ int block_prefix(bool flag, int* wsum, int* total) {
+// Exclusive prefix of v (0 <= v < 8) over the workgroup's 256 threads, from
+// one ballot per bit; returns it and sets *total.
+__device__ __forceinline__ int block_prefix_count(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  if (lane == 0) wsum[wave] = __popcll(m);
+  int pre = 0, sum = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1);
+    pre += __popcll(m & lt) << bit;
+    sum += __popcll(m) << bit;
+  }
+  if (lane == 0) wsum[wave] = sum;
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
@@ -162,9 +172,10 @@ __device__ __forceinline__ int block_prefix(bool flag, int* wsum, int* total) {
   }
   __syncthreads();   // wsum is reused by the next sweep
   *total = tot;
-  return base + __popcll(m & lt);
+  return base + pre;
 }
 
+template <int KC>
 __global__ void __launch_bounds__(kDispatchThreads) dispatch_expert_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int E, int S, int32_t* __restrict__ counts,
     int32_t* __restrict__ lists, int32_t* __restrict__ n_active, int32_t* __restrict__ active,
@@ -174,17 +185,30 @@ __global__ void __launch_bounds__(kDispatchThreads) dispatch_expert_kernel(
   __shared__ int bad_any;
   const int tid = threadIdx.x;
   const int e = (int)blockIdx.x;
+  if (KC > 0) k = KC;
   if (e < E) {
     int count = 0;
-    for (int64_t t0 = 0; t0 < T; t0 += kDispatchThreads) {
-      const int64_t t = t0 + tid;
-      int slot = -1;
-      if (t < T)
-        for (int j = k - 1; j >= 0; --j)   // the first slot holding e wins
-          if (idx[t * k + j] == e) slot = j;
+    for (int64_t t0 = 0; t0 < T; t0 += kDispatchThreads * kDispatchTokens) {
+      const int64_t tb = t0 + (int64_t)tid * kDispatchTokens;
+      int slot[kDispatchTokens];
+      int n = 0;
+#pragma unroll
+      for (int u = 0; u < kDispatchTokens; ++u) {
+        const int64_t t = tb + u;
+        int sl = -1;
+        if (t < T) {
+#pragma unroll
+          for (int j = (KC > 0 ? KC : k) - 1; j >= 0; --j)   // the first slot holding e wins
+            if (idx[t * k + j] == e) sl = j;
+        }
+        slot[u] = sl;
+        n += sl >= 0;
+      }
       int total;
-      const int pos = block_prefix(slot >= 0, wsum, &total);
-      if (slot >= 0) lists[(int64_t)e * T + count + pos] = (int32_t)(t * (k + S) + slot);
+      int pos = count + block_prefix_count(n, wsum, &total);
+#pragma unroll
+      for (int u = 0; u < kDispatchTokens; ++u)
+        if (slot[u] >= 0) lists[(int64_t)e * T + pos++] = (int32_t)((tb + u) * (k + S) + slot[u]);
       count += total;
     }
     if (tid == 0) counts[e] = count;
@@ -195,14 +219,43 @@ __global__ void __launch_bounds__(kDispatchThreads) dispatch_expert_kernel(
   if (tid == 0) bad_any = 0;
   __syncthreads();
   int bad = 0;
-  for (int64_t t = tid; t < T; t += kDispatchThreads) {
-    if (S) lists[(int64_t)E * T + t] = (int32_t)(t * (k + S) + k);
-    for (int j = 0; j < k; ++j) {
-      const int v = idx[t * k + j];
-      bool ok = v >= 0 && v < E;
-      for (int i = 0; i < j && ok; ++i) ok = idx[t * k + i] != v;
-      if (ok) present[v] = 1;
-      else bad = 1;
+  if constexpr (KC > 0) {
+    // kDispatchTokens tokens per thread and sweep, their entries loaded
+    // before any is checked, the repeat test done in registers
+    for (int64_t t0 = 0; t0 < T; t0 += kDispatchThreads * kDispatchTokens) {
+      int v[kDispatchTokens][KC];
+#pragma unroll
+      for (int u = 0; u < kDispatchTokens; ++u) {
+        const int64_t t = t0 + tid + (int64_t)u * kDispatchThreads;
+#pragma unroll
+        for (int j = 0; j < KC; ++j) v[u][j] = t < T ? idx[t * KC + j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kDispatchTokens; ++u) {
+        const int64_t t = t0 + tid + (int64_t)u * kDispatchThreads;
+        if (t < T) {
+          if (S) lists[(int64_t)E * T + t] = (int32_t)(t * (KC + S) + KC);
+#pragma unroll
+          for (int j = 0; j < KC; ++j) {
+            bool ok = v[u][j] >= 0 && v[u][j] < E;
+#pragma unroll
+            for (int i = 0; i < j; ++i) ok = ok && v[u][i] != v[u][j];
+            if (ok) present[v[u][j]] = 1;
+            else bad = 1;
+          }
+        }
+      }
+    }
+  } else {
+    for (int64_t t = tid; t < T; t += kDispatchThreads) {
+      if (S) lists[(int64_t)E * T + t] = (int32_t)(t * (k + S) + k);
+      for (int j = 0; j < k; ++j) {
+        const int v = idx[t * k + j];
+        bool ok = v >= 0 && v < E;
+        for (int i = 0; i < j && ok; ++i) ok = idx[t * k + i] != v;
+        if (ok) present[v] = 1;
+        else bad = 1;
+      }
     }
   }
   if (bad) atomicOr(&bad_any, 1);
@@ -441,8 +494,12 @@ hipError_t launch_route_topk(const float* logits, const float* bias, int64_t T, 
 hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, int32_t* counts,
                            int32_t* lists, int32_t* n_active, int32_t* active, int32_t* err,
                            const int8_t* xq, int64_t D, int32_t* xsum8, hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_expert_kernel, dim3((unsigned)(E + 1)), dim3(kDispatchThreads), 0, s,
-                     idx, T, k, E, S, counts, lists, n_active, active, err);
+  if (k == 8)
+    hipLaunchKernelGGL(dispatch_expert_kernel<8>, dim3((unsigned)(E + 1)), dim3(kDispatchThreads),
+                       0, s, idx, T, k, E, S, counts, lists, n_active, active, err);
+  else
+    hipLaunchKernelGGL(dispatch_expert_kernel<0>, dim3((unsigned)(E + 1)), dim3(kDispatchThreads),
+                       0, s, idx, T, k, E, S, counts, lists, n_active, active, err);
   hipError_t rc = hipGetLastError();
   if (rc != hipSuccess || !xq || T == 0) return rc;
   const int64_t nb = T * (D / 32);

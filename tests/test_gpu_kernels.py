@@ -170,7 +170,7 @@ def dispatch(idx, E, S):
         int(err.item())
 
 
-@pytest.mark.parametrize("wl,T", [(0, 4), (2, 4), (3, 2048)])
+@pytest.mark.parametrize("wl,T", [(0, 4), (2, 4), (3, 2048), (3, 2500)])
 def test_dispatch(wl, T):
     w = synth.WORKLOADS[wl]
     ridx, _ = oracle.route(synth.logits(w, T), synth.router_bias(w), w.k)
@@ -190,7 +190,7 @@ def _bad_routings():
     yield np.int32([[5, 5], [1, 2]]), 16
     yield np.int32([[5, 5], [5, 4]]), 16
     rng = np.random.default_rng(5)
-    for T, E, k in ((300, 256, 8), (700, 16, 2), (65, 64, 4)):
+    for T, E, k in ((300, 256, 8), (700, 16, 2), (65, 64, 4), (2301, 256, 8), (1030, 32, 3)):
         idx = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
         idx[::2, -1] = idx[::2, 0]
         yield idx, E
@@ -199,7 +199,7 @@ def _bad_routings():
 def test_dispatch_drops_bad_indices():
     """Out-of-range and repeated entries are left out of every list (the
     oracle's keep rule), the lists of the rest are exact, and the flag is set;
-    the larger cases span several 256-token sweeps."""
+    the larger cases span several 1024-token sweeps with a ragged tail."""
     for bad, E in _bad_routings():
         counts, lists, na, active, err = dispatch(bad, E, 1)
         assert err == coli.COLI_E_INDEX

@@ -194,7 +194,7 @@ def test_dropped_entries_one_token(tiny, bad):
 def test_dropped_entries_many_tokens(tiny, path, T):
     """Batches with repeats and out-of-range slots through both expert paths:
     T = 2 with a repeat that precedes a valid slot of the next token, and
-    ragged batches past one dispatch sweep (256 tokens)."""
+    ragged batches past the shared-list workgroup's 256-token sweep."""
     w, table, ox = tiny
     rng = np.random.default_rng(T)
     idx = np.stack([rng.choice(w.E, w.k, replace=False) for _ in range(T)]).astype(np.int32)
