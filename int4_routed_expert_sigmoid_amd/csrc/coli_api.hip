@@ -104,9 +104,8 @@ MoeWorkspace moe_workspace_layout(void* base, int E, int S, int64_t D, int64_t F
   w.h16 = static_cast<uint16_t*>(take(2 * P * (size_t)F));
   w.xbias = reinterpret_cast<float*>(w.xsum8);
   w.hbias = reinterpret_cast<float*>(w.hsum8);
-  w.gu_items = static_cast<int32_t*>(take(8 * chunks * (size_t)mfma_quads_gate_up(F)));
-  w.dn_items = static_cast<int32_t*>(take(8 * chunks * (size_t)mfma_quads_down(D)));
-  w.totals = static_cast<int32_t*>(take(2 * sizeof(int32_t)));
+  w.chunks = static_cast<int32_t*>(take(8 * chunks));
+  w.n_chunks = static_cast<int32_t*>(take(sizeof(int32_t)));
   w.bytes = off;
   return w;
 }

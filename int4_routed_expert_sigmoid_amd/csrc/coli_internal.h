@@ -210,9 +210,8 @@ struct MoeWorkspace {
   // of xsum8 and hsum8, which the grouped path does not use)
   float* xbias;      // [T][D/32]
   float* hbias;      // [P][F/32]
-  int32_t* gu_items; // [chunks * gate/up quads][2] work items
-  int32_t* dn_items; // [chunks * down quads][2]
-  int32_t* totals;   // [2] item counts
+  int32_t* chunks;   // [max chunks][2] (expert, chunk index) in execution order
+  int32_t* n_chunks; // [1]
   size_t bytes;
 };
 

@@ -139,24 +139,23 @@ struct Item {
   bool ok;
 };
 
-// Work item of this workgroup.  The lists are chunk-major (the row quads of
-// one chunk are consecutive, q per chunk) and sorted by descending work.
-// Workgroups are dispatched to the eight XCDs round robin by blockIdx.x, and
-// XCD x takes chunks x, x + 8, x + 16, ... with all q row quads of a chunk in
-// a row: every XCD gets the same mix of heavy and light chunks, and the row
-// quads of a chunk, which stage the same tokens, share them in that XCD's L2.
-__device__ __forceinline__ Item locate(const int2* items, const int32_t* total, int q) {
+// Work item of this workgroup: one row quad of one chunk.  The chunk list is
+// sorted by descending work.  Workgroups are dispatched to the eight XCDs
+// round robin by blockIdx.x, and XCD x takes chunks x, x + 8, x + 16, ...
+// with all q row quads of a chunk in a row: every XCD gets the same mix of
+// heavy and light chunks, and the row quads of a chunk, which stage the same
+// tokens, share them in that XCD's L2.
+__device__ __forceinline__ Item locate(const int2* chunks, const int32_t* n_chunks, int q) {
   Item it = {};
-  const int tot = *as_const(total);
+  const int tot = *as_const(n_chunks);
   const int bid = (int)blockIdx.x;
   const int k = bid >> 3;
-  const int L = ((k / q) * 8 + (bid & 7)) * q + k % q;
-  it.ok = L < tot;
+  const int p = (k / q) * 8 + (bid & 7);
+  it.ok = p < tot;
   if (!it.ok) return it;
-  const cptr<int32_t> v = as_const(reinterpret_cast<const int32_t*>(items) + 2 * (size_t)L);
-  const int x = v[0];
-  it.e = x & 0xFFFF;
-  it.quad = x >> 16;
+  const cptr<int32_t> v = as_const(reinterpret_cast<const int32_t*>(chunks) + 2 * (size_t)p);
+  it.e = v[0];
+  it.quad = k % q;
   it.chunk = v[1];
   return it;
 }
@@ -179,8 +178,8 @@ struct GArgs {
   const float* tokb;
   const int32_t* counts;
   const int32_t* lists;
-  const int2* items;
-  const int32_t* total;
+  const int2* chunks;     // (expert, chunk index) in execution order
+  const int32_t* n_chunks;
   int64_t T, D, F;
   int NB, RG, KS, row_div;
   int Q;                  // row quads per chunk (items per chunk)
@@ -669,7 +668,7 @@ __device__ __forceinline__ void down_item(const GArgs& a, Stage& L, const Item& 
 template <bool DOWN, bool TRACE>
 __global__ void __launch_bounds__(256, 2) mfma_ffn_kernel(GArgs a) {
   __shared__ Stage lds;
-  const Item it = locate(a.items, a.total, a.Q);
+  const Item it = locate(a.chunks, a.n_chunks, a.Q);
   if (!it.ok) return;
   const int tid = (int)threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -701,15 +700,15 @@ __global__ void __launch_bounds__(256, 2) mfma_ffn_kernel(GArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Front of the grouped path, after dispatch.  Workgroup 0 builds the work
-// lists: an expert of n tokens has n / 128 full chunks (M = 8) and, when
-// n % 128 > 0, one last chunk of M = ceil((n % 128) / 16) subtiles; every
-// chunk is qg gate/up and qd down items, one per row quad.  The lists hold the
-// M = 8 chunks first, then the last chunks by descending M, so workgroups
-// running side by side mostly execute the same code (each M is its own
-// unrolled loop; a last chunk of M = 8 follows the full ones); inside a
-// group the experts are in ascending order, and each chunk's q items (one per
-// row quad) are consecutive.  The other workgroups write the f16
+// Front of the grouped path, after dispatch.  Workgroup 0 builds the chunk
+// list that both matrix kernels share: an expert of n tokens has n / 128 full
+// chunks (M = 8) and, when n % 128 > 0, one last chunk of M = ceil((n % 128) /
+// 16) subtiles; each chunk is one work item per row quad of the kernel, found
+// by locate.  The list holds the M = 8 chunks first, then the last chunks by
+// descending M, so workgroups running side by side mostly execute the same
+// code (each M is its own unrolled loop; a last chunk of M = 8 follows the
+// full ones); inside a group the experts are in ascending order.  The other
+// workgroups write the f16
 // codes of the Q8 activations in the piece order the MFMA operands read:
 // piece g of block b holds columns 8g + {0, 2, 4, 6, 1, 3, 5, 7}, the columns
 // 4, 6, 5, 7 of each eight as q / 16 (exact in f16), and each block's
@@ -718,10 +717,8 @@ struct FrontArgs {
   const int32_t* counts;
   const int32_t* n_active;
   const int32_t* active;
-  int2* gu_items;
-  int2* dn_items;
-  int32_t* totals;   // [2]: gate/up items, down items
-  int qg, qd;
+  int2* chunks;
+  int32_t* n_chunks;
   const int8_t* xq;
   uint4* xh;
   float* xb;
@@ -750,12 +747,11 @@ __device__ __forceinline__ int wg_exclusive(int v, int* wsum, int* total) {
   return base + x - v;
 }
 
-// nc chunks c0 .. c0 + nc - 1 of expert e from chunk position pos, q row
-// quads each: items (e | quad << 16, chunk), chunk-major; one wavefront.
-__device__ __forceinline__ void emit_items(int2* items, int q, int pos, int e, int c0, int nc,
-                                           int lane) {
-  for (int i = lane; i < nc * q; i += kWave)
-    items[(size_t)pos * q + i] = make_int2(e | ((i % q) << 16), c0 + i / q);
+// nc chunks c0 .. c0 + nc - 1 of expert e from list position pos; one
+// wavefront.
+__device__ __forceinline__ void emit_chunks(int2* chunks, int pos, int e, int c0, int nc,
+                                            int lane) {
+  for (int i = lane; i < nc; i += kWave) chunks[pos + i] = make_int2(e, c0 + i);
 }
 
 __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
@@ -788,19 +784,12 @@ __global__ void __launch_bounds__(256) mfma_front_kernel(FrontArgs a) {
     }
     plan[2 * t] = make_int4(e[0], f[0], p8, last[0]);
     plan[2 * t + 1] = make_int4(e[1], f[1], p8 + f[0], last[1]);
-    if (t == 0) {
-      a.totals[0] = start * a.qg;
-      a.totals[1] = start * a.qd;
-    }
+    if (t == 0) *a.n_chunks = start;
     __syncthreads();
     for (int s = wave; s < nact; s += 4) {
       const int4 pl = plan[s];
-      emit_items(a.gu_items, a.qg, pl.z, pl.x, 0, pl.y, lane);
-      emit_items(a.dn_items, a.qd, pl.z, pl.x, 0, pl.y, lane);
-      if (pl.w >= 0) {
-        emit_items(a.gu_items, a.qg, pl.w, pl.x, pl.y, 1, lane);
-        emit_items(a.dn_items, a.qd, pl.w, pl.x, pl.y, 1, lane);
-      }
+      emit_chunks(a.chunks, pl.z, pl.x, 0, pl.y, lane);
+      if (pl.w >= 0) emit_chunks(a.chunks, pl.w, pl.x, pl.y, 1, lane);
     }
     return;
   }
@@ -857,11 +846,8 @@ hipError_t launch_mfma_front(const coli_expert_table& t, const int8_t* xq, int64
   f.counts = ws.counts;
   f.n_active = ws.n_active;
   f.active = ws.active;
-  f.gu_items = reinterpret_cast<int2*>(ws.gu_items);
-  f.dn_items = reinterpret_cast<int2*>(ws.dn_items);
-  f.totals = ws.totals;
-  f.qg = mfma_quads_gate_up(t.d_ff);
-  f.qd = mfma_quads_down(t.d_model);
+  f.chunks = reinterpret_cast<int2*>(ws.chunks);
+  f.n_chunks = ws.n_chunks;
   f.xq = xq;
   f.xh = reinterpret_cast<uint4*>(ws.xh);
   f.xb = ws.xbias;
@@ -887,8 +873,8 @@ hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t 
   g.tokb = ws.xbias;
   g.counts = ws.counts;
   g.lists = ws.lists;
-  g.items = reinterpret_cast<const int2*>(ws.gu_items);
-  g.total = ws.totals;
+  g.chunks = reinterpret_cast<const int2*>(ws.chunks);
+  g.n_chunks = ws.n_chunks;
   g.T = T;
   g.D = t.d_model;
   g.F = t.d_ff;
@@ -907,8 +893,6 @@ hipError_t launch_mfma_ffn(const coli_expert_table& t, const float* xd, int64_t 
   d.tok = reinterpret_cast<const uint4*>(ws.h16);
   d.tokd = ws.hd;
   d.tokb = ws.hbias;
-  d.items = reinterpret_cast<const int2*>(ws.dn_items);
-  d.total = ws.totals + 1;
   d.NB = (int)(t.d_ff / 32);
   d.RG = (int)(t.d_model / 64);
   d.row_div = 1;
