@@ -394,7 +394,7 @@ int coli_moe_block(const coli_expert_table* table, float* h, const float* logits
  * (64 MiB) that each GPU the library runs on holds until the process ends;
  * the call allocates and frees nothing.  A call needing more than that
  * (coli_moe_layer_workspace_bytes(table, T, k) > COLI_NOALLOC_BYTES; at
- * d_model 6144, d_ff 2048, top-8 with a shared expert: above 221 tokens)
+ * d_model 6144, d_ff 2048, top-8 with a shared expert: above 222 tokens)
  * returns COLI_E_WORKSPACE before any launch.  Resident tables only
  * (slot_of == NULL, else COLI_E_INVAL): with the routing inside the call no
  * index error can arise, so no status needs reading back.  Every call on one
