@@ -63,7 +63,7 @@ typedef enum {
                             a pass needs more experts than the tier's slots  */
 } coli_status;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define COLI_MAX_EXPERTS 256 /* routed experts per layer                    */
 #define COLI_MAX_TOPK 64     /* experts selected per token                  */
 #define COLI_MAX_DIM 32768   /* d_model and d_ff of an expert table         */
