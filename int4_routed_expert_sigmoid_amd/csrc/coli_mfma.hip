@@ -218,7 +218,7 @@ struct GArgs {
 template <int M>
 struct Cfg {
   static constexpr bool OFFSET = M <= 2;
-  static constexpr int S = M <= 2 ? 8 : M <= 4 ? 4 : M <= 6 ? 2 : 1;
+  static constexpr int S = M <= 2 ? 8 : M <= 4 ? 4 : 2;
   static constexpr int RS = M <= 4 ? 8 : 4;             // ring slots
   static constexpr int R = RS - 1;                      // blocks in flight
   static constexpr int U = (2 * S > RS ? 2 * S : RS);
