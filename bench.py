@@ -663,7 +663,9 @@ def paths_leg(table, coli, synth, torch, reps=8):
 
 
 def router_leg(coli, synth, torch, steps=50):
-    """The router projection (F32 weights [256][6144], fp64 sum) for 1 and 2048 tokens."""
+    """The router projection (F32 weights [256][6144], fp64 sum) for 1 and 2048
+    tokens: `steps` calls captured in a HIP graph, one replay timed (so the
+    one-token figure is the kernel and its dispatch, not the host's launch)."""
     w = synth.WORKLOADS[1]
     wr = torch.from_numpy(synth.router_weights(w)).cuda()
     res = {}
@@ -672,14 +674,19 @@ def router_leg(coli, synth, torch, steps=50):
         out = torch.empty((T, w.E), dtype=torch.float32, device="cuda")
         for _ in range(3):
             coli.coli_router_logits(x, wr, out)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                coli.coli_router_logits(x, wr, out)
+        g.replay()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record()
-        for _ in range(steps):
-            coli.coli_router_logits(x, wr, out)
+        g.replay()
         t1.record()
         torch.cuda.synchronize()
+        del g
         us = t0.elapsed_time(t1) / steps * 1e3
         nbytes = 4 * (w.E * w.D + T * w.D + T * w.E)
         res[f"t{T}_us"] = round(us, 2)

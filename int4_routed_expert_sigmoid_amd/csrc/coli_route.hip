@@ -522,64 +522,84 @@ hipError_t launch_dispatch(const int32_t* idx, int64_t T, int k, int E, int S, i
 namespace coli {
 namespace {
 
-// Few tokens: one wavefront per expert row streams the row once (float4
-// loads, eight in flight per lane) and reuses it for each token; four
-// independent fp64 chains per lane, then a fixed butterfly over the lanes.
+// Few tokens: one workgroup per expert row, its four wavefronts a quarter
+// of the row each.  A wavefront loads its quarter once (float4, every load in
+// flight together: up to 8 per lane, a quarter of up to 8,192 columns) and
+// keeps it in registers for every token; per token it loads the token's
+// quarter, runs four independent fp64 chains per lane and a fixed butterfly
+// over the lanes, and the four quarters are summed in order.
+constexpr int kRrChunks = 8;   // float4 per lane and quarter row
+
 __global__ void __launch_bounds__(256) router_rows_kernel(const float* __restrict__ x,
                                                           const float* __restrict__ wr,
                                                           int64_t T, int64_t D, int E,
                                                           float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+  __shared__ double part[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x;
+  const int64_t n4 = D / 4;              // a multiple of 16
+  const int64_t q4 = (n4 + 3) / 4;       // float4 per quarter (at most 64 * kRrChunks)
+  const int64_t lo = wave * q4, hi = lo + q4 < n4 ? lo + q4 : n4;
   const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)e * D);
-  const int64_t n4 = D / 4;   // a multiple of 16
-  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+  float4 a[kRrChunks];
+#pragma unroll
+  for (int u = 0; u < kRrChunks; ++u) {
+    const int64_t i = lo + lane + 64 * u;
+    a[u] = i < hi ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int64_t t = 0; t < T; ++t) {
     const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * D);
+    float4 b[kRrChunks];
+#pragma unroll
+    for (int u = 0; u < kRrChunks; ++u) {
+      const int64_t i = lo + lane + 64 * u;
+      b[u] = i < hi ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     double s[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int64_t i0 = lane; i0 < n4; i0 += 64 * 8) {
-      float4 a[8], b[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + 64 * u;
-        a[u] = i < n4 ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        b[u] = i < n4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        s[0] = __builtin_fma((double)a[u].x, (double)b[u].x, s[0]);
-        s[1] = __builtin_fma((double)a[u].y, (double)b[u].y, s[1]);
-        s[2] = __builtin_fma((double)a[u].z, (double)b[u].z, s[2]);
-        s[3] = __builtin_fma((double)a[u].w, (double)b[u].w, s[3]);
-      }
+    for (int u = 0; u < kRrChunks; ++u) {
+      s[0] = __builtin_fma((double)a[u].x, (double)b[u].x, s[0]);
+      s[1] = __builtin_fma((double)a[u].y, (double)b[u].y, s[1]);
+      s[2] = __builtin_fma((double)a[u].z, (double)b[u].z, s[2]);
+      s[3] = __builtin_fma((double)a[u].w, (double)b[u].w, s[3]);
     }
     double v = (s[0] + s[1]) + (s[2] + s[3]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == 0) out[(size_t)t * E + e] = (float)v;
+    if (lane == 0) part[wave][t] = v;
   }
+  __syncthreads();
+  if (threadIdx.x < T)
+    out[(size_t)threadIdx.x * E + e] =
+        (float)((part[0][threadIdx.x] + part[1][threadIdx.x]) +
+                (part[2][threadIdx.x] + part[3][threadIdx.x]));
 }
 
-// Many tokens: a workgroup owns 64 experts x 32 tokens; a thread owns 4
-// experts x 2 tokens (8 fp64 accumulators).  64-column slices of the weight
-// rows and of the tokens are staged in LDS (rows padded to 65 floats); per
-// column a thread reads 4 weights and 2 token values for 8 fmas.
-constexpr int kRtE = 64, kRtT = 32, kRtK = 64;
+// Many tokens: fp64 matrix cores (v_mfma_f64_16x16x4_f64), the fp32 inputs
+// converted to fp64 as they are read from LDS, so every product is exact and
+// every sum is an fp64 sum.  A workgroup owns 64 experts x 32 tokens,
+// wavefront w the experts 16 w .. 16 w + 15 against the 32 tokens (two 16 x 16
+// tiles).  64-column slices of the weight rows and of the tokens are staged
+// in LDS as fp32 (rows 66 floats apart: the 32 lanes of each half of an
+// operand read hit 32 different banks), double-buffered, the next slice's
+// global loads held in registers while the current one is used.
+// Operand layouts (16 x 16 x 4, fp64): A lane l = (row l % 16, k l / 16); B
+// lane l = (k l / 16, column l % 16); the result's element i of lane l = (row
+// l / 16 + 4 i, column l % 16).
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kRmE = 64, kRmT = 32, kRmK = 64, kRmLd = kRmK + 2;
 
-__global__ void __launch_bounds__(256) router_tiles_kernel(const float* __restrict__ x,
-                                                           const float* __restrict__ wr,
-                                                           int64_t T, int64_t D, int E,
-                                                           float* __restrict__ out) {
-  __shared__ float ws[kRtE][kRtK + 1];
-  __shared__ float xs[kRtT][kRtK + 1];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int e0 = blockIdx.x * kRtE;
-  const int64_t t0 = (int64_t)blockIdx.y * kRtT;
-  double acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.0;
-  // the next 64-column slice is loaded into registers (float4, 4 of the
-  // weights and 2 of the tokens per thread) while the current one is used
+__global__ void __launch_bounds__(256) router_mfma_kernel(const float* __restrict__ x,
+                                                          const float* __restrict__ wr,
+                                                          int64_t T, int64_t D, int E,
+                                                          float* __restrict__ out) {
+  __shared__ float ws[2][kRmE * kRmLd];
+  __shared__ float xs[2][kRmT * kRmLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * kRmE;
+  const int64_t t0 = (int64_t)blockIdx.y * kRmT;
+  // staging shares: weight float4 q = tid + 256 j (row q / 16, columns 4 (q % 16) ..),
+  // token float4 q = tid + 256 j likewise
   float4 rw[4], rx[2];
   auto load_slice = [&](int64_t k0) {
 #pragma unroll
@@ -595,43 +615,50 @@ __global__ void __launch_bounds__(256) router_tiles_kernel(const float* __restri
                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  load_slice(0);
-  for (int64_t k0 = 0; k0 < D; k0 += kRtK) {
+  auto store_slice = [&](int slot) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int q = tid + 256 * j, r = q >> 4, c = 4 * (q & 15);
-      ws[r][c] = rw[j].x; ws[r][c + 1] = rw[j].y; ws[r][c + 2] = rw[j].z; ws[r][c + 3] = rw[j].w;
+      float2* p = reinterpret_cast<float2*>(&ws[slot][r * kRmLd + c]);
+      p[0] = make_float2(rw[j].x, rw[j].y);
+      p[1] = make_float2(rw[j].z, rw[j].w);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int q = tid + 256 * j, r = q >> 4, c = 4 * (q & 15);
-      xs[r][c] = rx[j].x; xs[r][c + 1] = rx[j].y; xs[r][c + 2] = rx[j].z; xs[r][c + 3] = rx[j].w;
+      float2* p = reinterpret_cast<float2*>(&xs[slot][r * kRmLd + c]);
+      p[0] = make_float2(rx[j].x, rx[j].y);
+      p[1] = make_float2(rx[j].z, rx[j].w);
     }
-    __syncthreads();
-    if (k0 + kRtK < D) load_slice(k0 + kRtK);
-#pragma unroll 4
-    for (int c = 0; c < kRtK; ++c) {
-      double wv[4], xv[2];
+  };
+  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  const int ar = 16 * wave + (lane & 15), bk = lane >> 4, bc = lane & 15;
+  load_slice(0);
+  store_slice(0);
+  __syncthreads();
+  int slot = 0;
+  for (int64_t k0 = 0; k0 < D; k0 += kRmK) {
+    const bool more = k0 + kRmK < D;
+    if (more) load_slice(k0 + kRmK);
+    const float* wa = &ws[slot][ar * kRmLd + bk];
+    const float* xa = &xs[slot][bc * kRmLd + bk];
+    const float* xb = &xs[slot][(16 + bc) * kRmLd + bk];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wv[i] = (double)ws[4 * tx + i][c];
-      xv[0] = (double)xs[2 * ty][c];
-      xv[1] = (double)xs[2 * ty + 1][c];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i][0] = __builtin_fma(wv[i], xv[0], acc[i][0]);
-        acc[i][1] = __builtin_fma(wv[i], xv[1], acc[i][1]);
-      }
+    for (int kk = 0; kk < kRmK; kk += 4) {
+      const double a = (double)wa[kk];
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)xa[kk], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)xb[kk], acc1, 0, 0, 0);
     }
+    if (more) store_slice(slot ^ 1);
     __syncthreads();
+    slot ^= 1;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = e0 + 4 * tx + i;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t t = t0 + 2 * ty + j;
-      if (e < E && t < T) out[(size_t)t * E + e] = (float)acc[i][j];
-    }
+    const int e = e0 + 16 * wave + (lane >> 4) + 4 * i;
+    const int64_t ta = t0 + (lane & 15), tb = ta + 16;
+    if (e < E && ta < T) out[(size_t)ta * E + e] = (float)acc0[i];
+    if (e < E && tb < T) out[(size_t)tb * E + e] = (float)acc1[i];
   }
 }
 
@@ -640,12 +667,12 @@ __global__ void __launch_bounds__(256) router_tiles_kernel(const float* __restri
 hipError_t launch_router_logits(const float* x, const float* wr, int64_t T, int64_t D, int E,
                                 float* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T < 16) {
-    hipLaunchKernelGGL(router_rows_kernel, dim3((unsigned)((E + 3) / 4), (unsigned)T), dim3(256),
-                       0, s, x, wr, T, D, E, out);
+  if (T < 16 && D / 4 <= 4 * 64 * kRrChunks) {
+    hipLaunchKernelGGL(router_rows_kernel, dim3((unsigned)E), dim3(256), 0, s, x, wr, T, D, E,
+                       out);
   } else {
-    hipLaunchKernelGGL(router_tiles_kernel,
-                       dim3((unsigned)((E + kRtE - 1) / kRtE), (unsigned)((T + kRtT - 1) / kRtT)),
+    hipLaunchKernelGGL(router_mfma_kernel,
+                       dim3((unsigned)((E + kRmE - 1) / kRmE), (unsigned)((T + kRmT - 1) / kRmT)),
                        dim3(256), 0, s, x, wr, T, D, E, out);
   }
   return hipGetLastError();
