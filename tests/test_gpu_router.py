@@ -58,6 +58,24 @@ def test_router_logits(wl, T):
     assert_bitexact("w", wt.cpu().numpy(), rw)
 
 
+@pytest.mark.parametrize("D,E,T", [(64, 5, 3), (64, 5, 40), (8256, 70, 2), (8256, 70, 33),
+                                   (192, 129, 17)])
+def test_router_logits_odd_shapes(D, E, T):
+    """Shapes at the kernels' edges: a quarter row of one float4 per lane
+    group (D = 64), rows too long for the few-token kernel (D = 8256 > 8192:
+    the matrix-core kernel at 2 tokens too), expert and token counts that
+    leave partial 64-expert / 32-token tiles."""
+    from dataclasses import replace
+    w = replace(synth.WORKLOADS[0], D=D, E=E, k=min(synth.WORKLOADS[0].k, E), tag=11)
+    x = synth.activations(w, T, 950)
+    wr = synth.router_weights(w)
+    got = gpu_logits(x, wr).cpu().numpy()
+    ref = oracle.router_logits(x, wr)
+    absterm = np.abs(x.astype(np.float64)) @ np.abs(wr.astype(np.float64)).T
+    assert_within_tol("router logits", got, ref, absterm)
+    assert np.mean(got == ref) >= 0.999
+
+
 def test_router_logits_closed_form():
     x = np.full((3, 6144), 0.25, np.float32)
     wr = np.full((256, 6144), 0.5, np.float32)
