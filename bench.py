@@ -721,8 +721,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one MI355X: the hot path runs on one GPU's share and this "
-              "build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        print("bench.py measures one MI355X: the hot path runs on one GPU's share and the "
+              "library has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
